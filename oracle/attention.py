@@ -1,0 +1,144 @@
+"""Plain float64 definition of exact attention and its gradient (CPU oracle).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the GPU library.
+
+What is computed, per (batch, head), with Q, K, V, dO in R^{N x d} taken as the
+exact values the GPU received (dtype-rounded, then widened to float64):
+
+* scores S = scale * Q K^T, the scaled form on the FlashAttention walkthrough
+  (bluuewhale.github.io, "How Attention Is Computed");
+* entries that the causal rule (key j <= query i, FlashAttention-2 notes,
+  "Causal mask optimisation") or the block mask (walkthrough,
+  "Block-Sparse FlashAttention": one 0/1 entry per score tile) forbid are set
+  to -inf before the softmax;
+* P = row softmax of S with the row maximum subtracted first (safe softmax,
+  Flash Attention v1 notes on languisher.top, "Naive Attention");
+* O = P V and the row log-sum-exp LSE_i = m_i + ln(sum_j exp(S_ij - m_i))
+  (FlashAttention-2 notes, eq. (15));
+* the backward pass by the chain rule (FlashAttention-2 notes, eqs. (27)-(30)):
+  dV = P^T dO, dP = dO V^T, dS = P o (dP - <p, dp>), dQ = scale dS K,
+  dK = scale dS^T Q.  The row term <p, dp> is summed from P and dP directly,
+  not from rowsum(dO o O), so the D identity used by the GPU backward is
+  checked independently rather than assumed.
+
+S and P are materialised in full (no tiling, no online softmax); rows may be
+processed in chunks only to bound host memory, which changes no arithmetic
+beyond the summation order of dK and dV across chunks.
+
+Rows with no allowed key (unreachable for causal or diagonal-kept masks) follow
+a stated convention: O = 0, LSE = -inf, zero gradient contributions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK_BLOCK = 128  # tokens per block-mask entry
+
+
+def allowed(n_q: int, n_k: int, causal: bool, block_mask=None,
+            mask_block: int = MASK_BLOCK, rows=None) -> np.ndarray:
+    """Boolean matrix [len(rows), n_k]: True where query row i may see key j.
+
+    causal: j <= i (query and key positions share one index space, n_q == n_k).
+    block_mask: 0/1 array [ceil(n_q/mask_block), ceil(n_k/mask_block)]; entry
+    (i // mask_block, j // mask_block) must be 1.
+    """
+    i = np.arange(n_q) if rows is None else np.asarray(rows)
+    j = np.arange(n_k)
+    ok = np.ones((i.shape[0], n_k), dtype=bool)
+    if causal:
+        ok &= j[None, :] <= i[:, None]
+    if block_mask is not None:
+        bm = np.asarray(block_mask).astype(bool)
+        ok &= bm[i[:, None] // mask_block, j[None, :] // mask_block]
+    return ok
+
+
+def _softmax_rows(S: np.ndarray):
+    """Safe row softmax of S (entries may be -inf). Returns P, m, LSE."""
+    m = S.max(axis=1)
+    has = np.isfinite(m)
+    m0 = np.where(has, m, 0.0)
+    E = np.exp(S - m0[:, None])          # exp(-inf) = 0 for masked entries
+    l = E.sum(axis=1)
+    l1 = np.where(has, l, 1.0)
+    P = E / l1[:, None]
+    lse = np.where(has, m0 + np.log(l1), -np.inf)
+    return P, m, lse
+
+
+def scores(q, k, scale, causal=False, block_mask=None, mask_block=MASK_BLOCK, rows=None):
+    """S = scale * Q K^T with forbidden entries set to -inf (rows subset optional)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    r = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    S = scale * (q[r] @ k.T)
+    ok = allowed(q.shape[0], k.shape[0], causal, block_mask, mask_block, rows=r)
+    return np.where(ok, S, -np.inf)
+
+
+def forward_head(q, k, v, scale, causal=False, block_mask=None,
+                 mask_block=MASK_BLOCK, rows=None):
+    """One head: returns (O [R, d], LSE [R]) for the selected query rows."""
+    S = scores(q, k, scale, causal, block_mask, mask_block, rows)
+    P, _, lse = _softmax_rows(S)
+    O = P @ np.asarray(v, dtype=np.float64)
+    return O, lse
+
+
+def probs_head(q, k, scale, causal=False, block_mask=None, mask_block=MASK_BLOCK, rows=None):
+    """One head: the full probability rows P [R, N] (for invariant tests)."""
+    P, _, _ = _softmax_rows(scores(q, k, scale, causal, block_mask, mask_block, rows))
+    return P
+
+
+def _row_chunk(n: int) -> int:
+    # keep one fp64 chunk of S/P/dP near 64 MiB
+    return max(1, min(n, (1 << 23) // max(n, 1)))
+
+
+def backward_head(q, k, v, do, scale, causal=False, block_mask=None,
+                  mask_block=MASK_BLOCK, chunk=None):
+    """One head: (dQ, dK, dV) of loss sum(O o dO) by the chain rule.
+
+    Every row's P and dP are materialised; ``chunk`` only bounds memory.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n = q.shape[0]
+    c = chunk or _row_chunk(k.shape[0])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n, c):
+        rows = np.arange(r0, min(n, r0 + c))
+        P = probs_head(q, k, scale, causal, block_mask, mask_block, rows)
+        dv += P.T @ do[rows]                       # dV = P^T dO
+        dP = do[rows] @ v.T                        # dP = dO V^T
+        rowdot = (P * dP).sum(axis=1)              # <p, dp> per row, eq. (30)
+        dS = P * (dP - rowdot[:, None])            # softmax Jacobian, eq. (29)
+        dq[rows] = scale * (dS @ k)                # S = scale Q K^T
+        dk += scale * (dS.T @ q[rows])
+    return dq, dk, dv
+
+
+def _heads(B, H, heads):
+    return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+
+
+def forward(q, k, v, scale, causal=False, block_mask=None, mask_block=MASK_BLOCK, heads=None):
+    """Batched [B, H, N, d] float64 inputs -> dict {(b, h): (O, LSE)}."""
+    B, H = q.shape[:2]
+    return {(b, h): forward_head(q[b, h], k[b, h], v[b, h], scale, causal, block_mask, mask_block)
+            for (b, h) in _heads(B, H, heads)}
+
+
+def backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=MASK_BLOCK, heads=None):
+    """Batched [B, H, N, d] float64 inputs -> dict {(b, h): (dQ, dK, dV)}."""
+    B, H = q.shape[:2]
+    return {(b, h): backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal,
+                                  block_mask, mask_block)
+            for (b, h) in _heads(B, H, heads)}
