@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of exact attention (forward + backward) on one MI355X.
+
+One step = one forward pass and one backward pass of the whole path
+(fused online-softmax forward writing O and LSE; D pre-pass, dK/dV pass and
+dQ pass of the backward) over one batch of seeded synthetic inputs already
+resident in HBM.  The default workload is the long-context causal shape
+B=4, H=40, N=8192, d=128 in bf16 (Q, K, V, dO iid N(0,1) x 0.5).
+
+FLOPs follow the convention of the FlashAttention-2 notes ("Reproducibility
+notes"): forward 4 B H N^2 d, backward 2.5x forward, halved for causal,
+scaled by the realized block density for block-sparse masks.
+
+Prints ONE JSON line on stdout (rank 0); anything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd/bwd attention TFLOP/s + % of bf16 MFMA peak, N=1k–16k, d=64/128"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flop_counts(w, mask):
+    """(forward, backward) FLOPs of one step by the pages' convention."""
+    f = 4.0 * w["B"] * w["H"] * w["N"] ** 2 * w["d"]
+    if w["causal"]:
+        f *= 0.5
+    if mask is not None:
+        f *= float(mask.float().mean())
+    return f, (2.5 * f if w["backward"] else 0.0)
+
+
+def kernel_flops(w, mask):
+    """Algorithmic FLOPs per launch of each compute kernel: the products the
+    convention counts that this kernel performs (recomputed S and dP inside
+    the dQ pass are not counted)."""
+    unit = 2.0 * w["B"] * w["H"] * w["N"] ** 2 * w["d"]   # one N x N x d product
+    if w["causal"]:
+        unit *= 0.5
+    if mask is not None:
+        unit *= float(mask.float().mean())
+    return {"fwd": 2 * unit, "fwd_f32": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+
+
+def kernel_bytes(w):
+    """Compulsory HBM bytes of the memory-bound D pre-pass: read O and dO, write D."""
+    el = {"bf16": 2, "f16": 2, "f32": 4}[w["dtype"]]
+    rows = w["B"] * w["H"] * w["N"]
+    return {"bwd_pre": rows * (2 * w["d"] * el + 4)}
+
+
+def cpu_baseline(num, heads):
+    """The float64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    from oracle import attention as A
+    from io_aware_exact_flash_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = workloads.WORKLOADS[num]
+    q, k, v, do, mask = workloads.workload_inputs(num)
+    s = float(np.float32(1.0 / math.sqrt(w["d"])))
+    m = None if mask is None else mask.numpy()
+    pairs = workloads.head_subset(w["B"], w["H"], heads, seed=num + 2000)
+    t0 = time.perf_counter()
+    for (b, h) in pairs:
+        qq, kk, vv = (t[b, h].double().numpy() for t in (q, k, v))
+        A.forward_head(qq, kk, vv, s, w["causal"], m)
+        if w["backward"]:
+            A.backward_head(qq, kk, vv, do[b, h].double().numpy(), s, w["causal"], m)
+    dt = time.perf_counter() - t0
+    one = dict(w, B=1, H=1)
+    fl = flop_counts(one, mask)
+    per_head = fl[0] + fl[1]
+    return {"value": per_head * len(pairs) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {w['B'] * w['H']} (batch, head) pairs of the same workload, "
+                      f"forward{'+backward' if w['backward'] else ''} in float64 (NumPy), {dt:.1f} s"}
+
+
+def run_workload(num, steps, warmup, quiet=False):
+    import torch
+    from io_aware_exact_flash_amd import flash, workloads
+
+    w = workloads.WORKLOADS[num]
+    q, k, v, do, mask = workloads.workload_inputs(num)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    gm = None if mask is None else mask.to(dev)
+    s = float(1.0 / math.sqrt(w["d"]))
+    causal = w["causal"]
+
+    def step():
+        if gm is None:
+            o, lse = flash.fwd(q, k, v, scale=s, causal=causal)
+        else:
+            o, lse = flash.blocksparse_fwd(q, k, v, gm, scale=s, causal=causal)
+        e_mid.record()
+        if w["backward"]:
+            if gm is None:
+                flash.bwd(q, k, v, o, do, lse, scale=s, causal=causal, workspace=ws)
+            else:
+                flash.blocksparse_bwd(q, k, v, o, do, lse, gm, scale=s, causal=causal, workspace=ws)
+        return o
+
+    ws = torch.empty(max(1, flash.bwd_workspace_size(w["B"], w["H"], w["N"], w["d"], q.dtype)),
+                     dtype=torch.uint8, device=dev)
+    e_mid = torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    flash.timing_collect()          # drop anything recorded before the timed region
+    flash.timing_enable(True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        e_mid = mids[i]
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    flash.timing_enable(False)
+    kt = flash.timing_collect()
+
+    ms_step = (t1 - t0) * 1e3 / steps
+    fwd_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(steps)) / steps
+    bwd_ms = sum(mids[i].elapsed_time(ends[i]) for i in range(steps)) / steps
+    ff, fb = flop_counts(w, mask)
+    peak = PEAK_TFLOPS[w["dtype"]]
+    kf = kernel_flops(w, mask)
+    kb = kernel_bytes(w)
+    kernels = {}
+    for name, (tot, cnt) in kt.items():
+        if cnt:
+            avg = tot / cnt
+            entry = {"avg_ms": round(avg, 4), "launches": cnt}
+            if name in kf:
+                entry["tflops"] = round(kf[name] / (avg * 1e-3) / 1e12, 2)
+            if name in kb:
+                entry["gbs"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
+            kernels[name] = entry
+    dom = max(kernels, key=lambda n: kt[n][0]) if kernels else None
+    if dom in kf:
+        ach = kf[dom] / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+    elif dom in kb:
+        ach = kb[dom] / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = None
+    res = {
+        "value": (ff + fb) / (ms_step * 1e-3) / 1e12,
+        "ms_per_step": ms_step,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "fwd_tflops": ff / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": (fb / (bwd_ms * 1e-3) / 1e12) if fb else None,
+        "peak": peak, "kernels": kernels, "roofline": roof,
+        "density": None if mask is None else float(mask.float().mean()),
+    }
+    res["fwd_frac_of_peak"] = res["fwd_tflops"] / peak
+    res["bwd_frac_of_peak"] = res["bwd_tflops"] / peak if fb else None
+    if not quiet:
+        log(f"workload {num} ({w['name']}): {ms_step:.3f} ms/step, fwd {res['fwd_tflops']:.1f} TF/s "
+            f"({100 * res['fwd_frac_of_peak']:.1f}%), bwd "
+            + (f"{res['bwd_tflops']:.1f} TF/s ({100 * res['bwd_frac_of_peak']:.1f}%)" if fb else "-")
+            + f", kernels {kernels}")
+    del q, k, v, do, ws
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="workload timed for the JSON line (default 4: 4x40x8192x128 causal bf16)")
+    ap.add_argument("--all", action="store_true", help="also time every other workload (stderr lines)")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="(batch, head) pairs the oracle baseline runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; run one process per GPU instead).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device (MI355X); none is visible.", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+
+    if args.all:
+        for num in (1, 2, 3, 5, 4):
+            if num != args.workload:
+                w, r = run_workload(num, args.steps, args.warmup)
+                log(json.dumps({"workload": num, **{k: v for k, v in r.items()}}))
+    w, r = run_workload(args.workload, args.steps, args.warmup)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_heads)
+    line = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']} attention, B={w['B']} H={w['H']} N={w['N']} d={w['d']} "
+                               f"{w['dtype']}, {'causal' if w['causal'] else 'non-causal'}"
+                               + (", block-sparse" if w["density"] else "")
+                               + (", forward+backward" if w["backward"] else ", forward"),
+                   "B": w["B"], "H": w["H"], "N": w["N"], "d": w["d"], "causal": w["causal"],
+                   "parallelism": "single-gpu"},
+        "fwd_tflops": round(r["fwd_tflops"], 2),
+        "bwd_tflops": None if r["bwd_tflops"] is None else round(r["bwd_tflops"], 2),
+        "fwd_frac_of_peak": round(r["fwd_frac_of_peak"], 4),
+        "bwd_frac_of_peak": None if r["bwd_frac_of_peak"] is None else round(r["bwd_frac_of_peak"], 4),
+        "kernels": r["kernels"],
+        "roofline": r["roofline"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

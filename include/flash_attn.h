@@ -1,0 +1,168 @@
+/*
+ * flash_attn.h -- C ABI of the gfx950 exact-attention library (libflashattn.so)
+ *
+ * Exact softmax attention for one MI355X GPU:
+ *     S = scale * Q K^T,  P = softmax_row(S),  O = P V,  LSE_i = ln sum_j exp(S_ij)
+ * computed in one fused pass whose online-softmax statistics keep S and P
+ * off HBM, with a backward pass that recomputes them from Q, K, V and LSE.
+ *
+ * Sources the operations follow (titles of the pages, with the section,
+ * equation or algorithm):
+ *   [FA2]  FlashAttention-2 reading notes (zhongzhuzhou.org): Algorithm 1
+ *          (forward), Algorithm 2 (backward), eqs. (5)-(7) online softmax,
+ *          eqs. (10)-(16) deferred normalisation and log-sum-exp, eq. (17)
+ *          and eqs. (27)-(30) softmax Jacobian, "Causal mask optimisation",
+ *          "Reproducibility notes" (FLOP convention).
+ *   [FA1]  FlashAttention paper summary (zhaifeiyue.github.io/papers/
+ *          2205.14135): Technique 1 (tiling), Technique 2 (recomputation,
+ *          D_i = do_i . o_i), Block-Sparse FlashAttention.
+ *   [WALK] FlashAttention walkthrough (bluuewhale.github.io/posts/
+ *          flash-attention-en): "How Attention Is Computed" (scaled scores),
+ *          "Block-Sparse FlashAttention" (mask M in {0,1}^{Tr x Tc}).
+ *
+ * Common conventions
+ * ------------------
+ * Layout.  Every per-token tensor (q, k, v, o, dout, dq, dk, dv) is a dense,
+ *   contiguous [B][H][N][d] array of `dtype` elements (d innermost).  LSE is
+ *   a dense [B][H][N] float32 array.  Queries and keys share one length N.
+ * Pointers.  All tensor, mask and workspace pointers are DEVICE pointers,
+ *   owned by the caller, 16-byte aligned, and must stay valid until the
+ *   stream reaches the enqueued work.  The library never allocates or frees
+ *   device memory and keeps no pointer after a call returns.
+ * Streams.  Every call enqueues its kernels on `stream` (0 = null stream)
+ *   and returns without synchronising.
+ * Domain.  d in {64, 128}; N >= 0 (any value, no tile-multiple needed);
+ *   B*H*ceil(N/32) < 2^31; scale finite and > 0; causal in {0, 1}
+ *   (causal keeps key j for query i iff j <= i).  FA_F32 is accepted by the
+ *   forward calls only; FA_F16 and FA_BF16 by all calls.  Arithmetic is
+ *   float32 throughout (scores, statistics, accumulators); for 16-bit inputs
+ *   the probabilities are rounded to the input type only as an operand of
+ *   the P V product (and P, dS of the backward products).
+ * Empty problems.  B*H*N == 0 returns FA_OK and launches nothing.
+ * Rows with no allowed key (possible only with a block mask whose diagonal
+ *   entry is 0) give O = 0, LSE = -inf and zero gradient contributions.
+ * Errors.  Status codes only, never an abort.  All argument checks finish
+ *   before any HIP call, so an invalid call has no effect on the device.  A
+ *   failed kernel launch returns FA_ERR_HIP.  flash_attn_last_error() gives
+ *   a thread-local description of the last non-OK status on the calling
+ *   thread.  Faults inside kernels surface later, at the caller's
+ *   synchronisation, as HIP errors.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, negative size, bad scale/flag */
+  FA_ERR_UNSUPPORTED = 2,        /* valid but outside the supported domain (d, dtype, mask block) */
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,/* backward workspace smaller than flash_attn_bwd_workspace_size() */
+  FA_ERR_HIP = 4                 /* a HIP launch failed; see flash_attn_last_error() */
+} fa_status;
+
+typedef enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* Version of this ABI (incremented on any signature or semantic change). */
+int flash_attn_abi_version(void);
+
+/*
+ * Forward pass [FA2 Algorithm 1; FA2 eqs. (10)-(15)].
+ *   q, k, v  in   [B][H][N][d] dtype
+ *   o        out  [B][H][N][d] dtype     O = softmax(scale Q K^T (masked)) V
+ *   lse      out  [B][H][N]    float32   natural-log log-sum-exp of each row
+ *                                         of scale Q K^T over allowed keys
+ * causal = 1 masks keys after the query [FA2 "Causal mask optimisation"].
+ */
+fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype,
+                         const void* q, const void* k, const void* v,
+                         float scale, int causal,
+                         void* o, float* lse, hipStream_t stream);
+
+/*
+ * Device workspace bytes flash_attn_bwd / flash_attn_blocksparse_bwd need:
+ * one float32 per query row for D_i = rowsum(dO o O), rounded up to 256.
+ * Returns 0 for empty problems; never fails.
+ */
+size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Backward pass [FA2 Algorithm 2; FA2 eqs. (16), (17), (27)-(30);
+ * FA1 Technique 2].
+ *   q, k, v, o, dout  in   [B][H][N][d] dtype   (o, lse: the forward's outputs)
+ *   lse               in   [B][H][N] float32
+ *   dq, dk, dv        out  [B][H][N][d] dtype   gradients of sum(O o dout)
+ *   workspace         scratch, >= flash_attn_bwd_workspace_size() bytes;
+ *                     contents on entry are ignored and left undefined.
+ * scale and causal must equal the forward's.  dtype FA_F32 is unsupported.
+ */
+fa_status flash_attn_bwd(int B, int H, int N, int d, fa_dtype dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float scale, int causal,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block-sparse forward [FA1 "Block-Sparse FlashAttention"; WALK
+ * "Block-Sparse FlashAttention"]: as flash_attn_fwd, but key j is visible to
+ * query i only if block_mask[i / mask_block][j / mask_block] != 0, and tiles
+ * of zero mask blocks are skipped without being loaded.
+ *   block_mask  in  device uint8 [T][T], T = ceil(N / mask_block), row-major,
+ *               shared by every (batch, head); nonzero = keep.
+ *   mask_block  tokens per mask entry; must be 128 (FA_ERR_UNSUPPORTED else).
+ * causal may be combined with the mask (both must allow a key).
+ */
+fa_status flash_attn_blocksparse_fwd(int B, int H, int N, int d, fa_dtype dtype,
+                                     const void* q, const void* k, const void* v,
+                                     float scale, int causal,
+                                     const uint8_t* block_mask, int mask_block,
+                                     void* o, float* lse, hipStream_t stream);
+
+/*
+ * Block-sparse backward: the exact gradient of the masked attention above
+ * (the pages give the sparse forward only; this is the gradient of the same
+ * function), skipping the same zero tiles.  Arguments as flash_attn_bwd plus
+ * the mask as in flash_attn_blocksparse_fwd.
+ */
+fa_status flash_attn_blocksparse_bwd(int B, int H, int N, int d, fa_dtype dtype,
+                                     const void* q, const void* k, const void* v,
+                                     const void* o, const void* dout, const float* lse,
+                                     float scale, int causal,
+                                     const uint8_t* block_mask, int mask_block,
+                                     void* dq, void* dk, void* dv,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * Per-kernel timing (diagnostics; not part of the method).  While enabled,
+ * every kernel the library launches is bracketed by two HIP events recorded
+ * on its launch stream.  flash_attn_timing_collect waits for the recorded
+ * events, writes for each kernel class k < n the summed milliseconds and
+ * launch count since the previous collect, and forgets them.  Kernel
+ * classes: 0 forward (16-bit), 1 forward (float32), 2 backward D pre-pass,
+ * 3 backward dK/dV pass, 4 backward dQ pass; flash_attn_kernel_name(k)
+ * names them.  Events are created on first use and reused; no device
+ * memory is allocated.  Process-wide, guarded by a mutex.
+ */
+fa_status flash_attn_timing_enable(int enable);
+fa_status flash_attn_timing_collect(double* total_ms, int* launches, int n);
+const char* flash_attn_kernel_name(int kernel);
+
+/* Static name of a status code ("FA_OK", ...). */
+const char* flash_attn_status_string(fa_status status);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* flash_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASH_ATTN_H */

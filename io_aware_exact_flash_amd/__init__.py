@@ -1,0 +1,20 @@
+"""Exact IO-aware attention for MI355X (gfx950).
+
+The compute lives in ``libflashattn.so`` (HIP kernels behind a C ABI declared
+in ``include/flash_attn.h``); ``flash`` is its ctypes binding and
+``workloads`` the seeded synthetic inputs.  Importing the package loads
+nothing; the library is loaded on the first call and its absence is an
+error, never a fallback.
+"""
+from .flash import (  # noqa: F401
+    FlashAttnError,
+    blocksparse_bwd,
+    blocksparse_fwd,
+    bwd,
+    bwd_workspace_size,
+    fwd,
+    lib,
+)
+
+__all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "lib",
+           "FlashAttnError"]

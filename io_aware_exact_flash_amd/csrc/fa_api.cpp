@@ -1,0 +1,303 @@
+// C ABI of libflashattn.so: argument validation, shape bookkeeping and
+// dispatch to the gfx950 kernels.  Every check runs before the first HIP
+// call, so an invalid call never touches the device.
+#include "../../include/flash_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fa_kernels.hpp"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fa_status fail(fa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Problem {
+  int B, H, N, d;
+  fa_dtype dtype;
+  bool empty;
+  int bh;
+};
+
+// Shape/scalar checks shared by every entry point.
+fa_status check_common(const char* fn, int B, int H, int N, int d, fa_dtype dtype, float scale,
+                       int causal, bool backward, Problem* p) {
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: negative size (B=%d H=%d N=%d)", fn, B, H, N);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: scale must be finite and > 0 (got %g)", fn, (double)scale);
+  if (causal != 0 && causal != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1 (got %d)", fn, causal);
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s: head dimension %d not supported (64 or 128)", fn, d);
+  if (backward && dtype == FA_F32)
+    return fail(FA_ERR_UNSUPPORTED, "%s: float32 backward is not supported", fn);
+  const long long bh = (long long)B * H;
+  const long long blocks = bh * ((N + 31LL) / 32);
+  if (blocks >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "%s: problem too large (B*H*ceil(N/32) = %lld)", fn, blocks);
+  p->B = B;
+  p->H = H;
+  p->N = N;
+  p->d = d;
+  p->dtype = dtype;
+  p->bh = (int)bh;
+  p->empty = (bh == 0 || N == 0);
+  return FA_OK;
+}
+
+fa_status check_ptrs(const char* fn, const void* const* ptrs, const char* const* names, int count) {
+  for (int i = 0; i < count; ++i) {
+    if (!ptrs[i]) return fail(FA_ERR_INVALID_ARGUMENT, "%s: %s is null", fn, names[i]);
+    if (!aligned16(ptrs[i]))
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  return FA_OK;
+}
+
+fa_status check_mask(const char* fn, const uint8_t* mask, int mask_block) {
+  if (!mask) return fail(FA_ERR_INVALID_ARGUMENT, "%s: block_mask is null", fn);
+  if (mask_block != fa::kMaskBlockTokens)
+    return fail(FA_ERR_UNSUPPORTED, "%s: mask_block %d not supported (must be 128)", fn, mask_block);
+  return FA_OK;
+}
+
+fa_status hip_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+}
+
+size_t workspace_bytes(long long bh, long long n) {
+  size_t b = (size_t)bh * (size_t)n * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+fa_status run_fwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                  const void* k, const void* v, float scale, int causal, const uint8_t* mask,
+                  int mask_block, bool sparse, void* o, float* lse, hipStream_t stream) {
+  Problem p;
+  fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, false, &p);
+  if (s != FA_OK) return s;
+  if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
+  if (p.empty) return FA_OK;
+  const void* ptrs[] = {q, k, v, o, lse};
+  const char* names[] = {"q", "k", "v", "o", "lse"};
+  if ((s = check_ptrs(fn, ptrs, names, 5)) != FA_OK) return s;
+
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.mask = sparse ? mask : nullptr;
+  a.mask_t = (N + fa::kMaskBlockTokens - 1) / fa::kMaskBlockTokens;
+  a.n = N;
+  a.c = scale * 1.4426950408889634f;
+  hipError_t e = (dtype == FA_F32)
+                     ? fa::launch_fwd_f32(d, causal != 0, sparse, p.bh, a, stream)
+                     : fa::launch_fwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0,
+                                      sparse, p.bh, a, stream);
+  return hip_status(fn, e);
+}
+
+fa_status run_bwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                  const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  float scale, int causal, const uint8_t* mask, int mask_block, bool sparse,
+                  void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Problem p;
+  fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, true, &p);
+  if (s != FA_OK) return s;
+  if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
+  if (p.empty) return FA_OK;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
+  const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace"};
+  if ((s = check_ptrs(fn, ptrs, names, 10)) != FA_OK) return s;
+  const size_t need = workspace_bytes(p.bh, N);
+  if (ws_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dvec = static_cast<float*>(ws);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.mask = sparse ? mask : nullptr;
+  a.mask_t = (N + fa::kMaskBlockTokens - 1) / fa::kMaskBlockTokens;
+  a.n = N;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, sparse,
+                                p.bh, a, stream);
+  return hip_status(fn, e);
+}
+
+// ---------------------------------------------------------------- timing
+struct Mark {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<hipEvent_t> g_event_pool;
+std::vector<Mark> g_marks;
+int g_open_kernel = -1;
+hipEvent_t g_open_start = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+const char* kKernelNames[fa::kNumKernels] = {"fwd", "fwd_f32", "bwd_pre", "bwd_dkdv", "bwd_dq"};
+
+}  // namespace
+
+namespace fa {
+void timing_begin(int kernel, hipStream_t st) {
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  if (!g_timing_on) return;
+  g_open_start = take_event();
+  g_open_kernel = kernel;
+  if (g_open_start) hipEventRecord(g_open_start, st);
+}
+void timing_end(int kernel, hipStream_t st) {
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  if (!g_timing_on || g_open_kernel != kernel || !g_open_start) return;
+  hipEvent_t stop = take_event();
+  if (!stop) return;
+  hipEventRecord(stop, st);
+  g_marks.push_back({kernel, g_open_start, stop});
+  g_open_start = nullptr;
+  g_open_kernel = -1;
+}
+}  // namespace fa
+
+FA_EXPORT fa_status flash_attn_timing_enable(int enable) {
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  g_timing_on = enable != 0;
+  return FA_OK;
+}
+
+FA_EXPORT fa_status flash_attn_timing_collect(double* total_ms, int* launches, int n) {
+  if ((!total_ms || !launches) && n > 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "flash_attn_timing_collect: null output array");
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  fa_status st = FA_OK;
+  for (const Mark& m : g_marks) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(m.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, m.start, m.stop);
+    if (e != hipSuccess && st == FA_OK)
+      st = fail(FA_ERR_HIP, "flash_attn_timing_collect: %s", hipGetErrorString(e));
+    if (m.kernel < n && e == hipSuccess) {
+      total_ms[m.kernel] += ms;
+      launches[m.kernel] += 1;
+    }
+    g_event_pool.push_back(m.start);
+    g_event_pool.push_back(m.stop);
+  }
+  g_marks.clear();
+  return st;
+}
+
+FA_EXPORT const char* flash_attn_kernel_name(int kernel) {
+  return (kernel >= 0 && kernel < fa::kNumKernels) ? kKernelNames[kernel] : "";
+}
+
+FA_EXPORT int flash_attn_abi_version(void) { return 1; }
+
+FA_EXPORT fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                                   const void* k, const void* v, float scale, int causal, void* o,
+                                   float* lse, hipStream_t stream) {
+  return run_fwd("flash_attn_fwd", B, H, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o,
+                 lse, stream);
+}
+
+FA_EXPORT size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {
+  (void)d;
+  (void)dtype;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return workspace_bytes((long long)B * H, N);
+}
+
+FA_EXPORT fa_status flash_attn_bwd(int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                                   const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, float scale, int causal, void* dq, void* dk,
+                                   void* dv, void* workspace, size_t workspace_bytes_,
+                                   hipStream_t stream) {
+  return run_bwd("flash_attn_bwd", B, H, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr,
+                 0, false, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+FA_EXPORT fa_status flash_attn_blocksparse_fwd(int B, int H, int N, int d, fa_dtype dtype,
+                                               const void* q, const void* k, const void* v,
+                                               float scale, int causal, const uint8_t* block_mask,
+                                               int mask_block, void* o, float* lse,
+                                               hipStream_t stream) {
+  return run_fwd("flash_attn_blocksparse_fwd", B, H, N, d, dtype, q, k, v, scale, causal, block_mask,
+                 mask_block, true, o, lse, stream);
+}
+
+FA_EXPORT fa_status flash_attn_blocksparse_bwd(int B, int H, int N, int d, fa_dtype dtype,
+                                               const void* q, const void* k, const void* v,
+                                               const void* o, const void* dout, const float* lse,
+                                               float scale, int causal, const uint8_t* block_mask,
+                                               int mask_block, void* dq, void* dk, void* dv,
+                                               void* workspace, size_t workspace_bytes_,
+                                               hipStream_t stream) {
+  return run_bwd("flash_attn_blocksparse_bwd", B, H, N, d, dtype, q, k, v, o, dout, lse, scale,
+                 causal, block_mask, mask_block, true, dq, dk, dv, workspace, workspace_bytes_,
+                 stream);
+}
+
+FA_EXPORT const char* flash_attn_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_UNKNOWN_STATUS";
+}
+
+FA_EXPORT const char* flash_attn_last_error(void) { return g_last_error.c_str(); }

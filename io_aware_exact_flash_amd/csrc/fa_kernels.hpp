@@ -1,0 +1,63 @@
+// Kernel argument blocks and host-side launchers shared by the kernel
+// translation units and the C ABI in fa_api.cpp.  Nothing here is exported.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+constexpr int kMaskBlockTokens = 128;  // tokens per block-mask entry
+
+// Forward: one head is N x d, heads [B*H] contiguous.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;            // [B*H*N] natural-log log-sum-exp
+  const uint8_t* mask;   // [T][T] block mask or nullptr
+  int mask_t;            // T = ceil(N / 128)
+  int n;                 // tokens per head
+  int nqb;               // query blocks per head
+  int nblk;              // total workgroups
+  float c;               // scale * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;      // [B*H*N]
+  float* dvec;           // [B*H*N] rowsum(dO o O), written by the pre-pass
+  void* dq;
+  void* dk;
+  void* dv;
+  const uint8_t* mask;
+  int mask_t;
+  int n;
+  int nblk_q;            // workgroups of the dQ pass
+  int nqb;               // query blocks per head (dQ pass)
+  int nblk_kv;           // workgroups of the dK/dV pass
+  int nkb;               // key blocks per head (dK/dV pass)
+  float scale;
+  float c;               // scale * log2(e)
+};
+
+// Kernel classes for the optional per-kernel timing hooks.
+enum KernelId : int { kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kNumKernels = 5 };
+
+// Bracket one launch with events on its stream when timing is enabled
+// (no-ops otherwise).  Defined in fa_api.cpp.
+void timing_begin(int kernel, hipStream_t st);
+void timing_end(int kernel, hipStream_t st);
+
+// Launchers return hipGetLastError() after the launch.
+hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st);
+hipError_t launch_fwd_f32(int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st);
+hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st);
+
+}  // namespace fa

@@ -1,0 +1,188 @@
+"""Thin ctypes binding of libflashattn.so (argument marshalling only).
+
+Every function here checks tensor metadata, allocates outputs with torch on
+the inputs' device, and calls the C entry point of the same name on torch's
+current HIP stream.  All arithmetic happens in the gfx950 kernels; there is
+no fallback: if the library is missing or the tensors are not on a HIP
+device the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FLASHATTN_LIB", os.path.join(_HERE, "libflashattn.so"))
+
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_HIP = range(5)
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+MASK_BLOCK = 128
+
+_DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+# exported symbol -> (restype, argtypes)
+_I, _P, _F, _Z, _U8P = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "flash_attn_abi_version": (_I, []),
+    "flash_attn_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _P, _P, _P]),
+    "flash_attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "flash_attn_bwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _P, _Z, _P]),
+    "flash_attn_blocksparse_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _U8P, _I, _P, _P, _P]),
+    "flash_attn_blocksparse_bwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _U8P, _I,
+                                        _P, _P, _P, _P, _Z, _P]),
+    "flash_attn_status_string": (ctypes.c_char_p, [_I]),
+    "flash_attn_last_error": (ctypes.c_char_p, []),
+    "flash_attn_timing_enable": (_I, [_I]),
+    "flash_attn_timing_collect": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), _I]),
+    "flash_attn_kernel_name": (ctypes.c_char_p, [_I]),
+}
+KERNELS = 5  # timing classes: fwd, fwd_f32, bwd_pre, bwd_dkdv, bwd_dq
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argtypes set; raises if it was not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                   "(python -c 'import __graft_entry__ as g; g.build()')")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                f = getattr(h, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().flash_attn_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FlashAttnError(status, lib().flash_attn_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _shape(q: torch.Tensor, *others: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if not q.is_cuda:
+        raise ValueError("tensors must live on a HIP device (no CPU path exists)")
+    for t in (q,) + others:
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v (and o, dout) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    return B, H, N, d, _DT[q.dtype]
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def _lse_ok(lse, q):
+    B, H, N, _ = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on the inputs' device")
+
+
+def _mask_ok(mask, q):
+    N = q.shape[2]
+    T = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    if mask.shape != (T, T) or mask.dtype != torch.uint8 or mask.device != q.device or not mask.is_contiguous():
+        raise ValueError(f"block_mask must be a contiguous uint8 [{T}, {T}] tensor on the inputs' device")
+
+
+def timing_enable(on: bool = True):
+    _check(lib().flash_attn_timing_enable(int(bool(on))))
+
+
+def timing_collect():
+    """{kernel name: (total ms, launches)} since the last collect."""
+    ms = (ctypes.c_double * KERNELS)()
+    cnt = (ctypes.c_int * KERNELS)()
+    _check(lib().flash_attn_timing_collect(ms, cnt, KERNELS))
+    return {lib().flash_attn_kernel_name(i).decode(): (ms[i], cnt[i]) for i in range(KERNELS)}
+
+
+def fwd(q, k, v, scale=None, causal=False):
+    """(O, LSE) = flash_attn_fwd(q, k, v, scale, causal)."""
+    B, H, N, d, dt = _shape(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib().flash_attn_fwd(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                _scale(scale, d), int(bool(causal)), o.data_ptr(), lse.data_ptr(),
+                                _stream(q)))
+    return o, lse
+
+
+def bwd_workspace_size(B, H, N, d, dtype=torch.bfloat16) -> int:
+    return int(lib().flash_attn_bwd_workspace_size(B, H, N, d, _DT[dtype]))
+
+
+def _workspace(q):
+    B, H, N, d = q.shape
+    nbytes = bwd_workspace_size(B, H, N, d, q.dtype)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device), nbytes
+
+
+def bwd(q, k, v, o, dout, lse, scale=None, causal=False, workspace=None):
+    """(dQ, dK, dV) = flash_attn_bwd(q, k, v, o, dout, lse, scale, causal)."""
+    B, H, N, d, dt = _shape(q, k, v, o, dout)
+    _lse_ok(lse, q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws, nbytes = _workspace(q) if workspace is None else (workspace, workspace.numel())
+    _check(lib().flash_attn_bwd(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                dout.data_ptr(), lse.data_ptr(), _scale(scale, d), int(bool(causal)),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,
+                                _stream(q)))
+    return dq, dk, dv
+
+
+def blocksparse_fwd(q, k, v, block_mask, scale=None, causal=False):
+    """(O, LSE) = flash_attn_blocksparse_fwd(..., block_mask [T, T] uint8, 128)."""
+    B, H, N, d, dt = _shape(q, k, v)
+    _mask_ok(block_mask, q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib().flash_attn_blocksparse_fwd(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            _scale(scale, d), int(bool(causal)), block_mask.data_ptr(),
+                                            MASK_BLOCK, o.data_ptr(), lse.data_ptr(), _stream(q)))
+    return o, lse
+
+
+def blocksparse_bwd(q, k, v, o, dout, lse, block_mask, scale=None, causal=False, workspace=None):
+    """(dQ, dK, dV) = flash_attn_blocksparse_bwd(...)."""
+    B, H, N, d, dt = _shape(q, k, v, o, dout)
+    _lse_ok(lse, q)
+    _mask_ok(block_mask, q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws, nbytes = _workspace(q) if workspace is None else (workspace, workspace.numel())
+    _check(lib().flash_attn_blocksparse_bwd(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                            _scale(scale, d), int(bool(causal)), block_mask.data_ptr(),
+                                            MASK_BLOCK, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                            ws.data_ptr(), nbytes, _stream(q)))
+    return dq, dk, dv

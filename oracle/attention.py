@@ -142,3 +142,19 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=MASK_
     return {(b, h): backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal,
                                   block_mask, mask_block)
             for (b, h) in _heads(B, H, heads)}
+
+
+def grad_q_rows(q, k, v, do, scale, causal=False, block_mask=None, mask_block=MASK_BLOCK, rows=None):
+    """dQ for the selected query rows only: each row of dQ depends on its own
+    row of P and dP (and on all of K and V), so large problems can be checked
+    row by row."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    r = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    P = probs_head(q, k, scale, causal, block_mask, mask_block, r)
+    dP = do[r] @ v.T
+    rowdot = (P * dP).sum(axis=1)
+    dS = P * (dP - rowdot[:, None])
+    return scale * (dS @ k)

@@ -1,0 +1,142 @@
+"""The C-ABI library loads, exports what include/flash_attn.h declares, and
+rejects invalid calls with the documented status codes before any HIP call.
+
+CPU only: no call here reaches a kernel launch (every case fails validation
+or is an empty problem), so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_exact_flash_amd import flash
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+FAKE = 0x10000        # 16-byte aligned, never dereferenced: validation fails first
+FAKE_MISALIGNED = 0x10008
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flash_attn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_blocksparse_fwd",
+                     "flash_attn_blocksparse_bwd", "flash_attn_bwd_workspace_size"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = flash.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in flash.SIGNATURES, f"binding lacks a signature for {name}"
+
+
+def test_abi_version_and_status_strings():
+    lib = flash.lib()
+    assert lib.flash_attn_abi_version() == 1
+    for code, name in enumerate(["FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED",
+                                 "FA_ERR_WORKSPACE_TOO_SMALL", "FA_ERR_HIP"]):
+        assert flash.status_string(code) == name
+
+
+def _fwd(**kw):
+    a = dict(B=1, H=1, N=256, d=64, dt=flash.FA_BF16, q=FAKE, k=FAKE, v=FAKE, scale=0.125,
+             causal=0, o=FAKE, lse=FAKE, stream=None)
+    a.update(kw)
+    return flash.lib().flash_attn_fwd(a["B"], a["H"], a["N"], a["d"], a["dt"], a["q"], a["k"], a["v"],
+                                      a["scale"], a["causal"], a["o"], a["lse"], a["stream"])
+
+
+def _bwd(ws_bytes=None, **kw):
+    a = dict(B=1, H=2, N=256, d=128, dt=flash.FA_F16, scale=0.1, causal=1)
+    a.update(kw)
+    need = flash.lib().flash_attn_bwd_workspace_size(a["B"], a["H"], a["N"], a["d"], a["dt"])
+    ptr = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE)
+    ptr.update({k: v for k, v in kw.items() if k in ptr})
+    return flash.lib().flash_attn_bwd(a["B"], a["H"], a["N"], a["d"], a["dt"], ptr["q"], ptr["k"],
+                                      ptr["v"], ptr["o"], ptr["do"], ptr["lse"], a["scale"], a["causal"],
+                                      ptr["dq"], ptr["dk"], ptr["dv"], ptr["ws"],
+                                      need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), flash.FA_ERR_UNSUPPORTED),
+    (dict(d=32), flash.FA_ERR_UNSUPPORTED),
+    (dict(B=-1), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=-5), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=7), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-1.0), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(lse=None), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(v=FAKE_MISALIGNED), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 12), flash.FA_ERR_UNSUPPORTED),
+])
+def test_forward_validation(kw, code):
+    assert _fwd(**kw) == code
+    assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_fwd:")
+
+
+def test_forward_empty_problem_is_ok_without_launch():
+    assert _fwd(B=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
+    assert _fwd(N=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
+    # validation of scalars still applies to empty problems
+    assert _fwd(N=0, d=80) == flash.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=flash.FA_F32), flash.FA_ERR_UNSUPPORTED),
+    (dict(d=256), flash.FA_ERR_UNSUPPORTED),
+    (dict(do=None), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(dk=FAKE_MISALIGNED), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(causal=-1), flash.FA_ERR_INVALID_ARGUMENT),
+])
+def test_backward_validation(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_backward_workspace_too_small():
+    lib = flash.lib()
+    need = lib.flash_attn_bwd_workspace_size(1, 2, 256, 128, flash.FA_F16)
+    assert need == 2 * 256 * 4  # one float32 per query row, rounded to 256 bytes
+    assert _bwd(ws_bytes=need - 1) == flash.FA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.flash_attn_bwd_workspace_size(0, 2, 256, 128, flash.FA_F16) == 0
+    assert lib.flash_attn_bwd_workspace_size(1, 1, 1000, 64, flash.FA_BF16) == 4096
+
+
+def test_blocksparse_validation():
+    lib = flash.lib()
+    args = (1, 1, 256, 64, flash.FA_F16, FAKE, FAKE, FAKE, 0.125, 0)
+    assert lib.flash_attn_blocksparse_fwd(*args, None, 128, FAKE, FAKE, None) == flash.FA_ERR_INVALID_ARGUMENT
+    assert lib.flash_attn_blocksparse_fwd(*args, FAKE, 64, FAKE, FAKE, None) == flash.FA_ERR_UNSUPPORTED
+    bargs = (1, 1, 256, 64, flash.FA_F16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, 0)
+    assert lib.flash_attn_blocksparse_bwd(*bargs, FAKE, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                          None) == flash.FA_ERR_UNSUPPORTED
+    assert lib.flash_attn_blocksparse_bwd(*bargs, None, 128, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                          None) == flash.FA_ERR_INVALID_ARGUMENT
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        flash.fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(flash, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(flash, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        flash.lib()

@@ -396,3 +396,23 @@ def test_finite_differences_catch_planted_mistakes(bug):
             assert abs(num - Gg[idx]) <= 1e-6 * max(1.0, np.abs(Gg).max())
             worst = max(worst, abs(num - Gb[idx]))
     assert worst > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_restricted_dq_by_finite_differences(causal):
+    """grad_q_rows on a subset of rows against central differences."""
+    r = _rng(59)
+    n, d = 6, 3
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    rows = [0, 3, 5]
+    g = A.grad_q_rows(q, k, v, do, 0.6, causal, rows=rows)
+    h = 1e-6
+    for a, i in enumerate(rows):
+        for t in range(d):
+            old = q[i, t]
+            q[i, t] = old + h
+            fp = _loss(q, k, v, do, 0.6, causal, None, 128)
+            q[i, t] = old - h
+            fm = _loss(q, k, v, do, 0.6, causal, None, 128)
+            q[i, t] = old
+            assert abs((fp - fm) / (2 * h) - g[a, t]) <= 1e-6 * max(1.0, np.abs(g).max())

@@ -1,0 +1,200 @@
+"""GPU parity: the C-ABI kernels against the float64 oracle, element by element.
+
+Sizes are small enough for the oracle to finish in seconds yet span several
+key tiles (64 keys at d=128, 128 at d=64), several 128-row query blocks and a
+ragged tail (N not a multiple of any tile).
+"""
+import numpy as np
+import pytest
+import torch
+
+from io_aware_exact_flash_amd import flash, workloads
+from oracle import attention as A
+from tests._parity import REL_RMS, TOL, compare, compare_lse, fp32_scale, make, to64
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _oracle_fwd(f64, s, causal, mask=None):
+    q, k, v = f64[:3]
+    B, H = q.shape[:2]
+    O = np.zeros(q.shape)
+    L = np.zeros(q.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            O[b, h], L[b, h] = A.forward_head(q[b, h], k[b, h], v[b, h], s, causal, mask)
+    return O, L
+
+
+def _oracle_bwd(f64, s, causal, mask=None):
+    q, k, v, do = f64
+    B, H = q.shape[:2]
+    out = [np.zeros(q.shape) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            g = A.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], s, causal, mask)
+            for t in range(3):
+                out[t][b, h] = g[t]
+    return out
+
+
+SHAPES = [(2, 2, 1), (2, 2, 17), (1, 2, 128), (2, 1, 200), (1, 2, 384), (1, 1, 519)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_backward_small(dtype, d, causal, shape):
+    B, H, N = shape
+    seed = 100 + N + d + 7 * causal
+    (q, k, v, do), f64 = make(B, H, N, d, dtype, seed)
+    s = fp32_scale(d)
+    o, lse = flash.fwd(q, k, v, scale=s, causal=causal)
+    dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    O, L = _oracle_fwd(f64, s, causal)
+    tol = TOL[dtype]
+    compare("O", o, O, tol["o"], REL_RMS[dtype])
+    compare_lse("LSE", lse, L, tol["lse"])
+    # the backward takes the GPU's own O and LSE (as a training step would);
+    # the oracle gradient is the exact gradient at the same inputs
+    gQ, gK, gV = _oracle_bwd(f64, s, causal)
+    compare("dQ", dq, gQ, tol["grad"], REL_RMS[dtype])
+    compare("dK", dk, gK, tol["grad"], REL_RMS[dtype])
+    compare("dV", dv, gV, tol["grad"], REL_RMS[dtype])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 256), (2, 3, 100), (1, 2, 33), (1, 1, 1)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_forward_float32(d, causal, shape):
+    B, H, N = shape
+    (q, k, v, _), f64 = make(B, H, N, d, "f32", seed=1 + N + d)
+    s = fp32_scale(d)
+    o, lse = flash.fwd(q, k, v, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    O, L = _oracle_fwd(f64, s, causal)
+    compare("O", o, O, TOL["f32"]["o"], REL_RMS["f32"])
+    compare_lse("LSE", lse, L, TOL["f32"]["lse"])
+
+
+def _masks(T, seed):
+    g = torch.Generator().manual_seed(seed)
+    rnd = (torch.rand((T, T), generator=g) < 0.4).to(torch.uint8)
+    rnd.fill_diagonal_(1)
+    return {
+        "random": rnd,
+        "diag": torch.eye(T, dtype=torch.uint8),
+        "ones": torch.ones((T, T), dtype=torch.uint8),
+        "seeded25": workloads.block_mask(T, 0.25, seed),
+    }
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [256, 300, 640])
+@pytest.mark.parametrize("kind", ["random", "diag", "ones", "seeded25"])
+def test_blocksparse(dtype, d, causal, N, kind):
+    B, H = 1, 2
+    T = (N + 127) // 128
+    mask_cpu = _masks(T, seed=N + d)[kind]
+    (q, k, v, do), f64 = make(B, H, N, d, dtype, seed=7 + N + d)
+    s = fp32_scale(d)
+    m = mask_cpu.cuda()
+    o, lse = flash.blocksparse_fwd(q, k, v, m, scale=s, causal=causal)
+    dq, dk, dv = flash.blocksparse_bwd(q, k, v, o, do, lse, m, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    mk = mask_cpu.numpy()
+    O, L = _oracle_fwd(f64, s, causal, mk)
+    tol = TOL[dtype]
+    compare("O", o, O, tol["o"], REL_RMS[dtype])
+    compare_lse("LSE", lse, L, tol["lse"])
+    gQ, gK, gV = _oracle_bwd(f64, s, causal, mk)
+    compare("dQ", dq, gQ, tol["grad"], REL_RMS[dtype])
+    compare("dK", dk, gK, tol["grad"], REL_RMS[dtype])
+    compare("dV", dv, gV, tol["grad"], REL_RMS[dtype])
+
+
+def test_blocksparse_float32_forward():
+    N, d = 384, 64
+    T = 3
+    mask_cpu = _masks(T, 5)["random"]
+    (q, k, v, _), f64 = make(1, 2, N, d, "f32", seed=9)
+    s = fp32_scale(d)
+    o, lse = flash.blocksparse_fwd(q, k, v, mask_cpu.cuda(), scale=s)
+    torch.cuda.synchronize()
+    O, L = _oracle_fwd(f64, s, False, mask_cpu.numpy())
+    compare("O", o, O, TOL["f32"]["o"], REL_RMS["f32"])
+    compare_lse("LSE", lse, L, TOL["f32"]["lse"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rows_without_keys(dtype):
+    """A zero diagonal mask block leaves rows with no allowed key: O = 0,
+    LSE = -inf, and (16-bit) zero gradients for them, no NaN anywhere."""
+    N, d = 256, 64
+    mask_cpu = torch.tensor([[0, 0], [1, 1]], dtype=torch.uint8)
+    (q, k, v, do), f64 = make(1, 1, N, d, dtype, seed=3)
+    s = fp32_scale(d)
+    o, lse = flash.blocksparse_fwd(q, k, v, mask_cpu.cuda(), scale=s)
+    torch.cuda.synchronize()
+    O, L = _oracle_fwd(f64, s, False, mask_cpu.numpy())
+    assert (to64(o)[0, 0, :128] == 0).all()
+    assert np.isneginf(to64(lse)[0, 0, :128]).all()
+    tol = TOL[dtype]
+    compare("O", o, O, tol["o"])
+    compare_lse("LSE", lse, L, tol["lse"])
+    if dtype != "f32":
+        dq, dk, dv = flash.blocksparse_bwd(q, k, v, o, do, lse, mask_cpu.cuda(), scale=s)
+        torch.cuda.synchronize()
+        gQ, gK, gV = _oracle_bwd(f64, s, False, mask_cpu.numpy())
+        assert (to64(dq)[0, 0, :128] == 0).all()
+        compare("dQ", dq, gQ, tol["grad"])
+        compare("dK", dk, gK, tol["grad"])
+        compare("dV", dv, gV, tol["grad"])
+
+
+def test_empty_inputs():
+    for B, H, N in ((0, 2, 64), (1, 0, 64), (1, 2, 0)):
+        q = torch.zeros((B, H, N, 64), dtype=torch.bfloat16, device="cuda")
+        o, lse = flash.fwd(q, q, q)
+        dq, dk, dv = flash.bwd(q, q, q, o, q, lse)
+        torch.cuda.synchronize()
+        assert o.shape == q.shape and lse.shape == (B, H, N) and dq.shape == q.shape
+
+
+def test_large_magnitude_scores_stay_finite():
+    """Scores of magnitude ~1e3 exercise the max subtraction (safe softmax)."""
+    N, d = 300, 128
+    (q, k, v, do), f64 = make(1, 2, N, d, "bf16", seed=21, gain=6.0)
+    s = 1.0
+    o, lse = flash.fwd(q, k, v, scale=s, causal=True)
+    dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_fwd(f64, s, True)
+    compare("O", o, O, TOL["bf16"]["o"])
+    compare_lse("LSE", lse, L, 2e-2)  # |LSE| ~ 1e3: a few float32 ulps of 1e3
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+
+def test_stream_and_repeatability():
+    """Calls run on torch's current stream; two runs give identical bits
+    (no atomics anywhere in the path)."""
+    (q, k, v, do), _ = make(2, 3, 333, 128, "bf16", seed=5)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        o1, l1 = flash.fwd(q, k, v, causal=True)
+        g1 = flash.bwd(q, k, v, o1, do, l1, causal=True)
+    st.synchronize()
+    o2, l2 = flash.fwd(q, k, v, causal=True)
+    g2 = flash.bwd(q, k, v, o2, do, l2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

@@ -1,0 +1,177 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configuration
+``bench.py`` times.
+
+* every (batch, head) of the small workloads (256 tokens fp32; 8x16x1024 bf16)
+  and the forward of every head of 4x32x2048 causal are compared element by
+  element with the oracle; its backward on 16 seeded heads;
+* the two long workloads (4x40x8192 causal, 2x16x16384 block-sparse) compare
+  4 seeded heads (always (0, 0) and (B-1, H-1)) in full, plus 32 sampled
+  query rows of O, LSE and dQ on every head (each such row depends only on
+  its own scores), plus checks that hold at any size on every head:
+  finite outputs, LSE >= every allowed scaled score, sum_j dK_j = 0 and
+  sum_j dV_j = sum_i dO_i (the softmax Jacobian's rows sum to zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+from io_aware_exact_flash_amd import flash, workloads
+from oracle import attention as A
+from tests._parity import REL_RMS, TOL, compare, compare_lse, fp32_scale, to64
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def run(num):
+    """Run workload ``num`` once on the GPU; keep inputs and outputs on the host."""
+    if num in _CACHE:
+        return _CACHE[num]
+    w = workloads.WORKLOADS[num]
+    q, k, v, do, mask = workloads.workload_inputs(num)
+    s = fp32_scale(w["d"])
+    gq, gk, gv, gdo = (t.cuda() for t in (q, k, v, do))
+    gm = mask.cuda() if mask is not None else None
+    if gm is None:
+        o, lse = flash.fwd(gq, gk, gv, scale=s, causal=w["causal"])
+    else:
+        o, lse = flash.blocksparse_fwd(gq, gk, gv, gm, scale=s, causal=w["causal"])
+    out = dict(w=w, s=s, q=q, k=k, v=v, do=do, mask=None if mask is None else mask.numpy(),
+               o=o.cpu(), lse=lse.cpu())
+    if w["backward"]:
+        if gm is None:
+            dq, dk, dv = flash.bwd(gq, gk, gv, o, gdo, lse, scale=s, causal=w["causal"])
+        else:
+            dq, dk, dv = flash.blocksparse_bwd(gq, gk, gv, o, gdo, lse, gm, scale=s, causal=w["causal"])
+        torch.cuda.synchronize()
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            assert torch.isfinite(t).all(), f"{name} has non-finite values"
+        # column sums on the device in float32 (cheap at any size)
+        out["sum_dk"] = dk.float().sum(dim=2).cpu().double().numpy()
+        out["sum_dv"] = dv.float().sum(dim=2).cpu().double().numpy()
+        out["sum_do"] = gdo.float().sum(dim=2).cpu().double().numpy()
+        out["rms_dk"] = dk.float().pow(2).mean(dim=(2, 3)).sqrt().cpu().double().numpy()
+        out["rms_dv"] = dv.float().pow(2).mean(dim=(2, 3)).sqrt().cpu().double().numpy()
+        out.update(dq=dq.cpu(), dk=dk.cpu(), dv=dv.cpu())
+        del dq, dk, dv
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and not torch.isnan(lse).any()
+    del gq, gk, gv, gdo, o, lse
+    torch.cuda.empty_cache()
+    _CACHE.clear()
+    _CACHE[num] = out
+    return out
+
+
+def f64(t, b, h):
+    return t[b, h].to(torch.float64).numpy()
+
+
+def check_heads_full(r, heads, fwd=True, bwd=True):
+    w, s, m = r["w"], r["s"], r["mask"]
+    dt = w["dtype"]
+    tol = TOL[dt]
+    for (b, h) in heads:
+        q, k, v = f64(r["q"], b, h), f64(r["k"], b, h), f64(r["v"], b, h)
+        if fwd:
+            O, L = A.forward_head(q, k, v, s, w["causal"], m)
+            compare(f"O[{b},{h}]", r["o"][b, h], O, tol["o"], REL_RMS[dt])
+            compare_lse(f"LSE[{b},{h}]", r["lse"][b, h], L, tol["lse"])
+        if bwd and w["backward"]:
+            do = f64(r["do"], b, h)
+            gQ, gK, gV = A.backward_head(q, k, v, do, s, w["causal"], m)
+            compare(f"dQ[{b},{h}]", r["dq"][b, h], gQ, tol["grad"], REL_RMS[dt])
+            compare(f"dK[{b},{h}]", r["dk"][b, h], gK, tol["grad"], REL_RMS[dt])
+            compare(f"dV[{b},{h}]", r["dv"][b, h], gV, tol["grad"], REL_RMS[dt])
+
+
+def check_rows_all_heads(r, nrows=32, seed=0):
+    """O, LSE (and dQ) of sampled rows on every head, plus LSE >= allowed scores."""
+    w, s, m = r["w"], r["s"], r["mask"]
+    B, H, N = w["B"], w["H"], w["N"]
+    tol = TOL[w["dtype"]]
+    g = np.random.default_rng(seed)
+    for b in range(B):
+        for h in range(H):
+            rows = np.unique(np.concatenate([[0, N - 1], g.integers(0, N, nrows - 2)]))
+            q, k, v = f64(r["q"], b, h), f64(r["k"], b, h), f64(r["v"], b, h)
+            O, L = A.forward_head(q, k, v, s, w["causal"], m, rows=rows)
+            compare(f"O rows[{b},{h}]", r["o"][b, h][rows], O, tol["o"])
+            compare_lse(f"LSE rows[{b},{h}]", r["lse"][b, h][rows], L, tol["lse"])
+            S = A.scores(q, k, s, w["causal"], m, rows=rows)
+            lse = to64(r["lse"][b, h][rows])
+            assert (np.nan_to_num(S, neginf=-1e300).max(axis=1) <= lse + 1e-3).all()
+            if w["backward"]:
+                dq = A.grad_q_rows(q, k, v, f64(r["do"], b, h), s, w["causal"], m, rows=rows)
+                compare(f"dQ rows[{b},{h}]", r["dq"][b, h][rows], dq, tol["grad"])
+
+
+def check_column_sums(r, verified):
+    """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i on every head; residuals are
+    normalised by sqrt(N) * rms and must stay within 3x the largest seen on
+    the oracle-verified heads (plus a small floor)."""
+    N = r["w"]["N"]
+    res_k = np.abs(r["sum_dk"]).max(axis=-1) / (np.sqrt(N) * r["rms_dk"])
+    res_v = np.abs(r["sum_dv"] - r["sum_do"]).max(axis=-1) / (np.sqrt(N) * r["rms_dv"])
+    for name, res in (("dK", res_k), ("dV", res_v)):
+        ref = max(res[b, h] for (b, h) in verified)
+        worst = res.max()
+        assert worst <= 3 * ref + 0.02, f"{name} column-sum residual {worst:.3e} vs verified {ref:.3e}"
+
+
+def test_workload1_fp32_single_head():
+    r = run(1)
+    check_heads_full(r, [(0, 0)])
+
+
+def test_workload2_every_head():
+    r = run(2)
+    w = r["w"]
+    check_heads_full(r, [(b, h) for b in range(w["B"]) for h in range(w["H"])])
+
+
+def test_workload3_forward_every_head():
+    r = run(3)
+    w = r["w"]
+    check_heads_full(r, [(b, h) for b in range(w["B"]) for h in range(w["H"])], bwd=False)
+
+
+def test_workload3_backward_subset_and_rows():
+    r = run(3)
+    w = r["w"]
+    heads = workloads.head_subset(w["B"], w["H"], 16, seed=3 + 2000)
+    check_heads_full(r, heads, fwd=False)
+    check_column_sums(r, heads)
+
+
+def test_workload4_long_context_heads():
+    r = run(4)
+    w = r["w"]
+    heads = workloads.head_subset(w["B"], w["H"], 4, seed=4 + 2000)
+    check_heads_full(r, heads[:2])
+
+
+def test_workload4_long_context_rows_and_sums():
+    r = run(4)
+    w = r["w"]
+    heads = workloads.head_subset(w["B"], w["H"], 4, seed=4 + 2000)
+    check_heads_full(r, heads[2:])
+    check_rows_all_heads(r, seed=4)
+    check_column_sums(r, heads)
+
+
+def test_workload5_blocksparse_heads():
+    r = run(5)
+    w = r["w"]
+    heads = workloads.head_subset(w["B"], w["H"], 4, seed=5 + 2000)
+    check_heads_full(r, heads[:2])
+
+
+def test_workload5_blocksparse_rows_and_sums():
+    r = run(5)
+    w = r["w"]
+    heads = workloads.head_subset(w["B"], w["H"], 4, seed=5 + 2000)
+    check_heads_full(r, heads[2:])
+    check_rows_all_heads(r, seed=5)
+    check_column_sums(r, heads)
