@@ -177,7 +177,8 @@ def test_large_magnitude_scores_stay_finite():
     dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=True)
     torch.cuda.synchronize()
     O, L = _oracle_fwd(f64, s, True)
-    compare("O", o, O, TOL["bf16"]["o"])
+    # O is linear in V: inputs 6x larger scale the stated 2e-2 bound by 6
+    compare("O", o, O, 6 * TOL["bf16"]["o"], REL_RMS["bf16"])
     compare_lse("LSE", lse, L, 2e-2)  # |LSE| ~ 1e3: a few float32 ulps of 1e3
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
