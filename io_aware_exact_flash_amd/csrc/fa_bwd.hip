@@ -14,8 +14,8 @@
 //                  dS = P o (dP - D),  dV^T += dO^T P,  dK^T += Q^T dS;
 //                every row of P and dS is a register row, so P and dS feed
 //                the dV/dK products as B operands without leaving registers;
-//                Q and dO are staged in LDS twice, row-major (for S, dP) and
-//                transposed (for dV, dK);
+//                Q and dO are staged once, row-major, and read both by rows
+//                (for S, dP) and by LDS transpose reads (for dV, dK);
 //  3. dQ pass    one workgroup per 128 queries (4 waves x 32 queries), the
 //                forward's orientation: S^T = K Q^T, dP^T = V dO^T,
 //                dS^T = P^T o (dP^T - D), dQ^T += K^T dS^T.
@@ -56,14 +56,15 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(const uint16_t* __restrict
 // ------------------------------------------------------------ dK / dV pass
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BKV = 128;            // keys per workgroup
-  constexpr int BQ = 8192 / D;        // queries per tile
+  constexpr int BKV = 128;            // keys per workgroup (4 waves x 32)
+  constexpr int BQ = 64;              // queries per tile
   constexpr int NQB = BQ / 32;        // 32-query blocks per tile
   constexpr int KS = D / 16;
   constexpr int NB = D / 32;
   constexpr int PK = BQ / 16;
-  constexpr int TILE = BQ * D * 2;
-  constexpr int BUF = 4 * TILE + 2 * BQ * 4;  // Q rm, Q tt, dO rm, dO tt, L, D
+  using TL = Pad<D, true>;            // Q and dO: row reads and transpose reads
+  constexpr int TILE = TL::bytes(BQ);
+  constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // Q, dO, L*log2e, D
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
   const int tid = threadIdx.x;
@@ -96,7 +97,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   const int n_tiles = (n + BQ - 1) / BQ;
-  const int i_begin0 = CAUSAL ? k0 / BQ : 0;
   auto live = [&](int i) {
     if constexpr (SPARSE) return a.mask[(size_t)((i * BQ) / kMaskBlock) * a.mask_t + kb] != 0;
     return true;
@@ -107,38 +107,39 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return i;
   };
 
-  Stage<BQ, D, kNT> sq, sd;
-  auto stage_ld = [&](int i) {
-    sq.load(Qg, i * BQ, n, tid);
-    sd.load(dOg, i * BQ, n, tid);
-  };
+  Stage<BQ, D, kNT, true> sq, sd;
+  sq.init(tid);
+  sd.init(tid);
   float lv = 0.0f, dv = 0.0f;
-  auto stage_ld_vec = [&](int i) {
+  auto stage_ld = [&](int i) {
+    sq.load(Qg + (size_t)i * BQ * D, n - i * BQ);
+    sd.load(dOg + (size_t)i * BQ * D, n - i * BQ);
     if (tid < BQ) {
-      int row = i * BQ + tid;
-      float L = row < n ? Lg[row] : -INFINITY;
+      const int row = i * BQ + tid;
+      const float L = row < n ? Lg[row] : -INFINITY;
       lv = (L == -INFINITY) ? INFINITY : L * kLog2e;  // rows with no keys get P = 0
       dv = row < n ? Dg[row] : 0.0f;
     }
   };
   auto stage_st = [&](char* b) {
-    sq.store_rm(b, tid);
-    sq.store_tt(b + TILE, tid);
-    sd.store_rm(b + 2 * TILE, tid);
-    sd.store_tt(b + 3 * TILE, tid);
+    sq.store(b);
+    sd.store(b + TILE);
     if (tid < BQ) {
-      reinterpret_cast<float*>(b + 4 * TILE)[tid] = lv;
-      reinterpret_cast<float*>(b + 4 * TILE + BQ * 4)[tid] = dv;
+      reinterpret_cast<float*>(b + 2 * TILE)[tid] = lv;
+      reinterpret_cast<float*>(b + 2 * TILE + BQ * 4)[tid] = dv;
     }
   };
+  const int rread = TL::row_base(c32, g);
+  const int tread = TL::tr_base(lane);
 
-  int i = i_begin0;
+  int i = CAUSAL ? k0 / BQ : 0;
   if (!live(i)) i = next_tile(i);
   if (i < n_tiles) {
     stage_ld(i);
-    stage_ld_vec(i);
     stage_st(smem);
   }
+  settle(kreg);
+  settle(vreg);
   __syncthreads();
 
   f32x16 dkacc[NB], dvacc[NB];
@@ -152,34 +153,30 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   while (i < n_tiles) {
     const int in = next_tile(i);
-    if (in < n_tiles) {
-      stage_ld(in);
-      stage_ld_vec(in);
-    }
+    if (in < n_tiles) stage_ld(in);
     const char* B = smem + buf * BUF;
-    const char* Qrm = B;
-    const char* Qtt = B + TILE;
-    const char* Orm = B + 2 * TILE;
-    const char* Ott = B + 3 * TILE;
-    const float* Ls = reinterpret_cast<const float*>(B + 4 * TILE);
-    const float* Ds = Ls + BQ;
+    const char* qr = B + rread;
+    const char* orr = B + TILE + rread;
+    const char* qt = B + tread;
+    const char* ot = B + TILE + tread;
+    const float* Ls = reinterpret_cast<const float*>(B + 2 * TILE) + 4 * g;
+    const float* Ds = reinterpret_cast<const float*>(B + 2 * TILE + BQ * 4) + 4 * g;
     const int q0 = i * BQ;
     const bool wave_live = !CAUSAL || (q0 + BQ - 1 >= kw0);
     if (wave_live) {
       f32x16 s[NQB], dp[NQB];
+      const f32x16 zero = {};
 #pragma unroll
       for (int mq = 0; mq < NQB; ++mq) {
-        s[mq] = 0.0f;
-        dp[mq] = 0.0f;
+        s[mq] = mfma32<Tag>(ld_row(qr + TL::row_off(mq, 0)), kreg[0], zero);
+        dp[mq] = mfma32<Tag>(ld_row(orr + TL::row_off(mq, 0)), vreg[0], zero);
       }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 1; ks < KS; ++ks) {
 #pragma unroll
         for (int mq = 0; mq < NQB; ++mq) {
-          u32x4 aq = *reinterpret_cast<const u32x4*>(Qrm + Layout<D>::off(32 * mq + c32, 2 * ks + g));
-          s[mq] = mfma32<Tag>(aq, kreg[ks], s[mq]);
-          u32x4 ao = *reinterpret_cast<const u32x4*>(Orm + Layout<D>::off(32 * mq + c32, 2 * ks + g));
-          dp[mq] = mfma32<Tag>(ao, vreg[ks], dp[mq]);
+          s[mq] = mfma32<Tag>(ld_row(qr + TL::row_off(mq, ks)), kreg[ks], s[mq]);
+          dp[mq] = mfma32<Tag>(ld_row(orr + TL::row_off(mq, ks)), vreg[ks], dp[mq]);
         }
       }
       const bool need_mask = CAUSAL && (q0 < kw0 + 31);
@@ -187,14 +184,13 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int mq = 0; mq < NQB; ++mq) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int qrow = 32 * mq + 8 * r4 + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qrow);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qrow);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + 32 * mq + 8 * r4);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + 32 * mq + 8 * r4);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int v = 4 * r4 + t;
             float p = fast_exp2(fmaf(s[mq][v], cs, -l4[t]));
-            if (need_mask && (my_k > q0 + qrow + t)) p = 0.0f;
+            if (need_mask && (my_k > q0 + 32 * mq + 8 * r4 + 4 * g + t)) p = 0.0f;
             s[mq][v] = p;
             dp[mq][v] = p * (dp[mq][v] - d4[t]);
           }
@@ -202,14 +198,13 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < PK; ++kk) {
-        const u32x4 pb = pack8<Tag>(s[kk >> 1], 8 * (kk & 1));
-        const u32x4 db = pack8<Tag>(dp[kk >> 1], 8 * (kk & 1));
+        const int mq = kk >> 1, h = kk & 1;
+        const u32x4 pb = pack8<Tag>(s[mq], 8 * h);
+        const u32x4 db = pack8<Tag>(dp[mq], 8 * h);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          u32x4 ao = *reinterpret_cast<const u32x4*>(Ott + Layout<BQ>::off(32 * nb + c32, 2 * kk + g));
-          dvacc[nb] = mfma32<Tag>(ao, pb, dvacc[nb]);
-          u32x4 aq = *reinterpret_cast<const u32x4*>(Qtt + Layout<BQ>::off(32 * nb + c32, 2 * kk + g));
-          dkacc[nb] = mfma32<Tag>(aq, db, dkacc[nb]);
+          dvacc[nb] = mfma32<Tag>(ld_tr(ot + TL::tr_off(mq, h, 0, nb), ot + TL::tr_off(mq, h, 1, nb)), pb, dvacc[nb]);
+          dkacc[nb] = mfma32<Tag>(ld_tr(qt + TL::tr_off(mq, h, 0, nb), qt + TL::tr_off(mq, h, 1, nb)), db, dkacc[nb]);
         }
       }
     }
@@ -240,15 +235,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ dQ pass
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = 128;
-  constexpr int BC = 8192 / D;
+  constexpr int BC = 64;
   constexpr int NKB = BC / 32;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
   constexpr int PK = BC / 16;
-  constexpr int TILE = BC * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * TILE];  // [buf][K rm | K tt | V rm]
+  using KL = Pad<D, true>;            // K: row reads (S^T) and transpose reads (dQ^T)
+  using VL = Pad<D, false>;           // V: row reads (dP^T)
+  constexpr int KT = KL::bytes(BC), VT = VL::bytes(BC), BUF = KT + VT;
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -292,15 +289,23 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     return j;
   };
 
-  Stage<BC, D, kNT> sk, sv;
+  Stage<BC, D, kNT, true> sk;
+  Stage<BC, D, kNT, false> sv;
+  sk.init(tid);
+  sv.init(tid);
+  const int krow = KL::row_base(c32, g);
+  const int ktr = KL::tr_base(lane);
+  const int vrow = KT + VL::row_base(c32, g);
+
   int j = SPARSE ? next_tile(-1) : 0;
   if (j < j_end) {
-    sk.load(Kg, j * BC, n, tid);
-    sv.load(Vg, j * BC, n, tid);
-    sk.store_rm(smem, tid);
-    sk.store_tt(smem + TILE, tid);
-    sv.store_rm(smem + 2 * TILE, tid);
+    sk.load(Kg + (size_t)j * BC * D, n - j * BC);
+    sv.load(Vg + (size_t)j * BC * D, n - j * BC);
+    sk.store(smem);
+    sv.store(smem + KT);
   }
+  settle(qreg);
+  settle(oreg);
   __syncthreads();
 
   f32x16 acc[MB];
@@ -312,29 +317,28 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   while (j < j_end) {
     const int jn = next_tile(j);
     if (jn < j_end) {
-      sk.load(Kg, jn * BC, n, tid);
-      sv.load(Vg, jn * BC, n, tid);
+      sk.load(Kg + (size_t)jn * BC * D, n - jn * BC);
+      sv.load(Vg + (size_t)jn * BC * D, n - jn * BC);
     }
-    const char* Krm = smem + buf * 3 * TILE;
-    const char* Ktt = Krm + TILE;
-    const char* Vrm = Krm + 2 * TILE;
+    const char* kr = smem + buf * BUF + krow;
+    const char* kt = smem + buf * BUF + ktr;
+    const char* vr = smem + buf * BUF + vrow;
     const int k0 = j * BC;
     const bool wave_live = !CAUSAL || (k0 <= qw0 + 31);
     if (wave_live) {
       f32x16 s[NKB], dp[NKB];
+      const f32x16 zero = {};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = 0.0f;
-        dp[kb] = 0.0f;
+        s[kb] = mfma32<Tag>(ld_row(kr + KL::row_off(kb, 0)), qreg[0], zero);
+        dp[kb] = mfma32<Tag>(ld_row(vr + VL::row_off(kb, 0)), oreg[0], zero);
       }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 1; ks < KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          u32x4 ak = *reinterpret_cast<const u32x4*>(Krm + Layout<D>::off(32 * kb + c32, 2 * ks + g));
-          s[kb] = mfma32<Tag>(ak, qreg[ks], s[kb]);
-          u32x4 av = *reinterpret_cast<const u32x4*>(Vrm + Layout<D>::off(32 * kb + c32, 2 * ks + g));
-          dp[kb] = mfma32<Tag>(av, oreg[ks], dp[kb]);
+          s[kb] = mfma32<Tag>(ld_row(kr + KL::row_off(kb, ks)), qreg[ks], s[kb]);
+          dp[kb] = mfma32<Tag>(ld_row(vr + VL::row_off(kb, ks)), oreg[ks], dp[kb]);
         }
       }
       const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > n);
@@ -353,19 +357,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
         }
 #pragma unroll
       for (int kk = 0; kk < PK; ++kk) {
-        const u32x4 db = pack8<Tag>(dp[kk >> 1], 8 * (kk & 1));
+        const int kb = kk >> 1, h = kk & 1;
+        const u32x4 db = pack8<Tag>(dp[kb], 8 * h);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          u32x4 ak = *reinterpret_cast<const u32x4*>(Ktt + Layout<BC>::off(32 * mb + c32, 2 * kk + g));
-          acc[mb] = mfma32<Tag>(ak, db, acc[mb]);
-        }
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = mfma32<Tag>(ld_tr(kt + KL::tr_off(kb, h, 0, mb), kt + KL::tr_off(kb, h, 1, mb)), db, acc[mb]);
       }
     }
     if (jn < j_end) {
-      char* nb = smem + (buf ^ 1) * 3 * TILE;
-      sk.store_rm(nb, tid);
-      sk.store_tt(nb + TILE, tid);
-      sv.store_rm(nb + 2 * TILE, tid);
+      char* nb = smem + (buf ^ 1) * BUF;
+      sk.store(nb);
+      sv.store(nb + KT);
     }
     __syncthreads();
     buf ^= 1;
@@ -421,7 +423,7 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const BwdArgs& a, hipStrea
 }  // namespace
 
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st) {
-  a.nqb = (a.n + 127) / 128;
+  a.nqb = (a.n + 127) / 128;       // 128 queries per dQ workgroup
   a.nblk_q = a.nqb * bh;
   a.nkb = (a.n + 127) / 128;
   a.nblk_kv = a.nkb * bh;

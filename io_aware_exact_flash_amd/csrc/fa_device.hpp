@@ -98,101 +98,112 @@ __device__ __forceinline__ float half_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// LDS tile layouts.  A tile is R rows x C columns of 16-bit elements stored
-// row by row; 16-byte chunks inside a row are XOR-swizzled so that the
-// 16 lanes served together by the LDS hit distinct banks both when a wave
-// reads one chunk column down 32 consecutive rows (MFMA operand fetch) and
-// when it writes a tile.
-//   row-major ("RM"):   rows = tokens, columns = head dimension
-//   transposed ("TT"):  rows = head dimension, columns = tokens, with token
-//                       bits 2 and 3 swapped so the eight tokens of one
-//                       lane's k-slots are contiguous (see tt_pos).
+// LDS tiles.  A tile holds ROWS tokens x D columns of 16-bit elements, row
+// major, with padded rows so that every operand fetch is a per-lane base
+// address plus a compile-time offset (no per-read address arithmetic).
+//   Pad<D, false>: stride 2D+16 bytes; serves 16-byte row reads.
+//   Pad<D, true>:  stride 2D+64 bytes and a 16-byte rotation every 4 rows;
+//                  serves 16-byte row reads AND ds_read_b64_tr_b16 column
+//                  reads.
+// Both were chosen by enumerating strides/rotations against the 64-bank LDS
+// so that the MFMA operand fetches (16-lane groups for 16-byte reads, 32-lane
+// groups for 8-byte transpose reads) and the tile stores hit distinct banks.
 // ---------------------------------------------------------------------------
-template <int COLS>
-struct Layout {
-  static constexpr int kRowBytes = COLS * 2;
-  static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kRowsPer256 = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
-  static constexpr int kBytes(int rows) { return rows * kRowBytes; }
-  // byte offset of 16-byte chunk `c` of row `r`
-  __device__ __forceinline__ static int off(int r, int c) {
-    int f = ((r / kRowsPer256) ^ (r / (kRowsPer256 * kChunks))) % kChunks;
-    return r * kRowBytes + ((c ^ f) << 4);
+template <int D, bool TR>
+struct Pad {
+  static constexpr int S = 2 * D + (TR ? 64 : 16);  // row stride, bytes
+  __host__ __device__ static constexpr int rot(int r) { return TR ? 16 * ((r >> 2) & 3) : 0; }
+  __host__ __device__ static constexpr int bytes(int rows) { return rows * S; }
+
+  // Row read: lane (c32, g) fetches 16 bytes = k-slots of group g, i.e. the
+  // columns 16*ks + 8*g .. +7 of row 32*blk + c32:  base + row_off(blk, ks).
+  __device__ static int row_base(int c32, int g) { return c32 * S + rot(c32) + 16 * g; }
+  __host__ __device__ static constexpr int row_off(int blk, int ks) { return 32 * blk * S + 32 * ks; }
+
+  // Transpose read (ds_read_b64_tr_b16, two per operand).  Within a 16-lane
+  // group, output lane i slot j is element (i % 4) of the 8 bytes addressed by
+  // source lane 4j + i/4.  To give lane (c32, g) the column 32*mb + c32 of
+  // the tokens 32*kb + 16*h + 8*(t/4) + 4*g + t%4 (slots t = 0..7, the
+  // C-layout order of a 32-token block), source lane l = 16*G + 4*j + u
+  // addresses token 32*kb + 16*h + 8*second + 4*g + j, columns
+  // 32*mb + 16*(G%2) + 4*u .. +3.
+  __device__ static int tr_base(int lane) {
+    const int g = lane >> 5, j = (lane >> 2) & 3, u = lane & 3, half = (lane >> 4) & 1;
+    return (4 * g + j) * S + 16 * g + 32 * half + 8 * u;
+  }
+  __host__ __device__ static constexpr int tr_off(int kb, int h, int second, int mb) {
+    return (32 * kb + 16 * h + 8 * second) * S + 32 * second + 64 * mb;
   }
 };
 
-// Position of token t inside a TT row: bits 2 and 3 of t exchanged.
-__device__ __forceinline__ int tt_pos(int t) {
-  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+__device__ __forceinline__ u32x4 ld_row(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// One MFMA operand (8 slots) by two transpose reads.
+__device__ __forceinline__ u32x4 ld_tr(const char* p0, const char* p1) {
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  const s16x8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(u32x4, ab);
 }
 
-// Transpose a 4 x 8 block of 16-bit values held as four rows of u32x4 into
-// eight columns of four values (u32x2 each).
-__device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    // column 2c takes the low halves of dword c, column 2c+1 the high halves
-    out[2 * c][0] = (in[0][c] & 0xffffu) | (in[1][c] << 16);
-    out[2 * c][1] = (in[2][c] & 0xffffu) | (in[3][c] << 16);
-    out[2 * c + 1][0] = (in[0][c] >> 16) | (in[1][c] & 0xffff0000u);
-    out[2 * c + 1][1] = (in[2][c] >> 16) | (in[3][c] & 0xffff0000u);
-  }
-}
-
-// Global -> registers staging of a tile of ROWS tokens x D columns.  Thread
-// `tid` of NT owns units of 4 consecutive tokens x 8 columns; ROWS*D/32 units
-// per tile.  Token indices are clamped to [0, n-1] so every load is in
-// bounds; callers mask tokens >= n.
-template <int ROWS, int D, int NT>
+// Global -> registers -> LDS staging of a tile of ROWS tokens x D columns.
+// Unit = 4 consecutive tokens x 8 columns (16 bytes per token); thread tid
+// owns unit tid (threads beyond the unit count idle).  Tokens at or beyond
+// `valid` are clamped to the last valid row so every load stays in bounds;
+// callers mask them.
+template <int ROWS, int D, int NT, bool TR>
 struct Stage {
   static constexpr int kUnits = ROWS * D / 32;
-  static constexpr int kPer = (kUnits + NT - 1) / NT;
-  static_assert(kUnits % NT == 0, "tile units must divide evenly among threads");
-  u32x4 r[kPer][4];
+  static_assert(kUnits <= NT, "one unit per thread");
+  u32x4 r[4];
+  int goff;   // element offset of this thread's unit inside a tile
+  int soff;   // LDS byte offset of this thread's unit inside a tile
+  bool act;
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int row0, int n, int tid) {
+  __device__ void init(int tid) {
+    act = tid < kUnits;
+    const int dc = tid % (D / 8), tg = tid / (D / 8);
+    goff = 4 * tg * D + 8 * dc;
+    soff = 4 * tg * Pad<D, TR>::S + Pad<D, TR>::rot(4 * tg) + 16 * dc;
+  }
+  // tile: first row of the tile (uniform pointer); valid: rows of the tile
+  // that exist (ROWS or fewer on the last tile)
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ tile, int valid) {
+    if (!act) return;
+    if (valid >= ROWS) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      int unit = tid + u * NT;
-      int dc = unit % (D / 8);
-      int tg = unit / (D / 8);
+      for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const u32x4*>(tile + goff + j * D);
+    } else {
+      const int row0 = goff / D;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        int row = min(row0 + tg * 4 + j, n - 1);
-        r[u][j] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + dc * 8);
+        const int row = min(row0 + j, valid - 1);
+        r[j] = *reinterpret_cast<const u32x4*>(tile + (goff - row0 * D) + row * D);
       }
     }
   }
-  // row-major copy: [ROWS][D]
-  __device__ __forceinline__ void store_rm(char* lds, int tid) const {
+  __device__ __forceinline__ void store(char* lds_tile) const {
+    if (!act) return;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      int unit = tid + u * NT;
-      int dc = unit % (D / 8);
-      int tg = unit / (D / 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(lds + Layout<D>::off(tg * 4 + j, dc)) = r[u][j];
-    }
-  }
-  // transposed copy: [D][ROWS], token order permuted by tt_pos
-  __device__ __forceinline__ void store_tt(char* lds, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      int unit = tid + u * NT;
-      int dc = unit % (D / 8);
-      int tg = unit / (D / 8);
-      u32x2 t[8];
-      transpose4x8(r[u], t);
-      int pos = tt_pos(tg * 4);  // 4-aligned; the 4 tokens stay contiguous
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int drow = dc * 8 + j;
-        *reinterpret_cast<u32x2*>(lds + Layout<ROWS>::off(drow, pos >> 3) + ((pos & 4) << 1)) = t[j];
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(lds_tile + soff + j * Pad<D, TR>::S) = r[j];
   }
 };
+
+// Make the register operands loaded before a loop complete there: the
+// waitcnt pass otherwise keeps them "possibly pending" on some path into the
+// loop and waits on the counter inside it, which also waits for that
+// iteration's global prefetch.  An empty asm that reads the registers forces
+// the wait once, before the loop.
+template <int N>
+__device__ __forceinline__ void settle(const u32x4 (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
+}
 
 // Map a linear workgroup id so that each XCD (ids are dealt round-robin to
 // the 8 XCDs) receives a contiguous range of logical work items, keeping the

@@ -12,9 +12,11 @@
 //    running statistics (m, l), the exp(m_old - m_new) rescale of the
 //    accumulator, and the final division are lane-local.
 //  * The accumulator is O^T = V_j^T P^T: P^T comes straight out of the S^T
-//    accumulator as the B operand; V_j^T is read from a transposed LDS copy.
-//  * Key tiles of 8192/d keys (64 for d=128, 128 for d=64), double-buffered
-//    in LDS with a register prefetch: one barrier per tile.
+//    accumulator as the B operand; V_j^T is fetched from the row-major V
+//    tile with LDS transpose reads (ds_read_b64_tr_b16).
+//  * 64-key tiles, double-buffered in LDS with a register prefetch: one
+//    barrier per tile; padded rows make every operand fetch a per-lane base
+//    plus an immediate offset.
 //  * Causal: tiles above the diagonal are never loaded; only tiles crossing
 //    it are masked element-wise (FlashAttention-2 notes, "Causal mask
 //    optimisation").  Block-sparse: tiles whose 128 x 128 mask entry is zero
@@ -38,13 +40,15 @@ constexpr float kLazy = 8.0f;
 
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kNT, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int BC = 8192 / D;        // keys per tile
+  constexpr int BC = 64;              // keys per tile
   constexpr int NKB = BC / 32;        // 32-key blocks per tile
   constexpr int KS = D / 16;          // k-steps over the head dimension
   constexpr int MB = D / 32;          // 32-wide output column blocks
   constexpr int PK = BC / 16;         // k-steps of the PV product
-  constexpr int TILE = BC * D * 2;    // bytes of one K or V tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  using KL = Pad<D, false>;           // K: row reads
+  using VL = Pad<D, true>;            // V: transpose reads
+  constexpr int KT = KL::bytes(BC), VT = VL::bytes(BC), BUF = KT + VT;
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -81,14 +85,21 @@ __global__ __launch_bounds__(kNT, 2) void fwd_kernel(FwdArgs a) {
     return j;
   };
 
-  Stage<BC, D, kNT> sk, sv;
+  Stage<BC, D, kNT, false> sk;
+  Stage<BC, D, kNT, true> sv;
+  sk.init(tid);
+  sv.init(tid);
+  const int kread = KL::row_base(c32, g);
+  const int vread = KT + VL::tr_base(lane);
+
   int j = SPARSE ? next_tile(-1) : 0;
   if (j < j_end) {
-    sk.load(K, j * BC, n, tid);
-    sv.load(V, j * BC, n, tid);
-    sk.store_rm(smem, tid);
-    sv.store_tt(smem + TILE, tid);
+    sk.load(K + (size_t)j * BC * D, n - j * BC);
+    sv.load(V + (size_t)j * BC * D, n - j * BC);
+    sk.store(smem);
+    sv.store(smem + KT);
   }
+  settle(qreg);
   __syncthreads();
 
   f32x16 oacc[MB];
@@ -101,24 +112,23 @@ __global__ __launch_bounds__(kNT, 2) void fwd_kernel(FwdArgs a) {
   while (j < j_end) {
     const int jn = next_tile(j);
     if (jn < j_end) {
-      sk.load(K, jn * BC, n, tid);
-      sv.load(V, jn * BC, n, tid);
+      sk.load(K + (size_t)jn * BC * D, n - jn * BC);
+      sv.load(V + (size_t)jn * BC * D, n - jn * BC);
     }
-    const char* Kb = smem + buf * 2 * TILE;
-    const char* Vb = Kb + TILE;
+    const char* kb_ = smem + buf * BUF + kread;
+    const char* vb_ = smem + buf * BUF + vread;
     const int k0 = j * BC;
     const bool wave_live = !CAUSAL || (k0 <= qw0 + kQW - 1);
     if (wave_live) {
       f32x16 s[NKB];
+      const f32x16 zero = {};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = 0.0f;
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32<Tag>(ld_row(kb_ + KL::row_off(kb, 0)), qreg[0], zero);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 1; ks < KS; ++ks) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          u32x4 av = *reinterpret_cast<const u32x4*>(Kb + Layout<D>::off(32 * kb + c32, 2 * ks + g));
-          s[kb] = mfma32<Tag>(av, qreg[ks], s[kb]);
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+          s[kb] = mfma32<Tag>(ld_row(kb_ + KL::row_off(kb, ks)), qreg[ks], s[kb]);
       }
       const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > n);
       if (need_mask) {
@@ -159,19 +169,20 @@ __global__ __launch_bounds__(kNT, 2) void fwd_kernel(FwdArgs a) {
         }
       l_part += rs;
 #pragma unroll
-      for (int ks = 0; ks < PK; ++ks) {
-        const u32x4 pb = pack8<Tag>(s[ks >> 1], 8 * (ks & 1));
+      for (int kk = 0; kk < PK; ++kk) {
+        const int kb = kk >> 1, h = kk & 1;
+        const u32x4 pb = pack8<Tag>(s[kb], 8 * h);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          u32x4 av = *reinterpret_cast<const u32x4*>(Vb + Layout<BC>::off(32 * mb + c32, 2 * ks + g));
+          const u32x4 av = ld_tr(vb_ + VL::tr_off(kb, h, 0, mb), vb_ + VL::tr_off(kb, h, 1, mb));
           oacc[mb] = mfma32<Tag>(av, pb, oacc[mb]);
         }
       }
     }
     if (jn < j_end) {
-      char* nb = smem + (buf ^ 1) * 2 * TILE;
-      sk.store_rm(nb, tid);
-      sv.store_tt(nb + TILE, tid);
+      char* nb = smem + (buf ^ 1) * BUF;
+      sk.store(nb);
+      sv.store(nb + KT);
     }
     __syncthreads();
     buf ^= 1;
