@@ -55,9 +55,9 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(const uint16_t* __restrict
 
 // ------------------------------------------------------------ dK / dV pass
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 128;            // keys per workgroup (4 waves x 32)
-  constexpr int BQ = 64;              // queries per tile
+  constexpr int BQ = 32;              // queries per tile
   constexpr int NQB = BQ / 32;        // 32-query blocks per tile
   constexpr int KS = D / 16;
   constexpr int NB = D / 32;
@@ -107,13 +107,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return i;
   };
 
-  Stage<BQ, D, kNT, true> sq, sd;
-  sq.init(tid);
-  sd.init(tid);
+  Dma<BQ, D, true, kNT / 64> dma;  // Q and dO tiles share one geometry
+  dma.init(w, lane);
   float lv = 0.0f, dv = 0.0f;
-  auto stage_ld = [&](int i) {
-    sq.load(Qg + (size_t)i * BQ * D, n - i * BQ);
-    sd.load(dOg + (size_t)i * BQ * D, n - i * BQ);
+  // issue the DMA of tile i into buffer b; L*log2(e) and D go through registers
+  auto stage_ld = [&](int i, char* b) {
+    dma.issue2(Qg + (size_t)i * BQ * D, dOg + (size_t)i * BQ * D, n - i * BQ, b, b + TILE);
     if (tid < BQ) {
       const int row = i * BQ + tid;
       const float L = row < n ? Lg[row] : -INFINITY;
@@ -122,8 +121,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   auto stage_st = [&](char* b) {
-    sq.store(b);
-    sd.store(b + TILE);
     if (tid < BQ) {
       reinterpret_cast<float*>(b + 2 * TILE)[tid] = lv;
       reinterpret_cast<float*>(b + 2 * TILE + BQ * 4)[tid] = dv;
@@ -135,11 +132,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   int i = CAUSAL ? k0 / BQ : 0;
   if (!live(i)) i = next_tile(i);
   if (i < n_tiles) {
-    stage_ld(i);
+    stage_ld(i, smem);
     stage_st(smem);
   }
   settle(kreg);
   settle(vreg);
+  dma_wait();
   __syncthreads();
 
   f32x16 dkacc[NB], dvacc[NB];
@@ -153,7 +151,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   while (i < n_tiles) {
     const int in = next_tile(i);
-    if (in < n_tiles) stage_ld(in);
+    if (in < n_tiles) stage_ld(in, smem + (buf ^ 1) * BUF);
     const char* B = smem + buf * BUF;
     const char* qr = B + rread;
     const char* orr = B + TILE + rread;
@@ -209,6 +207,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     if (in < n_tiles) stage_st(smem + (buf ^ 1) * BUF);
+    dma_wait();
     __syncthreads();
     buf ^= 1;
     i = in;
@@ -235,9 +234,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ dQ pass
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kNT, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = 128;
-  constexpr int BC = 64;
+  constexpr int BC = 32;
   constexpr int NKB = BC / 32;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;

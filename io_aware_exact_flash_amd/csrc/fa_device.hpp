@@ -151,24 +151,28 @@ __device__ __forceinline__ u32x4 ld_tr(const char* p0, const char* p1) {
 }
 
 // Global -> registers -> LDS staging of a tile of ROWS tokens x D columns.
-// Unit = 4 consecutive tokens x 8 columns (16 bytes per token); thread tid
-// owns unit tid (threads beyond the unit count idle).  Tokens at or beyond
-// `valid` are clamped to the last valid row so every load stays in bounds;
-// callers mask them.
+// A unit is RPU consecutive tokens (RPU <= 4, inside one 4-row rotation
+// group) x 8 columns; thread tid owns unit tid (threads beyond the unit count
+// idle).  Tokens at or beyond `valid` are clamped to the last valid row so
+// every load stays in bounds; callers mask them.
 template <int ROWS, int D, int NT, bool TR>
 struct Stage {
-  static constexpr int kUnits = ROWS * D / 32;
-  static_assert(kUnits <= NT, "one unit per thread");
-  u32x4 r[4];
+  static constexpr int kChunks = ROWS * D / 8;
+  static constexpr int RPU = kChunks >= NT ? kChunks / NT : 1;
+  static constexpr int kUnits = kChunks / RPU;
+  static_assert(RPU <= 4 && kChunks % RPU == 0 && kUnits <= NT, "staging split");
+  u32x4 r[RPU];
   int goff;   // element offset of this thread's unit inside a tile
   int soff;   // LDS byte offset of this thread's unit inside a tile
+  int row0;   // first row of the unit
   bool act;
 
   __device__ void init(int tid) {
     act = tid < kUnits;
     const int dc = tid % (D / 8), tg = tid / (D / 8);
-    goff = 4 * tg * D + 8 * dc;
-    soff = 4 * tg * Pad<D, TR>::S + Pad<D, TR>::rot(4 * tg) + 16 * dc;
+    row0 = RPU * tg;
+    goff = row0 * D + 8 * dc;
+    soff = row0 * Pad<D, TR>::S + Pad<D, TR>::rot(row0) + 16 * dc;
   }
   // tile: first row of the tile (uniform pointer); valid: rows of the tile
   // that exist (ROWS or fewer on the last tile)
@@ -176,11 +180,10 @@ struct Stage {
     if (!act) return;
     if (valid >= ROWS) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const u32x4*>(tile + goff + j * D);
+      for (int j = 0; j < RPU; ++j) r[j] = *reinterpret_cast<const u32x4*>(tile + goff + j * D);
     } else {
-      const int row0 = goff / D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < RPU; ++j) {
         const int row = min(row0 + j, valid - 1);
         r[j] = *reinterpret_cast<const u32x4*>(tile + (goff - row0 * D) + row * D);
       }
@@ -189,10 +192,59 @@ struct Stage {
   __device__ __forceinline__ void store(char* lds_tile) const {
     if (!act) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < RPU; ++j)
       *reinterpret_cast<u32x4*>(lds_tile + soff + j * Pad<D, TR>::S) = r[j];
   }
 };
+
+// Global -> LDS staging without registers (global_load_lds_dwordx4: lane i
+// of a wave writes its 16 bytes at M0 + 16*i).  The padded LDS image of a
+// tile is cut into 1 KB blocks; block b is moved by wave b % NW, whose lane i
+// fetches the 16 bytes that belong at block offset 16*i (lanes that fall on
+// row padding or past the tile stay idle).  Rows at or beyond `valid` are
+// clamped to the last valid row so every load stays in bounds.  Completion
+// is awaited with dma_wait() (vmcnt) before the workgroup barrier.
+template <int ROWS, int D, bool TR, int NW>
+struct Dma {
+  using L = Pad<D, TR>;
+  static constexpr int kBytes = ROWS * L::S;
+  static constexpr int kBlocks = (kBytes + 1023) / 1024;
+  static constexpr int kPer = (kBlocks + NW - 1) / NW;
+  int src[kPer];  // element offset inside the tile, or -1
+  int wave;
+
+  __device__ void init(int w, int lane) {
+    wave = w;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int off = (w + NW * k) * 1024 + 16 * lane;
+      src[k] = -1;
+      if (off < kBytes) {
+        const int r = off / L::S;
+        const int p = off - r * L::S - L::rot(r);
+        if (p >= 0 && p < 2 * D) src[k] = r * D + p / 2;
+      }
+    }
+  }
+  // Moves two tiles of the same geometry with one set of offsets.
+  __device__ __forceinline__ void issue2(const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
+                                         int valid, char* l0, char* l1) const {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = wave + NW * k;
+      if (b < kBlocks && src[k] >= 0) {
+        int e = src[k];
+        if (valid < ROWS && e / D >= valid) e = (valid - 1) * D + (e % D);
+        __builtin_amdgcn_global_load_lds(t0 + e, (__attribute__((address_space(3))) void*)(l0 + b * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(t1 + e, (__attribute__((address_space(3))) void*)(l1 + b * 1024), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// Wait for this wave's outstanding global loads (including LDS DMA); a
+// workgroup barrier must follow before other waves read the data.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Make the register operands loaded before a loop complete there: the
 // waitcnt pass otherwise keeps them "possibly pending" on some path into the
