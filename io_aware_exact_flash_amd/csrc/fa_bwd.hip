@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NB = D / 32;
   constexpr int PK = BQ / 16;
   using TL = Pad<D, true>;            // Q and dO: row reads and transpose reads
-  constexpr int TILE = TL::bytes(BQ);
+  using QD = Dma<BQ, D, true, kNT / 64>;
+  constexpr int TILE = QD::kSlot;     // LDS bytes per tile (DMA writes whole slots)
   constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // Q, dO, L*log2e, D
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     return i;
   };
 
-  Dma<BQ, D, true, kNT / 64> dma;  // Q and dO tiles share one geometry
+  QD dma;  // Q and dO tiles share one geometry
   dma.init(w, lane);
   float lv = 0.0f, dv = 0.0f;
   // issue the DMA of tile i into buffer b; L*log2(e) and D go through registers
@@ -233,18 +234,32 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ dQ pass
+// K/V tiles stream through a ring of kRing LDS slots filled by DMA kRing-1
+// tiles ahead; each iteration waits (vmcnt) for its own tile, joins one
+// barrier, refills the slot all waves have just finished reading, computes.
+template <int C>
+__device__ __forceinline__ void wait_ahead(int ahead) {  // ahead: tiles issued after the one needed
+  if (ahead <= 0) vm_wait<0>();
+  else if (ahead == 1) vm_wait<C>();
+  else vm_wait<2 * C>();
+}
+
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kNT, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = 128;
   constexpr int BC = 32;
-  constexpr int NKB = BC / 32;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
   constexpr int PK = BC / 16;
+  constexpr int kRing = 3;
   using KL = Pad<D, true>;            // K: row reads (S^T) and transpose reads (dQ^T)
   using VL = Pad<D, false>;           // V: row reads (dP^T)
-  constexpr int KT = KL::bytes(BC), VT = VL::bytes(BC), BUF = KT + VT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  using KD = Dma<BC, D, true, kNT / 64>;
+  using VD = Dma<BC, D, false, kNT / 64>;
+  constexpr int SLOT = KD::kSlot + VD::kSlot;
+  constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
+  static_assert(2 * C < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -288,89 +303,84 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq_kernel(BwdArgs a) {
     return j;
   };
 
-  Stage<BC, D, kNT, true> sk;
-  Stage<BC, D, kNT, false> sv;
-  sk.init(tid);
-  sv.init(tid);
+  KD kd;
+  VD vd;
+  kd.init(w, lane);
+  vd.init(w, lane);
+  auto issue = [&](int jt, int slot) {
+    char* b = smem + slot * SLOT;
+    kd.issue(Kg + (size_t)jt * BC * D, n - jt * BC, b);
+    vd.issue(Vg + (size_t)jt * BC * D, n - jt * BC, b + KD::kSlot);
+  };
   const int krow = KL::row_base(c32, g);
   const int ktr = KL::tr_base(lane);
-  const int vrow = KT + VL::row_base(c32, g);
+  const int vrow = KD::kSlot + VL::row_base(c32, g);
 
-  int j = SPARSE ? next_tile(-1) : 0;
-  if (j < j_end) {
-    sk.load(Kg + (size_t)j * BC * D, n - j * BC);
-    sv.load(Vg + (size_t)j * BC * D, n - j * BC);
-    sk.store(smem);
-    sv.store(smem + KT);
-  }
+  // settle the register loads before the DMA so waits below count only DMA
   settle(qreg);
   settle(oreg);
-  __syncthreads();
+  int j = SPARSE ? next_tile(-1) : 0;
+  int jq = j;       // next tile to issue
+  int ahead = 0;    // tiles issued and not yet consumed
+  for (int s = 0; s < kRing - 1 && jq < j_end; ++s) {
+    issue(jq, s);
+    jq = next_tile(jq);
+    ++ahead;
+  }
 
   f32x16 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = 0.0f;
   const float cs = a.c;
-  int buf = 0;
+  int it = 0;
 
   while (j < j_end) {
-    const int jn = next_tile(j);
-    if (jn < j_end) {
-      sk.load(Kg + (size_t)jn * BC * D, n - jn * BC);
-      sv.load(Vg + (size_t)jn * BC * D, n - jn * BC);
+    wait_ahead<C>(ahead - 1);
+    __syncthreads();
+    if (jq < j_end) {  // refill the slot every wave finished reading last iteration
+      issue(jq, (it + kRing - 1) % kRing);
+      jq = next_tile(jq);
+      ++ahead;
     }
-    const char* kr = smem + buf * BUF + krow;
-    const char* kt = smem + buf * BUF + ktr;
-    const char* vr = smem + buf * BUF + vrow;
+    const char* base = smem + (it % kRing) * SLOT;
+    const char* kr = base + krow;
+    const char* kt = base + ktr;
+    const char* vr = base + vrow;
     const int k0 = j * BC;
     const bool wave_live = !CAUSAL || (k0 <= qw0 + 31);
     if (wave_live) {
-      f32x16 s[NKB], dp[NKB];
+      f32x16 s, dp;
       const f32x16 zero = {};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = mfma32<Tag>(ld_row(kr + KL::row_off(kb, 0)), qreg[0], zero);
-        dp[kb] = mfma32<Tag>(ld_row(vr + VL::row_off(kb, 0)), oreg[0], zero);
-      }
+      s = mfma32<Tag>(ld_row(kr + KL::row_off(0, 0)), qreg[0], zero);
+      dp = mfma32<Tag>(ld_row(vr + VL::row_off(0, 0)), oreg[0], zero);
 #pragma unroll
       for (int ks = 1; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          s[kb] = mfma32<Tag>(ld_row(kr + KL::row_off(kb, ks)), qreg[ks], s[kb]);
-          dp[kb] = mfma32<Tag>(ld_row(vr + VL::row_off(kb, ks)), oreg[ks], dp[kb]);
-        }
+        s = mfma32<Tag>(ld_row(kr + KL::row_off(0, ks)), qreg[ks], s);
+        dp = mfma32<Tag>(ld_row(vr + VL::row_off(0, ks)), oreg[ks], dp);
       }
       const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > n);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float p = fast_exp2(fmaf(s[kb][v], cs, -Lq));
-          if (need_mask) {
-            int key = k0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
-            bool dead = key >= n;
-            if constexpr (CAUSAL) dead = dead || key > my_q;
-            if (dead) p = 0.0f;
-          }
-          dp[kb][v] = p * (dp[kb][v] - Dq);
+      for (int v = 0; v < 16; ++v) {
+        float p = fast_exp2(fmaf(s[v], cs, -Lq));
+        if (need_mask) {
+          const int key = k0 + 8 * (v >> 2) + 4 * g + (v & 3);
+          bool dead = key >= n;
+          if constexpr (CAUSAL) dead = dead || key > my_q;
+          if (dead) p = 0.0f;
         }
+        dp[v] = p * (dp[v] - Dq);
+      }
 #pragma unroll
       for (int kk = 0; kk < PK; ++kk) {
-        const int kb = kk >> 1, h = kk & 1;
-        const u32x4 db = pack8<Tag>(dp[kb], 8 * h);
+        const u32x4 db = pack8<Tag>(dp, 8 * kk);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = mfma32<Tag>(ld_tr(kt + KL::tr_off(kb, h, 0, mb), kt + KL::tr_off(kb, h, 1, mb)), db, acc[mb]);
+          acc[mb] = mfma32<Tag>(ld_tr(kt + KL::tr_off(0, kk, 0, mb), kt + KL::tr_off(0, kk, 1, mb)), db, acc[mb]);
       }
     }
-    if (jn < j_end) {
-      char* nb = smem + (buf ^ 1) * BUF;
-      sk.store(nb);
-      sv.store(nb + KT);
-    }
-    __syncthreads();
-    buf ^= 1;
-    j = jn;
+    --ahead;
+    ++it;
+    j = next_tile(j);
   }
 
   if (my_q < n) {

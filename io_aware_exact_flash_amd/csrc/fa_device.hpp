@@ -209,8 +209,9 @@ struct Dma {
   using L = Pad<D, TR>;
   static constexpr int kBytes = ROWS * L::S;
   static constexpr int kBlocks = (kBytes + 1023) / 1024;
-  static constexpr int kPer = (kBlocks + NW - 1) / NW;
-  int src[kPer];  // element offset inside the tile, or -1
+  static constexpr int kPer = (kBlocks + NW - 1) / NW;   // DMA instructions per wave per tile
+  static constexpr int kSlot = kPer * NW * 1024;         // LDS bytes reserved per tile
+  int src[kPer];  // element offset inside the tile, or -1 (padding / past the tile)
   int wave;
 
   __device__ void init(int w, int lane) {
@@ -226,25 +227,37 @@ struct Dma {
       }
     }
   }
-  // Moves two tiles of the same geometry with one set of offsets.
-  __device__ __forceinline__ void issue2(const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
-                                         int valid, char* l0, char* l1) const {
+  // Every wave issues exactly kPer instructions per tile, with every lane
+  // active: lanes whose destination is row padding or lies past the tile
+  // (bytes no operand fetch reads) load the tile's first 16 bytes there.
+  // Outstanding-load counts are therefore exact and uniform across waves.
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ t0, int valid, char* l0) const {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = wave + NW * k;
-      if (b < kBlocks && src[k] >= 0) {
-        int e = src[k];
-        if (valid < ROWS && e / D >= valid) e = (valid - 1) * D + (e % D);
-        __builtin_amdgcn_global_load_lds(t0 + e, (__attribute__((address_space(3))) void*)(l0 + b * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(t1 + e, (__attribute__((address_space(3))) void*)(l1 + b * 1024), 16, 0, 0);
-      }
+      int e = src[k] < 0 ? 0 : src[k];
+      if (valid < ROWS && e / D >= valid) e = (valid - 1) * D + (e % D);
+      __builtin_amdgcn_global_load_lds(t0 + e, (__attribute__((address_space(3))) void*)(l0 + b * 1024), 16, 0, 0);
     }
+  }
+  // Moves two tiles of the same geometry with one set of offsets.
+  __device__ __forceinline__ void issue2(const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
+                                         int valid, char* l0, char* l1) const {
+    issue(t0, valid, l0);
+    issue(t1, valid, l1);
   }
 };
 
-// Wait for this wave's outstanding global loads (including LDS DMA); a
-// workgroup barrier must follow before other waves read the data.
-__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Wait until at most N of this wave's global loads (LDS DMA included) are
+// outstanding; a workgroup barrier must follow before other waves read the
+// data.  gfx9 s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt left at their "no wait" maxima.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void dma_wait() { vm_wait<0>(); }
 
 // Make the register operands loaded before a loop complete there: the
 // waitcnt pass otherwise keeps them "possibly pending" on some path into the
