@@ -16,12 +16,14 @@
 //                the dV/dK products as B operands without leaving registers;
 //                Q and dO are staged once, row-major, and read both by rows
 //                (for S, dP) and by LDS transpose reads (for dV, dK);
-//  3. dQ pass    one workgroup per 128 queries (4 waves x 32 queries), the
+//  3. dQ pass    one workgroup per 256 queries (4 waves x 64 queries), the
 //                forward's orientation: S^T = K Q^T, dP^T = V dO^T,
 //                dS^T = P^T o (dP^T - D), dQ^T += K^T dS^T.
 // dQ is computed in a separate pass instead of by cross-workgroup atomic
 // adds (the pages' choice): no float32 dQ buffer, no atomics, and the result
 // is deterministic; the cost is recomputing S and dP once more.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -29,6 +31,7 @@ namespace fa {
 namespace {
 
 constexpr int kNT = 256;
+constexpr int kDqRows = 256;  // queries per dQ workgroup
 
 // ------------------------------------------------------------ D pre-pass
 template <typename Tag, int D>
@@ -244,25 +247,41 @@ __device__ __forceinline__ void wait_ahead(int ahead) {  // ahead: tiles issued 
   else vm_wait<2 * C>();
 }
 
+// Each wave owns 64 queries, two 32-query blocks h = 0, 1, and runs one wave
+// per SIMD (the operands take ~400 registers).  Within a wave the matrix
+// cores and the vector ALU overlap only when their instructions are
+// interleaved, and every step of a block depends on the previous one
+// (S, dP -> dS -> dQ), so the wave software-pipelines its two blocks with
+// block 0 one step ahead.  Iteration t (tile j_t, next tile j_{t+1}):
+//   segment 1: products S^T, dP^T of (j_t, block 1)      | dS of (j_t, block 0)
+//   segment 2: products dQ^T of (j_t, block 0),
+//              S^T, dP^T of (j_{t+1}, block 0)           | dS of (j_t, block 1), DMA
+//   segment 3: products dQ^T of (j_t, block 1)
+// K/V tiles stream through a ring of four LDS slots; DMA runs two tiles
+// ahead, one barrier per iteration makes the next tile visible and frees
+// the slot refilled in the same iteration.
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BR = 128;
-  constexpr int BC = 32;
-  constexpr int KS = D / 16;
-  constexpr int MB = D / 32;
-  constexpr int PK = BC / 16;
-  constexpr int kRing = 3;
+__global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BR = kDqRows;         // queries per workgroup (4 waves x 64)
+  constexpr int BC = 32;              // keys per tile
+  constexpr int KS = D / 16;          // k-steps of the S/dP products
+  constexpr int MB = D / 32;          // 32-row blocks of dQ^T
+  constexpr int PK = BC / 16;         // k-steps of the dQ products
+  constexpr int NF = PK * MB;         // K^T fragments per tile
+  constexpr int kRing = 4;
   using KL = Pad<D, true>;            // K: row reads (S^T) and transpose reads (dQ^T)
   using VL = Pad<D, false>;           // V: row reads (dP^T)
   using KD = Dma<BC, D, true, kNT / 64>;
   using VD = Dma<BC, D, false, kNT / 64>;
   constexpr int SLOT = KD::kSlot + VD::kSlot;
   constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
-  static_assert(2 * C < 64, "vmcnt range");
+  static_assert(3 * C < 64, "vmcnt range");
+  static_assert(C <= NF, "DMA issue slots");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
   const int n = a.n;
   const int lb = xcd_remap(blockIdx.x, a.nblk_q);
@@ -275,126 +294,297 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
 
   const int q0 = qb * BR;
-  const int qw0 = q0 + w * 32;
-  const int my_q = qw0 + c32;
-  const int qr = min(my_q, n - 1);
+  const int qw0 = q0 + w * 64;        // the wave's first query; block h starts at qw0 + 32h
 
-  u32x4 qreg[KS], oreg[KS];
-  {
+  u32x4 qreg[2][KS], oreg[2][KS];     // Q^T and dO^T fragments, in AGPRs
+  float Lq[2], Dq[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int my_q = qw0 + 32 * h + c32;
+    const int qr = min(my_q, n - 1);
     const size_t r = (size_t)qr * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qreg[ks] = *reinterpret_cast<const u32x4*>(Qg + r + 16 * ks);
-      oreg[ks] = *reinterpret_cast<const u32x4*>(dOg + r + 16 * ks);
+      gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
+      gload_agpr(oreg[h][ks], dOg + r + 16 * ks);
     }
+    const float l = a.lse[(size_t)bh * n + qr];
+    Lq[h] = (l == -INFINITY || my_q >= n) ? INFINITY : l * kLog2e;
+    Dq[h] = a.dvec[(size_t)bh * n + qr];
   }
-  float Lq = a.lse[(size_t)bh * n + qr];
-  Lq = (Lq == -INFINITY || my_q >= n) ? INFINITY : Lq * kLog2e;
-  const float Dq = a.dvec[(size_t)bh * n + qr];
 
   const int n_tiles = (n + BC - 1) / BC;
   int j_end = n_tiles;
   if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + BR, n) - 1) / BC + 1);
-  const uint8_t* mrow = SPARSE ? a.mask + (size_t)(q0 / kMaskBlock) * a.mask_t : nullptr;
+  // block-sparse: the workgroup spans two 128-query mask rows, each wave one
+  const uint8_t* mrow0 = nullptr;
+  const uint8_t* mrow1 = nullptr;
+  const uint8_t* mwave = nullptr;
+  if constexpr (SPARSE) {
+    const int t0 = q0 / kMaskBlock;
+    const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
+    mrow0 = a.mask + (size_t)t0 * a.mask_t;
+    mrow1 = a.mask + (size_t)t1 * a.mask_t;
+    mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+  }
   auto next_tile = [&](int j) {
     ++j;
     if constexpr (SPARSE)
-      while (j < j_end && !mrow[(j * BC) / kMaskBlock]) ++j;
+      while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
     return j;
+  };
+  // tiles of this wave's queries that have allowed keys
+  auto live = [&](int jt) {
+    bool l = jt < j_end;
+    if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + 63);
+    if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
+    return l;
   };
 
   KD kd;
   VD vd;
   kd.init(w, lane);
   vd.init(w, lane);
-  auto issue = [&](int jt, int slot) {
-    char* b = smem + slot * SLOT;
-    kd.issue(Kg + (size_t)jt * BC * D, n - jt * BC, b);
-    vd.issue(Vg + (size_t)jt * BC * D, n - jt * BC, b + KD::kSlot);
+  // DMA instruction i (of C) of tile jt into the slot at byte offset so
+  auto dma = [&](int i, int jt, int so) {
+    char* b = smem + so;
+    if (i < KD::kPer) kd.issue_one(i, Kg + (size_t)jt * BC * D, n - jt * BC, b);
+    else vd.issue_one(i - KD::kPer, Vg + (size_t)jt * BC * D, n - jt * BC, b + KD::kSlot);
   };
   const int krow = KL::row_base(c32, g);
   const int ktr = KL::tr_base(lane);
   const int vrow = KD::kSlot + VL::row_base(c32, g);
+  auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
 
-  // settle the register loads before the DMA so waits below count only DMA
-  settle(qreg);
-  settle(oreg);
-  int j = SPARSE ? next_tile(-1) : 0;
-  int jq = j;       // next tile to issue
-  int ahead = 0;    // tiles issued and not yet consumed
-  for (int s = 0; s < kRing - 1 && jq < j_end; ++s) {
-    issue(jq, s);
-    jq = next_tile(jq);
-    ++ahead;
+  vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
+
+  const int j_first = SPARSE ? next_tile(-1) : 0;
+  if (j_first >= j_end) {  // no key tile at all: dQ = 0
+    for (int h = 0; h < 2; ++h) {
+      const int my_q = qw0 + 32 * h + c32;
+      if (my_q < n) {
+        uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
+        for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(dqp + c) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
+  // Every iteration issues exactly C DMA instructions (past the last tile
+  // they reload the first tile into a slot nobody reads), so "tile t+1 has
+  // landed" is always vmcnt <= C at the top of iteration t.
+  int jq = j_first;  // next tile to load
+  int sq = 0;        // its slot
+  auto dma_tile = [&](int i) { dma(i, jq < j_end ? jq : j_first, sq); };
+  auto dma_advance = [&]() {
+    if (jq < j_end) jq = next_tile(jq);
+    sq = slot_next(sq);
+  };
+  for (int t = 0; t < kRing - 1; ++t) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) dma_tile(i);
+    dma_advance();
   }
 
-  f32x16 acc[MB];
+  f32x16 acc[2][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = 0.0f;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
   const float cs = a.c;
-  int it = 0;
+  f32x16 s[2], dp[2];  // S^T and dP^T - D of one block; block 0 runs a tile ahead
 
-  while (j < j_end) {
-    wait_ahead<C>(ahead - 1);
-    __syncthreads();
-    if (jq < j_end) {  // refill the slot every wave finished reading last iteration
-      issue(jq, (it + kRing - 1) % kRing);
-      jq = next_tile(jq);
-      ++ahead;
+  // S^T, dP^T of block h from the K/V slot at byte offset so
+  auto sdp_first = [&](int h, int so) {  // no interleaved vector work
+    const lchar* base = lds_ptr(smem) + so;
+    const lchar* kr = lds_opaque(base + krow);
+    const lchar* vr = lds_opaque(base + vrow);
+    u32x4 kf[2], vf[2];
+    kf[0] = ld_row(kr + KL::row_off(0, 0));
+    vf[0] = ld_row(vr + VL::row_off(0, 0));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+        kf[(ks + 1) & 1] = ld_row(kr + KL::row_off(0, ks + 1));
+        vf[(ks + 1) & 1] = ld_row(vr + VL::row_off(0, ks + 1));
+      }
+      if (ks == 0) {
+        mfma32_vd<Tag, true, true>(s[h], kf[0], qreg[h][0]);
+        mfma32_vd<Tag, true, true>(dp[h], vf[0], oreg[h][0]);
+      } else {
+        mfma32_vd<Tag, false, true>(s[h], kf[ks & 1], qreg[h][ks]);
+        mfma32_vd<Tag, false, true>(dp[h], vf[ks & 1], oreg[h][ks]);
+      }
     }
-    const char* base = smem + (it % kRing) * SLOT;
-    const char* kr = base + krow;
-    const char* kt = base + ktr;
-    const char* vr = base + vrow;
+  };
+
+  // the first tile's block-0 products, then the pipelined sweep
+  vm_wait<2 * C>();
+  __syncthreads();
+  int j = j_first;
+  int so = 0;  // slot of tile j
+  if (!SPARSE || live(j)) sdp_first(0, so);
+
+  auto step = [&](auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int jn = next_tile(j);
+    const int son = slot_next(so);
+    vm_wait<C>();      // tile jn has landed (for this wave's share) ...
+    __syncthreads();   // ... for every wave; the slot refilled below is free
+    // Dense sweeps compute every tile (the causal mask zeroes what lies past
+    // the diagonal, and past the last tile the slot holds a valid reload), so
+    // their loop body has no branch; sparse sweeps skip what the mask drops.
+    const bool live_j = SPARSE ? live(j) : true;
+    const bool live_n = SPARSE ? live(jn) : true;
     const int k0 = j * BC;
-    const bool wave_live = !CAUSAL || (k0 <= qw0 + 31);
-    if (wave_live) {
-      f32x16 s, dp;
-      const f32x16 zero = {};
-      s = mfma32<Tag>(ld_row(kr + KL::row_off(0, 0)), qreg[0], zero);
-      dp = mfma32<Tag>(ld_row(vr + VL::row_off(0, 0)), oreg[0], zero);
+    const lchar* base = lds_ptr(smem) + so;
+    const lchar* kr = lds_opaque(base + krow);
+    const lchar* vr = lds_opaque(base + vrow);
+    const lchar* kt = lds_opaque(base + ktr);
+    u32x4 db[2][PK];
+    // dS^T of block h, elements v0..v1-1 (row v of this lane's column)
+    auto valu = [&](int h, int v0, int v1) {
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) {
-        s = mfma32<Tag>(ld_row(kr + KL::row_off(0, ks)), qreg[ks], s);
-        dp = mfma32<Tag>(ld_row(vr + VL::row_off(0, ks)), oreg[ks], dp);
-      }
-      const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > n);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = fast_exp2(fmaf(s[v], cs, -Lq));
-        if (need_mask) {
-          const int key = k0 + 8 * (v >> 2) + 4 * g + (v & 3);
-          bool dead = key >= n;
-          if constexpr (CAUSAL) dead = dead || key > my_q;
-          if (dead) p = 0.0f;
+      for (int v = v0; v < v1; ++v) {
+        const float p = fast_exp2(fmaf(s[h][v], cs, -Lq[h]));
+        float x = p * (dp[h][v] - Dq[h]);
+        if constexpr (MASK) {
+          // element v holds key k0 + 4g + 8(v/4) + v%4
+          int last = n - 1;
+          if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+          x = (8 * (v >> 2) + (v & 3) > last - k0 - 4 * g) ? 0.0f : x;
         }
-        dp[v] = p * (dp[v] - Dq);
+        dp[h][v] = x;
       }
+    };
+    auto pack = [&](int h) {
 #pragma unroll
-      for (int kk = 0; kk < PK; ++kk) {
-        const u32x4 db = pack8<Tag>(dp, 8 * kk);
+      for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[h], 8 * kk);
+    };
+    auto zero = [&](int h) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = mfma32<Tag>(ld_tr(kt + KL::tr_off(0, kk, 0, mb), kt + KL::tr_off(0, kk, 1, mb)), db, acc[mb]);
-      }
-    }
-    --ahead;
-    ++it;
-    j = next_tile(j);
-  }
+      for (int kk = 0; kk < PK; ++kk) db[h][kk] = 0u;
+    };
 
-  if (my_q < n) {
-    uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
-    const float sc = a.scale;
+    // DMA of the tile two ahead, spread over the iteration (one at a time
+    // keeps the address unit from stalling every wave at once)
+    auto dma_at = [&](int seg, int step, int nsteps) {
+      constexpr int kPerSeg = (C + 2) / 3;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 pk;
-        pk[0] = pack2<Tag>(acc[mb][4 * r] * sc, acc[mb][4 * r + 1] * sc);
-        pk[1] = pack2<Tag>(acc[mb][4 * r + 2] * sc, acc[mb][4 * r + 3] * sc);
-        *reinterpret_cast<u32x2*>(dqp + 32 * mb + 8 * r + 4 * g) = pk;
+      for (int q = 0; q < kPerSeg; ++q) {
+        const int i = seg * kPerSeg + q;
+        if (i < C && step == (2 * q + 1) * nsteps / (2 * kPerSeg)) dma_tile(i);
       }
+    };
+    // S^T, dP^T of block h from the K/V rows at kr/vr; the fragments run kPD
+    // k-steps ahead of the products; vec(ks) is interleaved vector work
+    constexpr int kPD = 3;
+    auto sdp = [&](int h, const lchar* rk, const lchar* rv, auto&& vec) {
+      u32x4 kf[kPD + 1], vf[kPD + 1];
+#pragma unroll
+      for (int ks = 0; ks < kPD && ks < KS; ++ks) {
+        kf[ks] = ld_row(rk + KL::row_off(0, ks));
+        vf[ks] = ld_row(rv + VL::row_off(0, ks));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + kPD < KS) {
+          kf[(ks + kPD) % (kPD + 1)] = ld_row(rk + KL::row_off(0, ks + kPD));
+          vf[(ks + kPD) % (kPD + 1)] = ld_row(rv + VL::row_off(0, ks + kPD));
+        }
+        const int r = ks % (kPD + 1);
+        if (ks == 0) {
+          mfma32_vd<Tag, true, true>(s[h], kf[r], qreg[h][0]);
+          mfma32_vd<Tag, true, true>(dp[h], vf[r], oreg[h][0]);
+        } else {
+          mfma32_vd<Tag, false, true>(s[h], kf[r], qreg[h][ks]);
+          mfma32_vd<Tag, false, true>(dp[h], vf[r], oreg[h][ks]);
+        }
+        vec(ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // ---- segment 1: S^T, dP^T (j, block 1) | dS (j, block 0)
+    if (live_j) {
+      sdp(1, kr, vr, [&](int ks) {
+        valu(0, ks * 16 / KS, (ks + 1) * 16 / KS);
+        dma_at(0, ks, KS);
+      });
+      pack(0);
+    } else {
+      for (int ks = 0; ks < KS; ++ks) dma_at(0, ks, KS);
+      zero(0);
+    }
+
+    // ---- segment 2: S^T, dP^T (jn, block 0) | dS (j, block 1)
+    if (live_n) {
+      const lchar* nbase = lds_ptr(smem) + son;
+      sdp(0, lds_opaque(nbase + krow), lds_opaque(nbase + vrow), [&](int ks) {
+        if (ks == 0 && live_j) {  // block 1's S^T, dP^T complete before its vector work
+          vgpr_drain(s);
+          vgpr_drain(dp);
+        }
+        if (live_j) valu(1, ks * 16 / KS, (ks + 1) * 16 / KS);
+        dma_at(1, ks, KS);
+      });
+    } else {
+      if (live_j) {
+        vgpr_drain(s);
+        vgpr_drain(dp);
+        valu(1, 0, 16);
+      }
+      for (int ks = 0; ks < KS; ++ks) dma_at(1, ks, KS);
+    }
+    if (live_j) pack(1);
+    else zero(1);
+
+    // ---- segment 3: dQ^T (j, blocks 0 and 1)
+    u32x4 kq[kPD + 1];
+#pragma unroll
+    for (int f = 0; f < kPD && f < NF; ++f)
+      kq[f] = ld_tr(kt + KL::tr_off(0, f / MB, 0, f % MB), kt + KL::tr_off(0, f / MB, 1, f % MB));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (f + kPD < NF) {
+        const int fn = f + kPD;
+        kq[fn % (kPD + 1)] = ld_tr(kt + KL::tr_off(0, fn / MB, 0, fn % MB), kt + KL::tr_off(0, fn / MB, 1, fn % MB));
+      }
+      mfma32_acc<Tag>(acc[0][f % MB], kq[f % (kPD + 1)], db[0][f / MB]);
+      mfma32_acc<Tag>(acc[1][f % MB], kq[f % (kPD + 1)], db[1][f / MB]);
+      dma_at(2, f, NF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dma_advance();
+
+    j = jn;
+    so = son;
+  };
+  auto masked = [&](int jt) {
+    return (CAUSAL && jt * BC + BC - 1 > qw0) || (jt * BC + BC > n);
+  };
+  // masked tiles come last: two loops over one body keep the accumulators
+  // out of any branch (the register allocator would copy them there)
+  while (j < j_end && !masked(j)) step(std::false_type{});
+  while (j < j_end) step(std::true_type{});
+
+  agpr_drain(acc[0]);
+  agpr_drain(acc[1]);
+  const float sc = a.scale;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int my_q = qw0 + 32 * h + c32;
+    if (my_q < n) {
+      uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 pk;
+          pk[0] = pack2<Tag>(acc[h][mb][4 * r] * sc, acc[h][mb][4 * r + 1] * sc);
+          pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * sc, acc[h][mb][4 * r + 3] * sc);
+          *reinterpret_cast<u32x2*>(dqp + 32 * mb + 8 * r + 4 * g) = pk;
+        }
+    }
   }
 }
 
@@ -432,7 +622,7 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const BwdArgs& a, hipStrea
 }  // namespace
 
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st) {
-  a.nqb = (a.n + 127) / 128;       // 128 queries per dQ workgroup
+  a.nqb = (a.n + kDqRows - 1) / kDqRows;
   a.nblk_q = a.nqb * bh;
   a.nkb = (a.n + 127) / 128;
   a.nblk_kv = a.nkb * bh;

@@ -48,6 +48,77 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// D += A B with D pinned to accumulation registers (AGPRs) for its whole
+// lifetime.  Left to itself the compiler copies long-lived accumulators
+// between register files every iteration once a kernel needs more than 256
+// registers.  Hazards the compiler cannot see through the asm: a VALU write
+// of A or B needs two wait states before the product reads it (the s_nop);
+// dependent accumulation into the same registers is interlocked; and VALU
+// reads of D after the last product wait in agpr_drain().
+template <typename Tag>
+__device__ __forceinline__ void mfma32_acc(f32x16& d, u32x4 a, u32x4 b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (std::is_same<Tag, bf16_tag>::value)
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+#endif
+}
+
+// D = A B (FIRST) or D += A B with D in VGPRs, for results the VALU reads
+// next (vgpr_drain() covers the read latency); B_AGPR: B is held in AGPRs.
+#define FA_MFMA_VD(OP, FIRST, BC)                                                         \
+  do {                                                                                   \
+    if (FIRST)                                                                           \
+      asm volatile("s_nop 2\n\t" OP " %0, %1, %2, 0" : "=&v"(d) : "v"(a), BC(b));        \
+    else                                                                                 \
+      asm volatile("s_nop 2\n\t" OP " %0, %1, %2, %0" : "+v"(d) : "v"(a), BC(b));        \
+  } while (0)
+#define FA_CONSTRAINT_A(x) "a"(x)
+#define FA_CONSTRAINT_V(x) "v"(x)
+template <typename Tag, bool FIRST, bool B_AGPR>
+__device__ __forceinline__ void mfma32_vd(f32x16& d, u32x4 a, u32x4 b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (std::is_same<Tag, bf16_tag>::value) {
+    if constexpr (B_AGPR) FA_MFMA_VD("v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_A);
+    else FA_MFMA_VD("v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_V);
+  } else {
+    if constexpr (B_AGPR) FA_MFMA_VD("v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_A);
+    else FA_MFMA_VD("v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_V);
+  }
+#endif
+}
+#undef FA_MFMA_VD
+#undef FA_CONSTRAINT_A
+#undef FA_CONSTRAINT_V
+
+template <int N>
+__device__ __forceinline__ void vgpr_drain(f32x16 (&d)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3" : "+v"(d[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("" : "+v"(d[i]));
+#endif
+}
+
+// 16-byte global load straight into AGPRs, for operands that only ever feed
+// products through the asm wrappers above.  The compiler does not track it:
+// the caller waits with vm_wait<0>() before the first use.
+__device__ __forceinline__ void gload_agpr(u32x4& r, const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(r) : "v"(p) : "memory");
+#endif
+}
+
+// Wait out the product-to-VALU read latency (at most 20 wait states for a
+// 32x32x16 product) before any accumulator in d is read.
+template <int N>
+__device__ __forceinline__ void agpr_drain(f32x16 (&d)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3" : "+a"(d[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("" : "+a"(d[i]));
+}
+
 // Round two floats to the 16-bit input type (nearest-even) and pack.
 template <typename Tag>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -141,8 +212,29 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 __device__ __forceinline__ u32x4 ld_row(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// 32-bit LDS pointers.  lds_opaque() hides a per-iteration base from the
+// optimiser so constant offsets stay in the instructions' offset fields
+// instead of being hoisted into one register per offset.
+typedef __attribute__((address_space(3))) char lchar;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ lchar* lds_ptr(char* p) { return (lchar*)p; }
+__device__ __forceinline__ const lchar* lds_opaque(const lchar* p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this; its asm constraints are x86's
+  asm volatile("" : "+v"(p));
+#endif
+  return p;
+}
+__device__ __forceinline__ u32x4 ld_row(const lchar* p) { return *(const lds_u32x4*)p; }
+
 // One MFMA operand (8 slots) by two transpose reads.
 __device__ __forceinline__ u32x4 ld_tr(const char* p0, const char* p1) {
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  const s16x8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(u32x4, ab);
+}
+__device__ __forceinline__ u32x4 ld_tr(const lchar* p0, const lchar* p1) {
   typedef short s16x8_t __attribute__((ext_vector_type(8)));
   const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
   const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
@@ -204,6 +296,19 @@ struct Stage {
 // row padding or past the tile stay idle).  Rows at or beyond `valid` are
 // clamped to the last valid row so every load stays in bounds.  Completion
 // is awaited with dma_wait() (vmcnt) before the workgroup barrier.
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.  Issued
+// through asm so the compiler does not track the LDS write: left to itself
+// it makes the next LDS read wait for every outstanding DMA (vmcnt(0)),
+// which would serialise the prefetch.  The caller orders the data with
+// explicit vm_wait<>() and barriers.  (An M0 write needs one wait state
+// before the DMA reads it.)
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+#endif
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(uintptr_t)(lchar*)p; }
+
 template <int ROWS, int D, bool TR, int NW>
 struct Dma {
   using L = Pad<D, TR>;
@@ -211,7 +316,7 @@ struct Dma {
   static constexpr int kBlocks = (kBytes + 1023) / 1024;
   static constexpr int kPer = (kBlocks + NW - 1) / NW;   // DMA instructions per wave per tile
   static constexpr int kSlot = kPer * NW * 1024;         // LDS bytes reserved per tile
-  int src[kPer];  // element offset inside the tile, or -1 (padding / past the tile)
+  int src[kPer];  // element offset inside the tile (0 for padding / past the tile)
   int wave;
 
   __device__ void init(int w, int lane) {
@@ -219,7 +324,7 @@ struct Dma {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int off = (w + NW * k) * 1024 + 16 * lane;
-      src[k] = -1;
+      src[k] = 0;
       if (off < kBytes) {
         const int r = off / L::S;
         const int p = off - r * L::S - L::rot(r);
@@ -232,13 +337,28 @@ struct Dma {
   // (bytes no operand fetch reads) load the tile's first 16 bytes there.
   // Outstanding-load counts are therefore exact and uniform across waves.
   __device__ __forceinline__ void issue(const uint16_t* __restrict__ t0, int valid, char* l0) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass only needs the declaration
+    if (valid >= ROWS) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int b = wave + NW * k;
-      int e = src[k] < 0 ? 0 : src[k];
-      if (valid < ROWS && e / D >= valid) e = (valid - 1) * D + (e % D);
-      __builtin_amdgcn_global_load_lds(t0 + e, (__attribute__((address_space(3))) void*)(l0 + b * 1024), 16, 0, 0);
+      for (int k = 0; k < kPer; ++k) dma16(t0 + src[k], lds_addr(l0 + (wave + NW * k) * 1024));
+    } else {  // last, partial tile: rows past the end re-read the last row
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        int e = src[k];
+        if (e / D >= valid) e = (valid - 1) * D + (e % D);
+        dma16(t0 + e, lds_addr(l0 + (wave + NW * k) * 1024));
+      }
     }
+#endif
+  }
+  // Instruction k of issue() alone, so a caller can spread a tile's DMA
+  // between its own products instead of queueing it all at once.
+  __device__ __forceinline__ void issue_one(int k, const uint16_t* __restrict__ t0, int valid, char* l0) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    int e = src[k];
+    if (valid < ROWS && e / D >= valid) e = (valid - 1) * D + (e % D);
+    dma16(t0 + e, lds_addr(l0 + (wave + NW * k) * 1024));
+#endif
   }
   // Moves two tiles of the same geometry with one set of offsets.
   __device__ __forceinline__ void issue2(const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
