@@ -248,18 +248,16 @@ __device__ __forceinline__ void wait_ahead(int ahead) {  // ahead: tiles issued 
 }
 
 // Each wave owns 64 queries, two 32-query blocks h = 0, 1, and runs one wave
-// per SIMD (the operands take ~400 registers).  Within a wave the matrix
+// per SIMD (Q and dO fragments and the dQ accumulators fill the 256 AGPRs).
+// Every K or V fragment read from LDS feeds both blocks' products, half the
+// LDS traffic per product of a 32-query wave.  Within a wave the matrix
 // cores and the vector ALU overlap only when their instructions are
-// interleaved, and every step of a block depends on the previous one
-// (S, dP -> dS -> dQ), so the wave software-pipelines its two blocks with
-// block 0 one step ahead.  Iteration t (tile j_t, next tile j_{t+1}):
-//   segment 1: products S^T, dP^T of (j_t, block 1)      | dS of (j_t, block 0)
-//   segment 2: products dQ^T of (j_t, block 0),
-//              S^T, dP^T of (j_{t+1}, block 0)           | dS of (j_t, block 1), DMA
-//   segment 3: products dQ^T of (j_t, block 1)
-// K/V tiles stream through a ring of four LDS slots; DMA runs two tiles
-// ahead, one barrier per iteration makes the next tile visible and frees
-// the slot refilled in the same iteration.
+// interleaved, and each tile's steps depend on each other (S, dP -> dS ->
+// dQ), so the sweep is software-pipelined by one tile: the products S^T,
+// dP^T of the next tile run interleaved with the softmax-gradient vector
+// work of the current one.  K/V tiles stream through a ring of four LDS
+// slots; DMA runs two tiles ahead, one barrier per iteration makes the next
+// tile visible and frees the slot refilled in the same iteration.
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = kDqRows;         // queries per workgroup (4 waves x 64)
@@ -391,154 +389,135 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
   const float cs = a.c;
-  f32x16 s[2], dp[2];  // S^T and dP^T - D of one block; block 0 runs a tile ahead
+  // S^T and dP^T - D of both blocks for two tiles: set X = the tile whose
+  // dS is being formed, set Y = the next tile, whose products run meanwhile
+  f32x16 s[2][2], dp[2][2];
+  constexpr int kPD = 6;  // LDS fragments run kPD k-steps ahead of the products
 
-  // S^T, dP^T of block h from the K/V slot at byte offset so
-  auto sdp_first = [&](int h, int so) {  // no interleaved vector work
-    const lchar* base = lds_ptr(smem) + so;
-    const lchar* kr = lds_opaque(base + krow);
-    const lchar* vr = lds_opaque(base + vrow);
-    u32x4 kf[2], vf[2];
-    kf[0] = ld_row(kr + KL::row_off(0, 0));
-    vf[0] = ld_row(vr + VL::row_off(0, 0));
+  // One product of both blocks for the tile in slot `so` into set Y: S^T =
+  // K Q^T (P = false, K rows) or dP^T - D = V dO^T (P = true, V rows).
+  // Each fragment feeds both blocks; vec(ks) is vector work interleaved per
+  // k-step.  S^T and dP^T run as two sweeps so that set Y's dP^T registers
+  // are only needed once half of set X has been consumed.
+  auto prod = [&](auto y_c, auto p_c, int so, bool on, auto&& vec) {
+    constexpr int Y = decltype(y_c)::value;
+    constexpr bool P = decltype(p_c)::value;
+    const lchar* rows = lds_opaque(lds_ptr(smem) + so + (P ? vrow : krow));
+    u32x4 fr[kPD + 1];
+    auto rd = [&](int ks) { return P ? ld_row(rows + VL::row_off(0, ks)) : ld_row(rows + KL::row_off(0, ks)); };
+    if (on) {
+#pragma unroll
+      for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd(ks);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) {
-        kf[(ks + 1) & 1] = ld_row(kr + KL::row_off(0, ks + 1));
-        vf[(ks + 1) & 1] = ld_row(vr + VL::row_off(0, ks + 1));
-      }
-      if (ks == 0) {
-        mfma32_vd<Tag, true, true>(s[h], kf[0], qreg[h][0]);
-        mfma32_vd<Tag, true, true>(dp[h], vf[0], oreg[h][0]);
+      if (on) {
+        if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd(ks + kPD);
+        const u32x4 f = fr[ks % (kPD + 1)];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x16& d = P ? dp[Y][h] : s[Y][h];
+          const u32x4 b = P ? oreg[h][ks] : qreg[h][ks];
+          if (ks == 0) mfma32_vd<Tag, true, true>(d, f, b);
+          else mfma32_vd<Tag, false, true>(d, f, b);
+          // each product is followed by its share of vector work, so the
+          // next product issues as the matrix core frees up
+          vec(2 * ks + h);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
-        mfma32_vd<Tag, false, true>(s[h], kf[ks & 1], qreg[h][ks]);
-        mfma32_vd<Tag, false, true>(dp[h], vf[ks & 1], oreg[h][ks]);
+        vec(2 * ks);
+        vec(2 * ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+  auto sdp = [&](auto y_c, int so, bool on) {
+    prod(y_c, std::false_type{}, so, on, [](int) {});
+    prod(y_c, std::true_type{}, so, on, [](int) {});
+  };
 
-  // the first tile's block-0 products, then the pipelined sweep
+  // the first tile's products, then the pipelined sweep
   vm_wait<2 * C>();
   __syncthreads();
   int j = j_first;
   int so = 0;  // slot of tile j
-  if (!SPARSE || live(j)) sdp_first(0, so);
+  sdp(std::integral_constant<int, 0>{}, so, !SPARSE || live(j));
+  vgpr_drain(s[0]);
+  vgpr_drain(dp[0]);
 
-  auto step = [&](auto mask_c) {
+  // Iteration over tile j (set X) with the next tile jn (set Y = 1 - X):
+  //   part A: S^T, dP^T of (jn, both blocks)  | dS of (j, both blocks), DMA
+  //   part B: dQ^T += K^T dS^T of (j, both blocks), DMA
+  // The body is unrolled for X = 0 and X = 1.  The tile count is the
+  // workgroup's, so every wave runs every iteration (barrier per iteration):
+  // keys past a query's diagonal or the sequence end get dS = 0.
+  auto step = [&](auto x_c, auto mask_c) {
+    constexpr int X = decltype(x_c)::value;
+    constexpr int Y = 1 - X;
     constexpr bool MASK = decltype(mask_c)::value;
     const int jn = next_tile(j);
     const int son = slot_next(so);
     vm_wait<C>();      // tile jn has landed (for this wave's share) ...
     __syncthreads();   // ... for every wave; the slot refilled below is free
-    // Dense sweeps compute every tile (the causal mask zeroes what lies past
-    // the diagonal, and past the last tile the slot holds a valid reload), so
-    // their loop body has no branch; sparse sweeps skip what the mask drops.
+    // dense sweeps compute every tile, the dummy one included: its keys lie
+    // past the sequence end, so the mask gives dS = 0, and its slot holds a
+    // valid reload; branches here would cost fetch bubbles a lone wave
+    // cannot hide
     const bool live_j = SPARSE ? live(j) : true;
     const bool live_n = SPARSE ? live(jn) : true;
     const int k0 = j * BC;
-    const lchar* base = lds_ptr(smem) + so;
-    const lchar* kr = lds_opaque(base + krow);
-    const lchar* vr = lds_opaque(base + vrow);
-    const lchar* kt = lds_opaque(base + ktr);
+    // element v of block h holds key k0 + 4g + 8(v/4) + v%4; it is allowed
+    // while that offset is at most lim[h]
+    int lim[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int last = n - 1;
+      if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+      lim[h] = last - k0 - 4 * g;
+    }
+    constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
+    // ---- part A
     u32x4 db[2][PK];
-    // dS^T of block h, elements v0..v1-1 (row v of this lane's column)
+    // dS^T of block h, elements v0..v1-1, then packed once the block is done
     auto valu = [&](int h, int v0, int v1) {
-#pragma unroll
-      for (int v = v0; v < v1; ++v) {
-        const float p = fast_exp2(fmaf(s[h][v], cs, -Lq[h]));
-        float x = p * (dp[h][v] - Dq[h]);
-        if constexpr (MASK) {
-          // element v holds key k0 + 4g + 8(v/4) + v%4
-          int last = n - 1;
-          if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
-          x = (8 * (v >> 2) + (v & 3) > last - k0 - 4 * g) ? 0.0f : x;
-        }
-        dp[h][v] = x;
-      }
-    };
-    auto pack = [&](int h) {
-#pragma unroll
-      for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[h], 8 * kk);
-    };
-    auto zero = [&](int h) {
-#pragma unroll
-      for (int kk = 0; kk < PK; ++kk) db[h][kk] = 0u;
-    };
-
-    // DMA of the tile two ahead, spread over the iteration (one at a time
-    // keeps the address unit from stalling every wave at once)
-    auto dma_at = [&](int seg, int step, int nsteps) {
-      constexpr int kPerSeg = (C + 2) / 3;
-#pragma unroll
-      for (int q = 0; q < kPerSeg; ++q) {
-        const int i = seg * kPerSeg + q;
-        if (i < C && step == (2 * q + 1) * nsteps / (2 * kPerSeg)) dma_tile(i);
-      }
-    };
-    // S^T, dP^T of block h from the K/V rows at kr/vr; the fragments run kPD
-    // k-steps ahead of the products; vec(ks) is interleaved vector work
-    constexpr int kPD = 3;
-    auto sdp = [&](int h, const lchar* rk, const lchar* rv, auto&& vec) {
-      u32x4 kf[kPD + 1], vf[kPD + 1];
-#pragma unroll
-      for (int ks = 0; ks < kPD && ks < KS; ++ks) {
-        kf[ks] = ld_row(rk + KL::row_off(0, ks));
-        vf[ks] = ld_row(rv + VL::row_off(0, ks));
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + kPD < KS) {
-          kf[(ks + kPD) % (kPD + 1)] = ld_row(rk + KL::row_off(0, ks + kPD));
-          vf[(ks + kPD) % (kPD + 1)] = ld_row(rv + VL::row_off(0, ks + kPD));
-        }
-        const int r = ks % (kPD + 1);
-        if (ks == 0) {
-          mfma32_vd<Tag, true, true>(s[h], kf[r], qreg[h][0]);
-          mfma32_vd<Tag, true, true>(dp[h], vf[r], oreg[h][0]);
-        } else {
-          mfma32_vd<Tag, false, true>(s[h], kf[r], qreg[h][ks]);
-          mfma32_vd<Tag, false, true>(dp[h], vf[r], oreg[h][ks]);
-        }
-        vec(ks);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    // ---- segment 1: S^T, dP^T (j, block 1) | dS (j, block 0)
-    if (live_j) {
-      sdp(1, kr, vr, [&](int ks) {
-        valu(0, ks * 16 / KS, (ks + 1) * 16 / KS);
-        dma_at(0, ks, KS);
-      });
-      pack(0);
-    } else {
-      for (int ks = 0; ks < KS; ++ks) dma_at(0, ks, KS);
-      zero(0);
-    }
-
-    // ---- segment 2: S^T, dP^T (jn, block 0) | dS (j, block 1)
-    if (live_n) {
-      const lchar* nbase = lds_ptr(smem) + son;
-      sdp(0, lds_opaque(nbase + krow), lds_opaque(nbase + vrow), [&](int ks) {
-        if (ks == 0 && live_j) {  // block 1's S^T, dP^T complete before its vector work
-          vgpr_drain(s);
-          vgpr_drain(dp);
-        }
-        if (live_j) valu(1, ks * 16 / KS, (ks + 1) * 16 / KS);
-        dma_at(1, ks, KS);
-      });
-    } else {
       if (live_j) {
-        vgpr_drain(s);
-        vgpr_drain(dp);
-        valu(1, 0, 16);
+#pragma unroll
+        for (int v = v0; v < v1; ++v) {
+          const float p = fast_exp2(fmaf(s[X][h][v], cs, -Lq[h]));
+          float x = p * (dp[X][h][v] - Dq[h]);
+          if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
+          dp[X][h][v] = x;
+        }
+        // keep the chunk's work here, between the products (the optimiser
+        // would otherwise sink the masking into the packing below)
+#pragma unroll
+        for (int v = v0; v < v1; ++v) asm volatile("" : "+v"(dp[X][h][v]));
+        if (v1 == 16) {
+#pragma unroll
+          for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[X][h], 8 * kk);
+        }
+      } else if (v1 == 16) {
+#pragma unroll
+        for (int kk = 0; kk < PK; ++kk) db[h][kk] = u32x4{0u, 0u, 0u, 0u};
       }
-      for (int ks = 0; ks < KS; ++ks) dma_at(1, ks, KS);
-    }
-    if (live_j) pack(1);
-    else zero(1);
-
-    // ---- segment 3: dQ^T (j, blocks 0 and 1)
+    };
+    // slot u = 0 .. 2KS-1 of a sweep: the product of k-step u/2, block u%2
+    auto dma_a = [&](int u, int half) {
+#pragma unroll
+      for (int q = 0; q < kDmaA; ++q)
+        if (half * 2 * KS + u == (2 * q + 1) * 2 * KS / kDmaA) dma_tile(q);
+    };
+    prod(std::integral_constant<int, Y>{}, std::false_type{}, son, live_n, [&](int u) {
+      valu(0, u * 16 / (2 * KS), (u + 1) * 16 / (2 * KS));
+      dma_a(u, 0);
+    });
+    prod(std::integral_constant<int, Y>{}, std::true_type{}, son, live_n, [&](int u) {
+      valu(1, u * 16 / (2 * KS), (u + 1) * 16 / (2 * KS));
+      dma_a(u, 1);
+    });
+    // ---- part B
+    const lchar* kt = lds_opaque(lds_ptr(smem) + so + ktr);
     u32x4 kq[kPD + 1];
 #pragma unroll
     for (int f = 0; f < kPD && f < NF; ++f)
@@ -551,21 +530,37 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       }
       mfma32_acc<Tag>(acc[0][f % MB], kq[f % (kPD + 1)], db[0][f / MB]);
       mfma32_acc<Tag>(acc[1][f % MB], kq[f % (kPD + 1)], db[1][f / MB]);
-      dma_at(2, f, NF);
+#pragma unroll
+      for (int q = kDmaA; q < C; ++q)
+        if (f == (2 * (q - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(q);
       __builtin_amdgcn_sched_barrier(0);
     }
     dma_advance();
-
     j = jn;
     so = son;
   };
-  auto masked = [&](int jt) {
-    return (CAUSAL && jt * BC + BC - 1 > qw0) || (jt * BC + BC > n);
-  };
-  // masked tiles come last: two loops over one body keep the accumulators
-  // out of any branch (the register allocator would copy them there)
-  while (j < j_end && !masked(j)) step(std::false_type{});
-  while (j < j_end) step(std::true_type{});
+  // Two iterations per trip: with an odd tile count the last iteration runs
+  // on no tile (dS = 0, its slot holds a valid reload), so the register sets
+  // X/Y keep fixed roles and the accumulators never sit in a branch (which
+  // would make the register allocator copy them every iteration).
+  // Dense sweeps start with the tiles no key of which is masked for this
+  // wave (keys below its diagonal and inside the sequence), an even number
+  // of them, without any per-element test; the rest, padded to an even
+  // count, run with the mask.  The total is the same for every wave.
+  int n_plain = 0;
+  if constexpr (!SPARSE) {
+    int jm = n / BC;                       // first tile reaching past the sequence end
+    if constexpr (CAUSAL) jm = min(jm, qw0 / BC);  // first tile crossing the diagonal
+    n_plain = max(jm - j_first, 0) & ~1;
+  }
+  for (int t = 0; t < n_plain; t += 2) {
+    step(std::integral_constant<int, 0>{}, std::false_type{});
+    step(std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  while (j < j_end) {
+    step(std::integral_constant<int, 0>{}, std::true_type{});
+    step(std::integral_constant<int, 1>{}, std::true_type{});
+  }
 
   agpr_drain(acc[0]);
   agpr_drain(acc[1]);

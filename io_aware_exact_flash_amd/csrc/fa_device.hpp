@@ -355,8 +355,8 @@ struct Dma {
   // between its own products instead of queueing it all at once.
   __device__ __forceinline__ void issue_one(int k, const uint16_t* __restrict__ t0, int valid, char* l0) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    int e = src[k];
-    if (valid < ROWS && e / D >= valid) e = (valid - 1) * D + (e % D);
+    // rows past the end re-read the last row (branch-free)
+    const int e = src[k] - max(src[k] / D - (valid - 1), 0) * D;
     dma16(t0 + e, lds_addr(l0 + (wave + NW * k) * 1024));
 #endif
   }
