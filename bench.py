@@ -197,7 +197,7 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="workload timed for the JSON line (default 4: 4x40x8192x128 causal bf16)")
     ap.add_argument("--all", action="store_true", help="also time every other workload (stderr lines)")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="(batch, head) pairs the oracle baseline runs")
+    ap.add_argument("--cpu-heads", type=int, default=10, help="(batch, head) pairs the oracle baseline runs (about 1 s each at N=8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
