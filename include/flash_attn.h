@@ -87,7 +87,8 @@ fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype,
 
 /*
  * Device workspace bytes flash_attn_bwd / flash_attn_blocksparse_bwd need:
- * one float32 per query row for D_i = rowsum(dO o O), rounded up to 256.
+ * two float32 per query row (D_i = rowsum(dO o O) and the log-sum-exp in
+ * base 2), each array rounded up to 256 bytes plus 256 spare bytes.
  * Returns 0 for empty problems; never fails.
  */
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype);

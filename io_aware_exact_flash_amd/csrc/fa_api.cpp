@@ -89,9 +89,16 @@ fa_status hip_status(const char* fn, hipError_t e) {
   return fail(FA_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
 }
 
-size_t workspace_bytes(long long bh, long long n) {
+// Two float32 arrays of B*H*N (D and the base-2 LSE), each followed by
+// 256 spare bytes (16-byte loads of a ragged last tile may reach past the
+// end) and 256-byte aligned.
+size_t ws_array_bytes(long long bh, long long n) {
   size_t b = (size_t)bh * (size_t)n * sizeof(float);
-  return (b + 255) & ~(size_t)255;
+  return ((b + 255) & ~(size_t)255) + 256;
+}
+size_t workspace_bytes(long long bh, long long n) {
+  if (bh <= 0 || n <= 0) return 0;
+  return 2 * ws_array_bytes(bh, n);
 }
 
 fa_status run_fwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q,
@@ -147,6 +154,7 @@ fa_status run_bwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, co
   a.dout = dout;
   a.lse = lse;
   a.dvec = static_cast<float*>(ws);
+  a.lt = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_array_bytes(p.bh, N));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -34,10 +34,14 @@ constexpr int kNT = 256;
 constexpr int kDqRows = 256;  // queries per dQ workgroup
 
 // ------------------------------------------------------------ D pre-pass
+// Also writes the base-2 log-sum-exp L log2(e) the dK/dV pass subtracts,
+// +inf for rows without any allowed key (so that P = exp2(S c - Lt) = 0).
 template <typename Tag, int D>
 __global__ __launch_bounds__(kNT) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dout,
-                                                      float* __restrict__ dvec, long rows) {
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ dvec,
+                                                      float* __restrict__ lt, long rows) {
   constexpr int TPR = D / 8;  // threads per row, 16 bytes each
   const long row = (long)blockIdx.x * (kNT / TPR) + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
@@ -53,26 +57,48 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) dvec[row] = acc;
+  if (row < rows && c == 0) {
+    dvec[row] = acc;
+    const float l = lse[row];
+    lt[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
 }
 
 // ------------------------------------------------------------ dK / dV pass
+// One workgroup per 128 keys, four waves of 32 keys, one wave per SIMD.  A
+// wave keeps its K^T and V^T fragments and its dK^T, dV^T accumulators in
+// AGPRs and sweeps the query tiles (32 queries), which stream through a ring
+// of four LDS slots by DMA two tiles ahead (Q and dO row-major and padded,
+// read by rows for S, dP and by transpose reads for dV, dK; plus the
+// tile's base-2 LSE and D).  Per tile:
+//   S = Q K^T, dP - D = dO V^T, P = exp2(S c - Lt), dS = P o (dP - D),
+//   dV^T += dO^T P, dK^T += Q^T dS.
+// Every row of P and dS is a register row (the lane holds one key), so they
+// feed the dV/dK products as B operands without leaving registers.  The
+// sweep is software-pipelined by one tile: S, dP of the next tile run
+// interleaved with the vector work (P, dS) of the current one.
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 128;            // keys per workgroup (4 waves x 32)
   constexpr int BQ = 32;              // queries per tile
-  constexpr int NQB = BQ / 32;        // 32-query blocks per tile
-  constexpr int KS = D / 16;
-  constexpr int NB = D / 32;
-  constexpr int PK = BQ / 16;
-  using TL = Pad<D, true>;            // Q and dO: row reads and transpose reads
+  constexpr int KS = D / 16;          // k-steps of the S/dP products
+  constexpr int NB = D / 32;          // 32-row blocks of dK^T / dV^T
+  constexpr int PK = BQ / 16;         // k-steps of the dK/dV products
+  constexpr int NF = PK * NB;         // transpose fragments per operand per tile
+  constexpr int kRing = 4;
+  using TL = Pad<D, true>;            // Q and dO tiles: row reads and transpose reads
   using QD = Dma<BQ, D, true, kNT / 64>;
-  constexpr int TILE = QD::kSlot;     // LDS bytes per tile (DMA writes whole slots)
-  constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // Q, dO, L*log2e, D
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  constexpr int LDO = QD::kSlot;      // dO tile within a slot
+  constexpr int LLD = 2 * QD::kSlot;  // base-2 LSE (32 floats) then D (32 floats)
+  constexpr int SLOT = 2 * QD::kSlot + 256;
+  constexpr int C = 2 * QD::kPer + 1; // DMA instructions per wave per tile
+  static_assert(3 * C < 64, "vmcnt range");
+  static_assert(SLOT % 256 == 0, "slot alignment");
+  __shared__ __attribute__((aligned(256))) char smem[kRing * SLOT];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
   const int n = a.n;
   const int lb = xcd_remap(blockIdx.x, a.nblk_kv);
@@ -83,66 +109,86 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
   const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
-  const float* __restrict__ Lg = a.lse + (size_t)bh * n;
+  const float* __restrict__ Ltg = a.lt + (size_t)bh * n;
   const float* __restrict__ Dg = a.dvec + (size_t)bh * n;
 
   const int k0 = kb * BKV;
   const int kw0 = k0 + w * 32;
   const int my_k = kw0 + c32;
 
-  u32x4 kreg[KS], vreg[KS];
+  u32x4 kreg[KS], vreg[KS];  // K^T, V^T fragments (B operands), in AGPRs
   {
     const size_t r = (size_t)min(my_k, n - 1) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = *reinterpret_cast<const u32x4*>(Kg + r + 16 * ks);
-      vreg[ks] = *reinterpret_cast<const u32x4*>(Vg + r + 16 * ks);
+      gload_agpr(kreg[ks], Kg + r + 16 * ks);
+      gload_agpr(vreg[ks], Vg + r + 16 * ks);
     }
   }
+  vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
 
   const int n_tiles = (n + BQ - 1) / BQ;
-  auto live = [&](int i) {
+  auto tile_live = [&](int i) {
     if constexpr (SPARSE) return a.mask[(size_t)((i * BQ) / kMaskBlock) * a.mask_t + kb] != 0;
     return true;
   };
   auto next_tile = [&](int i) {
     ++i;
-    while (i < n_tiles && !live(i)) ++i;
+    if constexpr (SPARSE)
+      while (i < n_tiles && !tile_live(i)) ++i;
     return i;
   };
-
-  QD dma;  // Q and dO tiles share one geometry
-  dma.init(w, lane);
-  float lv = 0.0f, dv = 0.0f;
-  // issue the DMA of tile i into buffer b; L*log2(e) and D go through registers
-  auto stage_ld = [&](int i, char* b) {
-    dma.issue2(Qg + (size_t)i * BQ * D, dOg + (size_t)i * BQ * D, n - i * BQ, b, b + TILE);
-    if (tid < BQ) {
-      const int row = i * BQ + tid;
-      const float L = row < n ? Lg[row] : -INFINITY;
-      lv = (L == -INFINITY) ? INFINITY : L * kLog2e;  // rows with no keys get P = 0
-      dv = row < n ? Dg[row] : 0.0f;
+  int i_first = CAUSAL ? k0 / BQ : 0;
+  if (!tile_live(i_first)) i_first = next_tile(i_first);
+  if (i_first >= n_tiles) {  // no query sees these keys: dK = dV = 0
+    if (my_k < n) {
+      uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
+      uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
+      for (int c = 8 * g; c < D; c += 16) {
+        *reinterpret_cast<u32x4*>(dkp + c) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(dvp + c) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
-  };
-  auto stage_st = [&](char* b) {
-    if (tid < BQ) {
-      reinterpret_cast<float*>(b + 2 * TILE)[tid] = lv;
-      reinterpret_cast<float*>(b + 2 * TILE + BQ * 4)[tid] = dv;
-    }
-  };
-  const int rread = TL::row_base(c32, g);
-  const int tread = TL::tr_base(lane);
-
-  int i = CAUSAL ? k0 / BQ : 0;
-  if (!live(i)) i = next_tile(i);
-  if (i < n_tiles) {
-    stage_ld(i, smem);
-    stage_st(smem);
+    return;
   }
-  settle(kreg);
-  settle(vreg);
-  dma_wait();
-  __syncthreads();
+
+  QD qd;  // Q and dO tiles share one geometry
+  qd.init(w, lane);
+  // DMA instruction t (of C) of tile it into the slot at byte offset so:
+  // Q and dO share the tile geometry; the last one moves the tile's base-2
+  // LSE (lanes 0-7) and D (lanes 8-15), four rows per lane.  A lane whose
+  // rows start past the end reads the last row instead (those rows are
+  // dead); one that straddles the end reads up to 3 floats past it, which
+  // the workspace's spare bytes cover.
+  auto dma = [&](int t, int it, int so) {
+    char* b = smem + so;
+    const int valid = n - it * BQ;
+    if (t < QD::kPer) qd.issue_one(t, Qg + (size_t)it * BQ * D, valid, b);
+    else if (t < 2 * QD::kPer) qd.issue_one(t - QD::kPer, dOg + (size_t)it * BQ * D, valid, b + LDO);
+    else if (lane < 16) {
+      const int row = min(it * BQ + 4 * (lane & 7), n - 1);
+      dma16((lane < 8 ? Ltg : Dg) + row, lds_addr(b + LLD));
+    }
+  };
+  const int rrow = TL::row_base(c32, g);
+  const int rtr = TL::tr_base(lane);
+  auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
+
+  // Every iteration issues exactly C DMA instructions (past the last tile
+  // they reload the first tile into a slot nobody reads), so "tile t+1 has
+  // landed" is always vmcnt <= C at the top of iteration t.
+  int iq = i_first;  // next tile to load
+  int sq = 0;        // its slot
+  auto dma_tile = [&](int t) { dma(t, iq < n_tiles ? iq : i_first, sq); };
+  auto dma_advance = [&]() {
+    if (iq < n_tiles) iq = next_tile(iq);
+    sq = slot_next(sq);
+  };
+  for (int t = 0; t < kRing - 1; ++t) {
+#pragma unroll
+    for (int u = 0; u < C; ++u) dma_tile(u);
+    dma_advance();
+  }
 
   f32x16 dkacc[NB], dvacc[NB];
 #pragma unroll
@@ -151,72 +197,175 @@ __global__ __launch_bounds__(kNT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     dvacc[nb] = 0.0f;
   }
   const float cs = a.c;
-  int buf = 0;
+  // S and dP - D for two tiles: set X = the tile whose P, dS are being
+  // formed, set Y = the next tile, whose products run meanwhile
+  f32x16 s[2], dp[2];
+  constexpr int kPD = 3;  // LDS fragments run kPD k-steps ahead of the products
 
-  while (i < n_tiles) {
-    const int in = next_tile(i);
-    if (in < n_tiles) stage_ld(in, smem + (buf ^ 1) * BUF);
-    const char* B = smem + buf * BUF;
-    const char* qr = B + rread;
-    const char* orr = B + TILE + rread;
-    const char* qt = B + tread;
-    const char* ot = B + TILE + tread;
-    const float* Ls = reinterpret_cast<const float*>(B + 2 * TILE) + 4 * g;
-    const float* Ds = reinterpret_cast<const float*>(B + 2 * TILE + BQ * 4) + 4 * g;
-    const int q0 = i * BQ;
-    const bool wave_live = !CAUSAL || (q0 + BQ - 1 >= kw0);
-    if (wave_live) {
-      f32x16 s[NQB], dp[NQB];
-      const f32x16 zero = {};
+  // S = Q K^T and dP = dO V^T for the tile in slot `so` into set Y, the two
+  // accumulation chains interleaved (a single chain would wait out each
+  // product's latency); vec(u) is vector work after product u (0 .. 2KS-1)
+  auto prod = [&](auto y_c, int so, auto&& vec) {
+    constexpr int Y = decltype(y_c)::value;
+    const lchar* rq = lds_opaque(lds_ptr(smem) + so + rrow);
+    const lchar* ro = lds_opaque(lds_ptr(smem) + so + LDO + rrow);
+    u32x4 fq[kPD + 1], fo[kPD + 1];
 #pragma unroll
-      for (int mq = 0; mq < NQB; ++mq) {
-        s[mq] = mfma32<Tag>(ld_row(qr + TL::row_off(mq, 0)), kreg[0], zero);
-        dp[mq] = mfma32<Tag>(ld_row(orr + TL::row_off(mq, 0)), vreg[0], zero);
-      }
-#pragma unroll
-      for (int ks = 1; ks < KS; ++ks) {
-#pragma unroll
-        for (int mq = 0; mq < NQB; ++mq) {
-          s[mq] = mfma32<Tag>(ld_row(qr + TL::row_off(mq, ks)), kreg[ks], s[mq]);
-          dp[mq] = mfma32<Tag>(ld_row(orr + TL::row_off(mq, ks)), vreg[ks], dp[mq]);
-        }
-      }
-      const bool need_mask = CAUSAL && (q0 < kw0 + 31);
-#pragma unroll
-      for (int mq = 0; mq < NQB; ++mq) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + 32 * mq + 8 * r4);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + 32 * mq + 8 * r4);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int v = 4 * r4 + t;
-            float p = fast_exp2(fmaf(s[mq][v], cs, -l4[t]));
-            if (need_mask && (my_k > q0 + 32 * mq + 8 * r4 + 4 * g + t)) p = 0.0f;
-            s[mq][v] = p;
-            dp[mq][v] = p * (dp[mq][v] - d4[t]);
-          }
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < PK; ++kk) {
-        const int mq = kk >> 1, h = kk & 1;
-        const u32x4 pb = pack8<Tag>(s[mq], 8 * h);
-        const u32x4 db = pack8<Tag>(dp[mq], 8 * h);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          dvacc[nb] = mfma32<Tag>(ld_tr(ot + TL::tr_off(mq, h, 0, nb), ot + TL::tr_off(mq, h, 1, nb)), pb, dvacc[nb]);
-          dkacc[nb] = mfma32<Tag>(ld_tr(qt + TL::tr_off(mq, h, 0, nb), qt + TL::tr_off(mq, h, 1, nb)), db, dkacc[nb]);
-        }
-      }
+    for (int ks = 0; ks < kPD && ks < KS; ++ks) {
+      fq[ks] = ld_row(rq + TL::row_off(0, ks));
+      fo[ks] = ld_row(ro + TL::row_off(0, ks));
     }
-    if (in < n_tiles) stage_st(smem + (buf ^ 1) * BUF);
-    dma_wait();
-    __syncthreads();
-    buf ^= 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + kPD < KS) {
+        fq[(ks + kPD) % (kPD + 1)] = ld_row(rq + TL::row_off(0, ks + kPD));
+        fo[(ks + kPD) % (kPD + 1)] = ld_row(ro + TL::row_off(0, ks + kPD));
+      }
+      const int r = ks % (kPD + 1);
+      if (ks == 0) mfma32_vd<Tag, true, true>(s[Y], fq[r], kreg[0]);
+      else mfma32_vd<Tag, false, true>(s[Y], fq[r], kreg[ks]);
+      vec(2 * ks);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 0) mfma32_vd<Tag, true, true>(dp[Y], fo[r], vreg[0]);
+      else mfma32_vd<Tag, false, true>(dp[Y], fo[r], vreg[ks]);
+      vec(2 * ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // the first tile's products, then the pipelined sweep
+  vm_wait<2 * C>();
+  __syncthreads();
+  int i = i_first;
+  int so = 0;  // slot of tile i
+  prod(std::integral_constant<int, 0>{}, so, [](int) {});
+  vgpr_drain(s);
+  vgpr_drain(dp);
+
+  // Iteration over tile i (set X) with the next tile in (set Y = 1 - X):
+  //   part A: S, dP of in                   | P, dS of i, DMA
+  //   part B: dV^T, dK^T += ... of i        | DMA
+  auto step = [&](auto x_c, auto mask_c) {
+    constexpr int X = decltype(x_c)::value;
+    constexpr int Y = 1 - X;
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int in = next_tile(i);
+    const int son = slot_next(so);
+    vm_wait<C>();      // tile `in` has landed (for this wave's share) ...
+    __syncthreads();   // ... for every wave; the slot refilled below is free
+    const int q0 = i * BQ;
+    const lchar* base = lds_ptr(smem) + so;
+    // element v holds query q0 + 4g + 8(v/4) + v%4 (and this lane's key);
+    // it is allowed while that offset lies in [lo, hi)
+    const int lo = CAUSAL ? my_k - q0 - 4 * g : -BQ;
+    const int hi = n - q0 - 4 * g;
+    const lchar* ls = lds_opaque(base + LLD + 16 * g);
+    f32x4 lt4[4], d4[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      lt4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 32 * r4);
+      d4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 128 + 32 * r4);
+    }
+    // P and dS of element v in three stages, software-pipelined so that the
+    // work after each product is three independent operations (a single
+    // element's chain would stall on its own latencies while the matrix
+    // core idles): t = S c - Lt, P = exp2(t), dS = P (dP - D) (+ mask).
+    // The asm pins each finished element here, between the products.
+    auto st1 = [&](int v) { s[X][v] = fmaf(s[X][v], cs, -lt4[v >> 2][v & 3]); };
+    auto st2 = [&](int v) { s[X][v] = fast_exp2(s[X][v]); };
+    auto st3 = [&](int v) {
+      float pp = s[X][v];
+      float x = pp * (dp[X][v] - d4[v >> 2][v & 3]);
+      if constexpr (MASK) {
+        const int o = 8 * (v >> 2) + (v & 3);
+        const bool dead = o < lo || o >= hi;
+        pp = dead ? 0.0f : pp;
+        x = dead ? 0.0f : x;
+      }
+      s[X][v] = pp;
+      dp[X][v] = x;
+      asm volatile("" : "+v"(s[X][v]), "+v"(dp[X][v]));
+    };
+    auto staged = [&](int u) {  // after product u: element u enters, u-2 leaves
+      if (u < 16) st1(u);
+      if (u >= 1 && u - 1 < 16) st2(u - 1);
+      if (u >= 2 && u - 2 < 16) st3(u - 2);
+    };
+    constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
+    // ---- part A (16 elements over 2KS products: 1 or 2 per product)
+    prod(std::integral_constant<int, Y>{}, son, [&](int u) {
+      constexpr int R = 16 / (2 * KS);  // elements entering per product
+#pragma unroll
+      for (int e = 0; e < R; ++e) staged(u * R + e);
+#pragma unroll
+      for (int t = 0; t < kDmaA; ++t)
+        if (u == (2 * t + 1) * 2 * KS / (2 * kDmaA)) dma_tile(t);
+    });
+    staged(16);
+    staged(17);
+    u32x4 pb[PK], db[PK];
+#pragma unroll
+    for (int kk = 0; kk < PK; ++kk) {
+      pb[kk] = pack8<Tag>(s[X], 8 * kk);
+      db[kk] = pack8<Tag>(dp[X], 8 * kk);
+    }
+    // ---- part B: dV^T += dO^T P, dK^T += Q^T dS (transpose fragments of tile i)
+    const lchar* ot = lds_opaque(base + LDO + rtr);
+    const lchar* qt = lds_opaque(base + rtr);
+    auto trf = [&](const lchar* t, int f) {
+      return ld_tr(t + TL::tr_off(0, f / NB, 0, f % NB), t + TL::tr_off(0, f / NB, 1, f % NB));
+    };
+    u32x4 fo[kPD + 1], fq[kPD + 1];
+#pragma unroll
+    for (int f = 0; f < kPD && f < NF; ++f) {
+      fo[f] = trf(ot, f);
+      fq[f] = trf(qt, f);
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (f + kPD < NF) {
+        fo[(f + kPD) % (kPD + 1)] = trf(ot, f + kPD);
+        fq[(f + kPD) % (kPD + 1)] = trf(qt, f + kPD);
+      }
+      mfma32_acc<Tag>(dvacc[f % NB], fo[f % (kPD + 1)], pb[f / NB]);
+      mfma32_acc<Tag>(dkacc[f % NB], fq[f % (kPD + 1)], db[f / NB]);
+#pragma unroll
+      for (int t = kDmaA; t < C; ++t)
+        if (f == (2 * (t - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dma_advance();
     i = in;
+    so = son;
+  };
+
+  // Dense sweeps: the tiles crossing this wave's diagonal come first (an
+  // even number, masked), then an even number without any per-element test,
+  // then the rest (the sequence end), masked and padded to an even count
+  // with a tile past the end (every row dead).  The total is the same for
+  // every wave; two iterations per trip keep the sets X/Y in fixed roles
+  // and the accumulators out of any branch.
+  int n_pre = 0, n_plain = 0;
+  if constexpr (!SPARSE) {
+    const int T = n_tiles - i_first;
+    if constexpr (CAUSAL) n_pre = min((w + 2) & ~1, (T + 1) & ~1);
+    n_plain = max(n / BQ - (i_first + n_pre), 0) & ~1;
+  }
+  for (int t = 0; t < n_pre; t += 2) {
+    step(std::integral_constant<int, 0>{}, std::true_type{});
+    step(std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  for (int t = 0; t < n_plain; t += 2) {
+    step(std::integral_constant<int, 0>{}, std::false_type{});
+    step(std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  while (i < n_tiles) {
+    step(std::integral_constant<int, 0>{}, std::true_type{});
+    step(std::integral_constant<int, 1>{}, std::true_type{});
   }
 
+  agpr_drain(dkacc);
+  agpr_drain(dvacc);
   if (my_k < n) {
     uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
     uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
@@ -508,12 +657,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int q = 0; q < kDmaA; ++q)
         if (half * 2 * KS + u == (2 * q + 1) * 2 * KS / kDmaA) dma_tile(q);
     };
+    // elements in pairs after every other product (two independent chains
+    // hide each other's latency under one product)
+    constexpr int E = 16 / KS;  // elements per pair of products
     prod(std::integral_constant<int, Y>{}, std::false_type{}, son, live_n, [&](int u) {
-      valu(0, u * 16 / (2 * KS), (u + 1) * 16 / (2 * KS));
+      if (u & 1) valu(0, (u >> 1) * E, (u >> 1) * E + E);
       dma_a(u, 0);
     });
     prod(std::integral_constant<int, Y>{}, std::true_type{}, son, live_n, [&](int u) {
-      valu(1, u * 16 / (2 * KS), (u + 1) * 16 / (2 * KS));
+      if (u & 1) valu(1, (u >> 1) * E, (u >> 1) * E + E);
       dma_a(u, 1);
     });
     // ---- part B
@@ -590,7 +742,7 @@ hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
   timing_begin(kBwdPre, st);
   hipLaunchKernelGGL((bwd_pre_kernel<Tag, D>), dim3((rows + rows_per_blk - 1) / rows_per_blk), dim3(kNT),
                      0, st, reinterpret_cast<const uint16_t*>(a.o),
-                     reinterpret_cast<const uint16_t*>(a.dout), a.dvec, rows);
+                     reinterpret_cast<const uint16_t*>(a.dout), a.lse, a.dvec, a.lt, rows);
   hipError_t e = hipGetLastError();
   timing_end(kBwdPre, st);
   if (e != hipSuccess) return e;

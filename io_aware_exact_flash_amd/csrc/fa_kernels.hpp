@@ -33,6 +33,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;      // [B*H*N]
   float* dvec;           // [B*H*N] rowsum(dO o O), written by the pre-pass
+  float* lt;             // [B*H*N] LSE * log2(e), +inf where LSE = -inf (pre-pass)
   void* dq;
   void* dk;
   void* dv;

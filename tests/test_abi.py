@@ -110,10 +110,11 @@ def test_backward_validation(kw, code):
 def test_backward_workspace_too_small():
     lib = flash.lib()
     need = lib.flash_attn_bwd_workspace_size(1, 2, 256, 128, flash.FA_F16)
-    assert need == 2 * 256 * 4  # one float32 per query row, rounded to 256 bytes
+    # two float32 arrays of B*H*N rows, each rounded to 256 bytes plus 256 spare
+    assert need == 2 * (2 * 256 * 4 + 256)
     assert _bwd(ws_bytes=need - 1) == flash.FA_ERR_WORKSPACE_TOO_SMALL
     assert lib.flash_attn_bwd_workspace_size(0, 2, 256, 128, flash.FA_F16) == 0
-    assert lib.flash_attn_bwd_workspace_size(1, 1, 1000, 64, flash.FA_BF16) == 4096
+    assert lib.flash_attn_bwd_workspace_size(1, 1, 1000, 64, flash.FA_BF16) == 2 * (4096 + 256)
 
 
 def test_blocksparse_validation():
