@@ -259,23 +259,27 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // it is allowed while that offset lies in [lo, hi)
     const int lo = CAUSAL ? my_k - q0 - 4 * g : -BQ;
     const int hi = n - q0 - 4 * g;
+    // element v needs the base-2 LSE and D of query 8(v/4) + 4g + v%4: the
+    // LSE by four LDS reads; D by one read of group c32 % 4, the other groups
+    // coming from the lanes of the quad by DPP broadcast folded into the
+    // subtraction that uses them
     const lchar* ls = lds_opaque(base + LLD + 16 * g);
-    f32x4 lt4[4], d4[4];
+    f32x4 lt4[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      lt4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 32 * r4);
-      d4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 128 + 32 * r4);
-    }
+    for (int r4 = 0; r4 < 4; ++r4) lt4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 32 * r4);
+    const f32x4 dq4 = *(const __attribute__((address_space(3))) f32x4*)(ls + 128 + 32 * (c32 & 3));
+    auto ltv = [&](int v) { return lt4[v >> 2][v & 3]; };
+    auto dv = [&](int v) { return quad_bcast(dq4[v & 3], v >> 2); };
     // P and dS of element v in three stages, software-pipelined so that the
     // work after each product is three independent operations (a single
     // element's chain would stall on its own latencies while the matrix
     // core idles): t = S c - Lt, P = exp2(t), dS = P (dP - D) (+ mask).
     // The asm pins each finished element here, between the products.
-    auto st1 = [&](int v) { s[X][v] = fmaf(s[X][v], cs, -lt4[v >> 2][v & 3]); };
+    auto st1 = [&](int v) { s[X][v] = fmaf(s[X][v], cs, -ltv(v)); };
     auto st2 = [&](int v) { s[X][v] = fast_exp2(s[X][v]); };
     auto st3 = [&](int v) {
       float pp = s[X][v];
-      float x = pp * (dp[X][v] - d4[v >> 2][v & 3]);
+      float x = pp * (dp[X][v] - dv(v));
       if constexpr (MASK) {
         const int o = 8 * (v >> 2) + (v & 3);
         const bool dead = o < lo || o >= hi;
@@ -309,6 +313,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       pb[kk] = pack8<Tag>(s[X], 8 * kk);
       db[kk] = pack8<Tag>(dp[X], 8 * kk);
     }
+    valu_to_mfma(pb);
+    valu_to_mfma(db);
     // ---- part B: dV^T += dO^T P, dK^T += Q^T dS (transpose fragments of tile i)
     const lchar* ot = lds_opaque(base + LDO + rtr);
     const lchar* qt = lds_opaque(base + rtr);
@@ -668,6 +674,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       if (u & 1) valu(1, (u >> 1) * E, (u >> 1) * E + E);
       dma_a(u, 1);
     });
+    valu_to_mfma(db[0]);
+    valu_to_mfma(db[1]);
     // ---- part B
     const lchar* kt = lds_opaque(lds_ptr(smem) + so + ktr);
     u32x4 kq[kPD + 1];

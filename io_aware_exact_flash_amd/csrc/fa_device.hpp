@@ -51,28 +51,32 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // D += A B with D pinned to accumulation registers (AGPRs) for its whole
 // lifetime.  Left to itself the compiler copies long-lived accumulators
 // between register files every iteration once a kernel needs more than 256
-// registers.  Hazards the compiler cannot see through the asm: a VALU write
-// of A or B needs two wait states before the product reads it (the s_nop);
-// dependent accumulation into the same registers is interlocked; and VALU
-// reads of D after the last product wait in agpr_drain().
+// registers.  Hazards the compiler cannot see through the asm are the
+// caller's: a VALU write of A or B needs two wait states before a product
+// reads it (valu_to_mfma()); dependent accumulation into the same registers
+// is interlocked; VALU reads of D after the last product wait in
+// agpr_drain() / vgpr_drain().  Operands loaded from memory are covered by
+// the compiler's own s_waitcnt.
 template <typename Tag>
 __device__ __forceinline__ void mfma32_acc(f32x16& d, u32x4 a, u32x4 b) {
 #if defined(__HIP_DEVICE_COMPILE__)
   if constexpr (std::is_same<Tag, bf16_tag>::value)
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
   else
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 #endif
 }
 
 // D = A B (FIRST) or D += A B with D in VGPRs, for results the VALU reads
 // next (vgpr_drain() covers the read latency); B_AGPR: B is held in AGPRs.
+// These keep two wait states in front of the product: around branches the
+// compiler may copy A or D with VALU moves right before it.
 #define FA_MFMA_VD(OP, FIRST, BC)                                                         \
   do {                                                                                   \
     if (FIRST)                                                                           \
-      asm volatile("s_nop 2\n\t" OP " %0, %1, %2, 0" : "=&v"(d) : "v"(a), BC(b));        \
+      asm volatile("s_nop 1\n\t" OP " %0, %1, %2, 0" : "=&v"(d) : "v"(a), BC(b));        \
     else                                                                                 \
-      asm volatile("s_nop 2\n\t" OP " %0, %1, %2, %0" : "+v"(d) : "v"(a), BC(b));        \
+      asm volatile("s_nop 1\n\t" OP " %0, %1, %2, %0" : "+v"(d) : "v"(a), BC(b));        \
   } while (0)
 #define FA_CONSTRAINT_A(x) "a"(x)
 #define FA_CONSTRAINT_V(x) "v"(x)
@@ -91,6 +95,17 @@ __device__ __forceinline__ void mfma32_vd(f32x16& d, u32x4 a, u32x4 b) {
 #undef FA_MFMA_VD
 #undef FA_CONSTRAINT_A
 #undef FA_CONSTRAINT_V
+
+// Two wait states between VALU writes of the given operand registers and
+// the asm products that read them (the asm ties the order to the values).
+template <int N>
+__device__ __forceinline__ void valu_to_mfma(u32x4 (&r)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 1" : "+v"(r[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("" : "+v"(r[i]));
+#endif
+}
 
 template <int N>
 __device__ __forceinline__ void vgpr_drain(f32x16 (&d)[N]) {
@@ -212,6 +227,20 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 __device__ __forceinline__ u32x4 ld_row(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Value of lane 4*(lane/4) + i in every lane of the quad (DPP quad_perm
+// broadcast; i is a compile-time constant after unrolling).
+__device__ __forceinline__ float quad_bcast(float x, int i) {
+  const int bits = __builtin_bit_cast(int, x);
+  int r;
+  switch (i) {
+    case 0: r = __builtin_amdgcn_mov_dpp(bits, 0x00, 0xf, 0xf, true); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(bits, 0x55, 0xf, 0xf, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(bits, 0xaa, 0xf, 0xf, true); break;
+    default: r = __builtin_amdgcn_mov_dpp(bits, 0xff, 0xf, 0xf, true); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // 32-bit LDS pointers.  lds_opaque() hides a per-iteration base from the
 // optimiser so constant offsets stay in the instructions' offset fields
 // instead of being hoisted into one register per offset.
@@ -308,6 +337,13 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 #endif
 }
 __device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(uintptr_t)(lchar*)p; }
+// Same, from a wave-uniform base plus a per-lane 32-bit byte offset (no
+// 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+#endif
+}
 
 template <int ROWS, int D, bool TR, int NW>
 struct Dma {
@@ -316,7 +352,9 @@ struct Dma {
   static constexpr int kBlocks = (kBytes + 1023) / 1024;
   static constexpr int kPer = (kBlocks + NW - 1) / NW;   // DMA instructions per wave per tile
   static constexpr int kSlot = kPer * NW * 1024;         // LDS bytes reserved per tile
-  int src[kPer];  // element offset inside the tile (0 for padding / past the tile)
+  int src[kPer];   // element offset inside the tile (0 for padding / past the tile)
+  int row[kPer];   // its row and its column in bytes
+  int colb[kPer];
   int wave;
 
   __device__ void init(int w, int lane) {
@@ -330,6 +368,8 @@ struct Dma {
         const int p = off - r * L::S - L::rot(r);
         if (p >= 0 && p < 2 * D) src[k] = r * D + p / 2;
       }
+      row[k] = src[k] / D;
+      colb[k] = 2 * (src[k] % D);
     }
   }
   // Every wave issues exactly kPer instructions per tile, with every lane
@@ -355,9 +395,9 @@ struct Dma {
   // between its own products instead of queueing it all at once.
   __device__ __forceinline__ void issue_one(int k, const uint16_t* __restrict__ t0, int valid, char* l0) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    // rows past the end re-read the last row (branch-free)
-    const int e = src[k] - max(src[k] / D - (valid - 1), 0) * D;
-    dma16(t0 + e, lds_addr(l0 + (wave + NW * k) * 1024));
+    // rows past the end re-read the last row (branch-free: two VALU ops)
+    const uint32_t off = (uint32_t)min(row[k], valid - 1) * (2 * D) + colb[k];
+    dma16_s(t0, off, lds_addr(l0 + (wave + NW * k) * 1024));
 #endif
   }
   // Moves two tiles of the same geometry with one set of offsets.
