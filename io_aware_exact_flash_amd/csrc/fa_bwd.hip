@@ -466,6 +466,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     Dq[h] = a.dvec[(size_t)bh * n + qr];
   }
 
+  f32x16 negD[2];  // -D of each block's query, the dP^T accumulators' starting value
+#pragma unroll
+  for (int h = 0; h < 2; ++h) negD[h] = -Dq[h];
   const int n_tiles = (n + BC - 1) / BC;
   int j_end = n_tiles;
   if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + BR, n) - 1) / BC + 1);
@@ -573,8 +576,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
         for (int h = 0; h < 2; ++h) {
           f32x16& d = P ? dp[Y][h] : s[Y][h];
           const u32x4 b = P ? oreg[h][ks] : qreg[h][ks];
-          if (ks == 0) mfma32_vd<Tag, true, true>(d, f, b);
-          else mfma32_vd<Tag, false, true>(d, f, b);
+          if (ks == 0) {
+            if (P) mfma32_vc<Tag>(d, f, b, negD[h]);  // dP^T - D accumulates from -D
+            else mfma32_vd<Tag, true, true>(d, f, b);
+          } else {
+            mfma32_vd<Tag, false, true>(d, f, b);
+          }
           // each product is followed by its share of vector work, so the
           // next product issues as the matrix core frees up
           vec(2 * ks + h);
@@ -640,7 +647,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int v = v0; v < v1; ++v) {
           const float p = fast_exp2(fmaf(s[X][h][v], cs, -Lq[h]));
-          float x = p * (dp[X][h][v] - Dq[h]);
+          float x = p * dp[X][h][v];
           if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
           dp[X][h][v] = x;
         }

@@ -92,6 +92,16 @@ __device__ __forceinline__ void mfma32_vd(f32x16& d, u32x4 a, u32x4 b) {
   }
 #endif
 }
+// D = A B + C with C a VGPR tuple (an accumulator starting value), B in AGPRs.
+template <typename Tag>
+__device__ __forceinline__ void mfma32_vc(f32x16& d, u32x4 a, u32x4 b, const f32x16& c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (std::is_same<Tag, bf16_tag>::value)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+#endif
+}
 #undef FA_MFMA_VD
 #undef FA_CONSTRAINT_A
 #undef FA_CONSTRAINT_V
