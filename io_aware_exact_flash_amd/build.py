@@ -36,12 +36,36 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm 7.x required to build libflashattn.so)")
 
 
+def _spills(remarks: str):
+    """Kernels the compiler reports with register spills (resource-usage remarks)."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        txt = line.split("remark:", 1)[1].strip()
+        if txt.startswith("Function Name:"):
+            name = txt.split(":", 1)[1].strip()
+        elif txt.startswith(("VGPRs Spill:", "SGPRs Spill:")):
+            n = int(txt.split(":", 1)[1].split()[0])
+            if n and name:
+                bad.append(f"{name} ({txt.split(' [')[0]})")
+    return bad
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *extra, "-Rpass-analysis=kernel-resource-usage",
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # The backward kernels issue matrix products and DMA through inline asm
+    # whose hazards the compiler does not see; spill code (register copies
+    # and scratch memory traffic inside the loops) would break the
+    # assumptions those asm statements rely on.  Refuse such a build.
+    bad = _spills(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: register spills in " + ", ".join(bad))
     return obj
 
 

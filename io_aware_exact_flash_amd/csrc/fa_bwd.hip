@@ -642,27 +642,32 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     // ---- part A
     u32x4 db[2][PK];
     // dS^T of block h, elements v0..v1-1, then packed once the block is done
-    auto valu = [&](int h, int v0, int v1) {
-      if (live_j) {
+    // dS^T of element e (block e/16, row e%16) in three stages, software-
+    // pipelined so the vector work after each product is independent
+    // operations (one element's chain alone would stall on its latencies
+    // while the matrix core idles): t = S^T c - L, P = exp2(t),
+    // dS = P (dP^T - D) (+ mask).  The asm pins each finished element here,
+    // between the products; a block's dS^T is packed once complete.
+    auto st1 = [&](int e) { s[X][e >> 4][e & 15] = fmaf(s[X][e >> 4][e & 15], cs, -Lq[e >> 4]); };
+    auto st2 = [&](int e) { s[X][e >> 4][e & 15] = fast_exp2(s[X][e >> 4][e & 15]); };
+    auto st3 = [&](int e) {
+      const int h = e >> 4, v = e & 15;
+      float x = s[X][h][v] * dp[X][h][v];
+      if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
+      dp[X][h][v] = x;
+      asm volatile("" : "+v"(dp[X][h][v]));
+      if (v == 15) {
 #pragma unroll
-        for (int v = v0; v < v1; ++v) {
-          const float p = fast_exp2(fmaf(s[X][h][v], cs, -Lq[h]));
-          float x = p * dp[X][h][v];
-          if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
-          dp[X][h][v] = x;
-        }
-        // keep the chunk's work here, between the products (the optimiser
-        // would otherwise sink the masking into the packing below)
-#pragma unroll
-        for (int v = v0; v < v1; ++v) asm volatile("" : "+v"(dp[X][h][v]));
-        if (v1 == 16) {
-#pragma unroll
-          for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[X][h], 8 * kk);
-        }
-      } else if (v1 == 16) {
-#pragma unroll
-        for (int kk = 0; kk < PK; ++kk) db[h][kk] = u32x4{0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[X][h], 8 * kk);
       }
+    };
+    // (runs whether or not the tile is live: a skipped tile's registers hold
+    // stale finite values and its dS^T is replaced by zeros below, which
+    // keeps branches out of the product sequence)
+    auto staged = [&](int t) {  // element t enters, t-2 leaves
+      if (t < 32) st1(t);
+      if (t >= 1 && t - 1 < 32) st2(t - 1);
+      if (t >= 2 && t - 2 < 32) st3(t - 2);
     };
     // slot u = 0 .. 2KS-1 of a sweep: the product of k-step u/2, block u%2
     auto dma_a = [&](int u, int half) {
@@ -670,17 +675,25 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int q = 0; q < kDmaA; ++q)
         if (half * 2 * KS + u == (2 * q + 1) * 2 * KS / kDmaA) dma_tile(q);
     };
-    // elements in pairs after every other product (two independent chains
-    // hide each other's latency under one product)
-    constexpr int E = 16 / KS;  // elements per pair of products
+    constexpr int R = 32 / (4 * KS);  // elements entering per product
     prod(std::integral_constant<int, Y>{}, std::false_type{}, son, live_n, [&](int u) {
-      if (u & 1) valu(0, (u >> 1) * E, (u >> 1) * E + E);
+#pragma unroll
+      for (int r = 0; r < R; ++r) staged(u * R + r);
       dma_a(u, 0);
     });
     prod(std::integral_constant<int, Y>{}, std::true_type{}, son, live_n, [&](int u) {
-      if (u & 1) valu(1, (u >> 1) * E, (u >> 1) * E + E);
+#pragma unroll
+      for (int r = 0; r < R; ++r) staged((2 * KS + u) * R + r);
       dma_a(u, 1);
     });
+    staged(32);
+    staged(33);
+    if (!live_j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kk = 0; kk < PK; ++kk) db[h][kk] = u32x4{0u, 0u, 0u, 0u};
+    }
     valu_to_mfma(db[0]);
     valu_to_mfma(db[1]);
     // ---- part B
