@@ -71,24 +71,32 @@ __device__ __forceinline__ void mfma32_acc(f32x16& d, u32x4 a, u32x4 b) {
 // next (vgpr_drain() covers the read latency); B_AGPR: B is held in AGPRs.
 // These keep two wait states in front of the product: around branches the
 // compiler may copy A or D with VALU moves right before it.
-#define FA_MFMA_VD(OP, FIRST, BC)                                                         \
+#define FA_MFMA_VD(PRE, OP, FIRST, BC)                                                    \
   do {                                                                                   \
     if (FIRST)                                                                           \
-      asm volatile("s_nop 1\n\t" OP " %0, %1, %2, 0" : "=&v"(d) : "v"(a), BC(b));        \
+      asm volatile(PRE OP " %0, %1, %2, 0" : "=&v"(d) : "v"(a), BC(b));                   \
     else                                                                                 \
-      asm volatile("s_nop 1\n\t" OP " %0, %1, %2, %0" : "+v"(d) : "v"(a), BC(b));        \
+      asm volatile(PRE OP " %0, %1, %2, %0" : "+v"(d) : "v"(a), BC(b));                   \
   } while (0)
 #define FA_CONSTRAINT_A(x) "a"(x)
 #define FA_CONSTRAINT_V(x) "v"(x)
-template <typename Tag, bool FIRST, bool B_AGPR>
+// NOP = false drops the two wait states, for call sites where no VALU
+// instruction writes A, B or D (operands loaded from LDS or memory, D
+// written by the products only).
+template <typename Tag, bool FIRST, bool B_AGPR, bool NOP = true>
 __device__ __forceinline__ void mfma32_vd(f32x16& d, u32x4 a, u32x4 b) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  if constexpr (std::is_same<Tag, bf16_tag>::value) {
-    if constexpr (B_AGPR) FA_MFMA_VD("v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_A);
-    else FA_MFMA_VD("v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_V);
+  constexpr bool BF = std::is_same<Tag, bf16_tag>::value;
+  if constexpr (NOP) {
+    if constexpr (BF && B_AGPR) FA_MFMA_VD("s_nop 1\n\t", "v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_A);
+    else if constexpr (BF) FA_MFMA_VD("s_nop 1\n\t", "v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_V);
+    else if constexpr (B_AGPR) FA_MFMA_VD("s_nop 1\n\t", "v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_A);
+    else FA_MFMA_VD("s_nop 1\n\t", "v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_V);
   } else {
-    if constexpr (B_AGPR) FA_MFMA_VD("v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_A);
-    else FA_MFMA_VD("v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_V);
+    if constexpr (BF && B_AGPR) FA_MFMA_VD("", "v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_A);
+    else if constexpr (BF) FA_MFMA_VD("", "v_mfma_f32_32x32x16_bf16", FIRST, FA_CONSTRAINT_V);
+    else if constexpr (B_AGPR) FA_MFMA_VD("", "v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_A);
+    else FA_MFMA_VD("", "v_mfma_f32_32x32x16_f16", FIRST, FA_CONSTRAINT_V);
   }
 #endif
 }
@@ -192,6 +200,19 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max(a, b, c) as one instruction.  fmaxf() on values the compiler cannot
+// prove canonical (results of asm products) costs an extra NaN-quieting
+// max per operand; these kernels never hold signalling NaNs.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(a, fmaxf(b, c));
+#endif
+}
 
 // ---------------------------------------------------------------------------
 // LDS tiles.  A tile holds ROWS tokens x D columns of 16-bit elements, row
@@ -410,6 +431,15 @@ struct Dma {
     dma16_s(t0, off, lds_addr(l0 + (wave + NW * k) * 1024));
 #endif
   }
+  // Same, with the tile's addressing hoisted by the caller (once per tile):
+  // t0 its first row, last its last valid row (rows past it re-read it),
+  // lds_w the LDS byte address of the tile plus 1024 * wave.
+  __device__ __forceinline__ void issue_at(int k, const uint16_t* __restrict__ t0, int last, uint32_t lds_w) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t off = (uint32_t)min(row[k], last) * (2 * D) + colb[k];
+    dma16_s(t0, off, lds_w + NW * k * 1024);
+#endif
+  }
   // Moves two tiles of the same geometry with one set of offsets.
   __device__ __forceinline__ void issue2(const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
                                          int valid, char* l0, char* l1) const {
@@ -428,6 +458,17 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
 __device__ __forceinline__ void dma_wait() { vm_wait<0>(); }
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// makes every wave first wait for its own outstanding LDS reads, which
+// serialises the operand prefetch issued right before the barrier.  DMA
+// completion is ordered by the vm_wait<>() in front of it; the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
 
 // Make the register operands loaded before a loop complete there: the
 // waitcnt pass otherwise keeps them "possibly pending" on some path into the

@@ -2,21 +2,31 @@
 //
 // Computes, per head, O = softmax(scale * Q K^T) V and the row log-sum-exp
 // L = m + ln(l) in one pass over K and V (FlashAttention-2 notes,
-// Algorithm 1 and eqs. (10)-(15)): each workgroup owns 128 query rows, keeps
+// Algorithm 1 and eqs. (10)-(15)): each workgroup owns 256 query rows, keeps
 // Q in registers, streams K/V tiles through LDS, and never writes the score
 // or probability matrix anywhere.
 //
 // Work split (chosen for CDNA4, not taken from the pages' A100 design):
-//  * 4 waves x 32 query rows.  Each wave computes S^T = K_j Q_w^T with
-//    v_mfma_f32_32x32x16, so every query row is one lane column and the
-//    running statistics (m, l), the exp(m_old - m_new) rescale of the
-//    accumulator, and the final division are lane-local.
+//  * 4 waves x 64 query rows, one wave per SIMD.  A wave holds two 32-query
+//    blocks h = 0, 1 and computes S^T = K_j Q_h^T with v_mfma_f32_32x32x16,
+//    so every query row is one lane column and the running statistics
+//    (m, l), the exp(m_old - m_new) rescale of the accumulator, and the
+//    final division are lane-local.  Every K or V fragment read from LDS
+//    feeds the products of both blocks, half the LDS traffic per product of
+//    a 32-query wave.
 //  * The accumulator is O^T = V_j^T P^T: P^T comes straight out of the S^T
 //    accumulator as the B operand; V_j^T is fetched from the row-major V
-//    tile with LDS transpose reads (ds_read_b64_tr_b16).
-//  * 64-key tiles, double-buffered in LDS with a register prefetch: one
-//    barrier per tile; padded rows make every operand fetch a per-lane base
-//    plus an immediate offset.
+//    tile with LDS transpose reads (ds_read_b64_tr_b16).  Q^T and O^T live
+//    in the accumulation registers (AGPRs) for the whole sweep.
+//  * 32-key tiles stream through a ring of four LDS slots by global->LDS
+//    DMA two tiles ahead; one barrier per tile.
+//  * A lone wave per SIMD overlaps its matrix products with its own vector
+//    work only when the two are interleaved, and a tile's steps depend on
+//    each other (S -> max -> P -> PV), so the sweep is software-pipelined by
+//    one tile: the S^T products of the next tile run interleaved with the
+//    exponentials of the current one, and the PV products of the current
+//    tile with the row sums of the current and the masks and row maxima of
+//    the next.
 //  * Causal: tiles above the diagonal are never loaded; only tiles crossing
 //    it are masked element-wise (FlashAttention-2 notes, "Causal mask
 //    optimisation").  Block-sparse: tiles whose 128 x 128 mask entry is zero
@@ -27,182 +37,404 @@
 //    contribution is scaled by the same stale m, and L = m + ln l holds for
 //    any m), and the accumulator rescale is skipped whole-wave when no row
 //    needs it.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kNT = 256;     // threads per workgroup
-constexpr int kQW = 32;      // query rows per wave
-constexpr int kBR = 128;     // query rows per workgroup
+constexpr int kNT = 256;       // threads per workgroup
+constexpr int kWQ = 64;        // query rows per wave
+constexpr int kBR = 4 * kWQ;   // query rows per workgroup
 constexpr float kLazy = 8.0f;
 
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int BC = 64;              // keys per tile
-  constexpr int NKB = BC / 32;        // 32-key blocks per tile
-  constexpr int KS = D / 16;          // k-steps over the head dimension
-  constexpr int MB = D / 32;          // 32-wide output column blocks
-  constexpr int PK = BC / 16;         // k-steps of the PV product
+__global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
+  constexpr int BC = 32;              // keys per tile
+  constexpr int KS = D / 16;          // k-steps of the S^T products
+  constexpr int MB = D / 32;          // 32-row blocks of O^T
+  constexpr int PK = BC / 16;         // k-steps of the PV products
+  constexpr int NF = PK * MB;         // V^T fragments per tile
+  constexpr int kRing = 6;            // LDS tile slots
   using KL = Pad<D, false>;           // K: row reads
   using VL = Pad<D, true>;            // V: transpose reads
-  constexpr int KT = KL::bytes(BC), VT = VL::bytes(BC), BUF = KT + VT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  using KD = Dma<BC, D, false, kNT / 64>;
+  using VD = Dma<BC, D, true, kNT / 64>;
+  constexpr int SLOT = KD::kSlot + VD::kSlot;
+  constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
+  static_assert(4 * C < 64, "vmcnt range");
+  static_assert(C <= NF, "DMA issue slots");
+  static_assert(2 * KS == 2 * NF, "both phases hold the same number of products");
+  __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
   const int n = a.n;
-
   const int lb = xcd_remap(blockIdx.x, a.nblk);
   const int bh = lb / a.nqb;
   const int qb = a.nqb - 1 - (lb % a.nqb);  // longest causal rows first
   const size_t hoff = (size_t)bh * n * D;
-  const uint16_t* __restrict__ Q = reinterpret_cast<const uint16_t*>(a.q) + hoff;
-  const uint16_t* __restrict__ K = reinterpret_cast<const uint16_t*>(a.k) + hoff;
-  const uint16_t* __restrict__ V = reinterpret_cast<const uint16_t*>(a.v) + hoff;
+  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
 
   const int q0 = qb * kBR;
-  const int qw0 = q0 + w * kQW;
-  const int my_q = qw0 + c32;
+  const int qw0 = q0 + w * kWQ;       // the wave's first query; block h starts at qw0 + 32h
 
-  u32x4 qreg[KS];
-  {
-    const uint16_t* qp = Q + (size_t)min(my_q, n - 1) * D + 8 * g;
+  u32x4 qreg[2][KS];                  // Q^T fragments, in AGPRs
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+  for (int h = 0; h < 2; ++h) {
+    const size_t r = (size_t)min(qw0 + 32 * h + c32, n - 1) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
   }
 
   const int n_tiles = (n + BC - 1) / BC;
   int j_end = n_tiles;
   if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + kBR, n) - 1) / BC + 1);
-  const uint8_t* mrow = SPARSE ? a.mask + (size_t)(q0 / kMaskBlock) * a.mask_t : nullptr;
+  // block-sparse: the workgroup spans two 128-query mask rows, each wave one
+  const uint8_t* mrow0 = nullptr;
+  const uint8_t* mrow1 = nullptr;
+  const uint8_t* mwave = nullptr;
+  if constexpr (SPARSE) {
+    const int t0 = q0 / kMaskBlock;
+    const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
+    mrow0 = a.mask + (size_t)t0 * a.mask_t;
+    mrow1 = a.mask + (size_t)t1 * a.mask_t;
+    mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+  }
   auto next_tile = [&](int j) {
     ++j;
     if constexpr (SPARSE)
-      while (j < j_end && !mrow[(j * BC) / kMaskBlock]) ++j;
+      while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
     return j;
   };
+  // tiles of this wave's queries that have allowed keys
+  auto live = [&](int jt) {
+    bool l = jt < j_end;
+    if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + kWQ - 1);
+    if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
+    return l;
+  };
+  // Element v of block h of tile jt holds key jt*BC + 4g + 8(v/4) + v%4; it
+  // is allowed while 8(v/4) + v%4 is at most lim[h].
+  auto limits = [&](int jt, int (&lim)[2]) {
+    const bool lv = SPARSE ? live(jt) : true;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int last = n - 1;
+      if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+      lim[h] = lv ? last - jt * BC - 4 * g : -1;
+    }
+  };
 
-  Stage<BC, D, kNT, false> sk;
-  Stage<BC, D, kNT, true> sv;
-  sk.init(tid);
-  sv.init(tid);
-  const int kread = KL::row_base(c32, g);
-  const int vread = KT + VL::tr_base(lane);
+  KD kd;
+  VD vd;
+  kd.init(w, lane);
+  vd.init(w, lane);
+  const int krow = KL::row_base(c32, g);
+  const int vtr = KD::kSlot + VL::tr_base(lane);
+  auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
 
-  int j = SPARSE ? next_tile(-1) : 0;
-  if (j < j_end) {
-    sk.load(K + (size_t)j * BC * D, n - j * BC);
-    sv.load(V + (size_t)j * BC * D, n - j * BC);
-    sk.store(smem);
-    sv.store(smem + KT);
+  vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
+
+  const int j_first = SPARSE ? next_tile(-1) : 0;
+  if (j_first >= j_end) {  // no key tile at all: O = 0, L = -inf
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int my_q = qw0 + 32 * h + c32;
+      if (my_q < n) {
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
+        for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(op + c) = u32x4{0u, 0u, 0u, 0u};
+        if (g == 0) a.lse[(size_t)bh * n + my_q] = -INFINITY;
+      }
+    }
+    return;
   }
-  settle(qreg);
-  __syncthreads();
+  // Every iteration issues exactly C DMA instructions (past the last tile
+  // they reload the first tile into a slot nobody reads), so the tile after
+  // the next one has landed once vmcnt <= C at the barrier.
+  int jq = j_first;  // next tile to load
+  int sq = 0;        // its slot
+  // its addressing, set once per tile: K and V rows, last valid row, LDS
+  // address of this wave's share
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+  const uint16_t* dk = Kg;
+  const uint16_t* dv = Vg;
+  int d_last = 0;
+  uint32_t d_lds = 0;
+  auto dma_set = [&]() {
+    const int jt = jq < j_end ? jq : j_first;
+    dk = Kg + (size_t)jt * BC * D;
+    dv = Vg + (size_t)jt * BC * D;
+    d_last = n - 1 - jt * BC;
+    d_lds = lds_base + sq + 1024 * w;
+  };
+  // DMA instruction i (of C) of the tile
+  auto dma_tile = [&](int i) {
+    if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
+    else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
+  };
+  auto dma_advance = [&]() {
+    if (jq < j_end) jq = next_tile(jq);
+    sq = slot_next(sq);
+    dma_set();
+  };
+  dma_set();
+  // A tile's DMA is split: instructions 0..kDB-1 are issued in the B
+  // phase of one iteration, the rest in the A phase of the next (spreading
+  // the address work of the four waves over the whole iteration)
+  constexpr int kDB = C / 2;
+  for (int t = 0; t < 3; ++t) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) dma_tile(i);
+    dma_advance();
+  }
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) dma_tile(i);
 
-  f32x16 oacc[MB];
+  f32x16 acc[2][MB];  // O^T of both blocks, in AGPRs
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) oacc[mb] = 0.0f;
-  float m_run = -INFINITY, l_part = 0.0f;
-  const float cs = a.c;
-  int buf = 0;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
+  const float cs = a.c;  // scale * log2(e): scores in exp2 units
+  const float inv_cs = 1.0f / cs;
+  // S^T of both blocks for two tiles, register sets 0 and 1 by tile parity
+  f32x16 s[2][2];
+  // packed P^T (B operands of the PV products) for two tiles
+  u32x4 pb[2][2][PK];
+  constexpr int kPD = 6;  // LDS fragments run kPD products ahead
+  u32x4 fr[kPD + 1];      // K row fragments (ring)
+  u32x4 kq[kPD + 1];      // V^T fragments (ring)
+  auto rd_k = [&](const lchar* rows, int ks) { return ld_row(rows + KL::row_off(0, ks)); };
+  auto rd_v = [&](const lchar* vt, int f) {
+    return ld_tr(vt + VL::tr_off(0, f / MB, 0, f % MB), vt + VL::tr_off(0, f / MB, 1, f % MB));
+  };
+  auto k_rows = [&](int so) { return lds_opaque(lds_ptr(smem) + so + krow); };
+  auto v_cols = [&](int so) { return lds_opaque(lds_ptr(smem) + so + vtr); };
+  auto prefetch_k = [&](int so) {
+    const lchar* rows = k_rows(so);
+#pragma unroll
+    for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd_k(rows, ks);
+  };
 
-  while (j < j_end) {
-    const int jn = next_tile(j);
-    if (jn < j_end) {
-      sk.load(K + (size_t)jn * BC * D, n - jn * BC);
-      sv.load(V + (size_t)jn * BC * D, n - jn * BC);
+
+  // S^T = K Q^T of both blocks for the tile in slot `so` into set Y (its
+  // first kPD K fragments already in flight), with vec(u) = vector work
+  // after product u = 2 ks + h.
+  // (No VALU instruction writes their operands: K fragments come from LDS,
+  // Q^T from memory, and the accumulators only from the products.)
+  auto prod_s = [&](auto y_c, int so, auto&& vec) {
+    constexpr int Y = decltype(y_c)::value;
+    const lchar* rows = k_rows(so);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd_k(rows, ks + kPD);
+      const u32x4 f = fr[ks % (kPD + 1)];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (ks == 0) mfma32_vd<Tag, true, true, false>(s[Y][h], f, qreg[h][ks]);
+        else mfma32_vd<Tag, false, true, false>(s[Y][h], f, qreg[h][ks]);
+        vec(2 * ks + h);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    const char* kb_ = smem + buf * BUF + kread;
-    const char* vb_ = smem + buf * BUF + vread;
-    const int k0 = j * BC;
-    const bool wave_live = !CAUSAL || (k0 <= qw0 + kQW - 1);
-    if (wave_live) {
-      f32x16 s[NKB];
-      const f32x16 zero = {};
+  };
+
+  // Row statistics.  m_run[h] is the stale maximum every P of block h is
+  // taken against (exp2 units, -inf until a row sees its first key); nmu is
+  // -m_run, or 0 while m_run = -inf so that masked scores give exp2(-inf);
+  // thr is the raw score above which a row's maximum has outgrown m_run by
+  // more than the lazy margin.
+  float m_run[2] = {-INFINITY, -INFINITY}, nmu[2] = {0.0f, 0.0f};
+  float thr[2] = {-INFINITY, -INFINITY};
+  float l_part[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};  // two partial sums per block (independent add chains)
+
+  // the first tile's products; its P^T "predecessor" is zero
+  vm_wait<C + kDB>();  // tiles 0 and 1 have landed (for this wave's share) ...
+  __syncthreads();   // ... for every wave
+  int j = j_first;
+  int so = 0;        // slot of tile j
+  int sp = 0;        // slot of the tile whose PV products run next (none yet: any landed slot)
+  prefetch_k(so);
+  prod_s(std::integral_constant<int, 0>{}, so, [](int) {});
+  vgpr_drain(s[0]);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32<Tag>(ld_row(kb_ + KL::row_off(kb, 0)), qreg[0], zero);
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) {
+    for (int kk = 0; kk < PK; ++kk) pb[1][h][kk] = u32x4{0u, 0u, 0u, 0u};
+  int jn = next_tile(j);
+  int sn = slot_next(so);
+  prefetch_k(sn);
+
+  // Iteration i (tile j = set X, its successor jn = set Y, its predecessor
+  // jp in slot sp):
+  //   A: S^T of jn (matrix products into VGPRs)
+  //      | mask, running-row maximum and t = S^T c - m of j
+  //   barrier (the tile after jn has landed; every wave is past A)
+  //   B: O^T += V^T P^T of jp (products into AGPRs)
+  //      | P = exp2(t), row sums and packing of j, DMA
+  // If a row's maximum outgrew the lazy margin in A, m is refreshed right
+  // after A (l and the t values of j rescaled) and O^T right after B.  The
+  // exponentials run beside the AGPR-destination products only: next to
+  // products that write VGPRs they issue markedly slower.
+  auto step = [&](auto x_c, auto mask_c) {
+    constexpr int X = decltype(x_c)::value;
+    constexpr int Y = 1 - X;
+    constexpr bool MASK = decltype(mask_c)::value;
+    int lim[2];
+    if constexpr (MASK) limits(j, lim);
+    // ---- A
+    float mx[2] = {-INFINITY, -INFINITY};
+    constexpr int R = 32 / (2 * KS);  // elements per product slot
+    // the first V^T fragments of tile jp are read during the last products
+    constexpr int kPV = kPD < NF ? kPD : NF;
+    const lchar* vtp = v_cols(sp);
+    prod_s(std::integral_constant<int, Y>{}, sn, [&](int u) {
+      if (u >= 2 * KS - kPV) kq[u - (2 * KS - kPV)] = rd_v(vtp, u - (2 * KS - kPV));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          s[kb] = mfma32<Tag>(ld_row(kb_ + KL::row_off(kb, ks)), qreg[ks], s[kb]);
-      }
-      const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > n);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            int key = k0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
-            bool dead = key >= n;
-            if constexpr (CAUSAL) dead = dead || key > my_q;
-            if (dead) s[kb][v] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * cs);
-      const bool grow = m_new > m_run + kLazy;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
-        if (grow) m_run = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
-      }
-      const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float p = fast_exp2(fmaf(s[kb][v], cs, -mu));
-          s[kb][v] = p;
-          rs += p;
+      for (int r = 0; r < R; r += 2) {
+        const int e = u * R + r, h = e >> 4, v = e & 15;
+        if constexpr (MASK) {
+          s[X][h][v] = (8 * (v >> 2) + (v & 3) > lim[h]) ? -INFINITY : s[X][h][v];
+          s[X][h][v + 1] = (8 * ((v + 1) >> 2) + ((v + 1) & 3) > lim[h]) ? -INFINITY : s[X][h][v + 1];
         }
-      l_part += rs;
+        mx[h] = max3(mx[h], s[X][h][v], s[X][h][v + 1]);
+        s[X][h][v] = fmaf(s[X][h][v], cs, nmu[h]);
+        s[X][h][v + 1] = fmaf(s[X][h][v + 1], cs, nmu[h]);
+      }
 #pragma unroll
-      for (int kk = 0; kk < PK; ++kk) {
-        const int kb = kk >> 1, h = kk & 1;
-        const u32x4 pb = pack8<Tag>(s[kb], 8 * h);
+      for (int q = kDB; q < C; ++q)
+        if (u == 1 + (q - kDB) * (2 * KS - 2) / (C - kDB)) dma_tile(q);
+    });
+    dma_advance();
+    const bool grow = __builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1]) != 0;
+    float alpha[2] = {1.0f, 1.0f};
+    if (grow) {  // rare: refresh m for the rows whose maximum outgrew it
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const u32x4 av = ld_tr(vb_ + VL::tr_off(kb, h, 0, mb), vb_ + VL::tr_off(kb, h, 1, mb));
-          oacc[mb] = mfma32<Tag>(av, pb, oacc[mb]);
-        }
+      for (int h = 0; h < 2; ++h) {
+        const float mt = half_max(mx[h]) * cs;
+        const bool gr = mt > m_run[h] + kLazy;
+        alpha[h] = gr ? fast_exp2(m_run[h] - mt) : 1.0f;
+        const float nmu_new = gr ? -mt : nmu[h];
+        const float delta = nmu_new - nmu[h];
+        m_run[h] = gr ? mt : m_run[h];
+        nmu[h] = nmu_new;
+        thr[h] = (m_run[h] + kLazy) * inv_cs;
+        l_part[h][0] *= alpha[h];
+        l_part[h][1] *= alpha[h];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[X][h][v] += delta;
       }
     }
-    if (jn < j_end) {
-      char* nb = smem + (buf ^ 1) * BUF;
-      sk.store(nb);
-      sv.store(nb + KT);
+    const int jnn = next_tile(jn);
+    const int snn = slot_next(sn);
+    vm_wait<C>();      // tile jnn has landed (for this wave's share) ...
+    wg_barrier();      // ... for every wave; the slot refilled below is free
+    // ---- B
+    // element e (block e/16, row e%16) of tile j in two stages one slot
+    // apart: P = exp2(t), then the row sum; each 8-element group is packed
+    // once summed
+    auto stx = [&](int e) {
+      const int h = e >> 4, v = e & 15;
+      s[X][h][v] = fast_exp2(s[X][h][v]);
+      asm volatile("" : "+v"(s[X][h][v]));
+    };
+    auto sty = [&](int e) {
+      const int h = e >> 4, v = e & 15;
+      l_part[h][v & 1] += s[X][h][v];
+      asm volatile("" : "+v"(l_part[h][v & 1]));
+      if ((v & 7) == 7) {
+        pb[X][h][v >> 3] = pack8<Tag>(s[X][h], v & 8);
+        asm volatile("" : "+v"(pb[X][h][v >> 3]));
+      }
+    };
+    auto staged = [&](int t) {
+      if (t < 32) stx(t);
+      if (t >= R && t - R < 32) sty(t - R);
+    };
+    const lchar* vt = v_cols(sp);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (f + kPD < NF) kq[(f + kPD) % (kPD + 1)] = rd_v(vt, f + kPD);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        mfma32_acc<Tag>(acc[h][f % MB], kq[f % (kPD + 1)], pb[Y][h][f / MB]);
+        const int u = 2 * f + h;
+#pragma unroll
+        for (int r = 0; r < R; ++r) staged(u * R + r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int q = 0; q < kDB; ++q)
+        if (f == (2 * q + 1) * NF / (2 * kDB)) dma_tile(q);
     }
-    __syncthreads();
-    buf ^= 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) staged(32 + r);
+    prefetch_k(snn);
+    if (grow) {
+      agpr_drain(acc[0]);
+      agpr_drain(acc[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[h][mb] *= alpha[h];
+    }
+    sp = so;
+    so = sn;
+    sn = snn;
     j = jn;
+    jn = jnn;
+  };
+  // Two iterations per trip keep the register sets in fixed roles.  The
+  // sweep runs until the PV products of the last tile are done; iterations
+  // past it see no tile (all keys masked, slots holding valid reloads).
+  // Dense sweeps start with the iterations whose tile j has no masked key
+  // for this wave (keys below its diagonal and inside the sequence), an
+  // even number of them, without any per-element test; the rest run with
+  // the mask.  The total is the same for every wave.
+  int n_plain = 0;
+  if constexpr (!SPARSE) {
+    int jm = n / BC;                                   // first tile reaching past the sequence end
+    if constexpr (CAUSAL) jm = min(jm, qw0 / BC);     // first tile crossing the diagonal
+    n_plain = max(jm - j_first, 0) & ~1;
   }
+  for (int t = 0; t < n_plain; t += 2) {
+    step(std::integral_constant<int, 0>{}, std::false_type{});
+    step(std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  // The iteration of tile j_end (the first past the last) runs the PV
+  // products of the last tile; the trip containing it is the last.
+  do {
+    step(std::integral_constant<int, 0>{}, std::true_type{});
+    step(std::integral_constant<int, 1>{}, std::true_type{});
+  } while (j <= j_end);
 
-  const float l = half_sum(l_part);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  if (my_q < n) {
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
+  agpr_drain(acc[0]);
+  agpr_drain(acc[1]);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int h = 0; h < 2; ++h) {
+    const float l = half_sum(l_part[h][0] + l_part[h][1]);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int my_q = qw0 + 32 * h + c32;
+    if (my_q < n) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 pk;
-        pk[0] = pack2<Tag>(oacc[mb][4 * r] * inv, oacc[mb][4 * r + 1] * inv);
-        pk[1] = pack2<Tag>(oacc[mb][4 * r + 2] * inv, oacc[mb][4 * r + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * r + 4 * g) = pk;
-      }
-    if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run * kLn2 + logf(l) : -INFINITY;
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 pk;
+          pk[0] = pack2<Tag>(acc[h][mb][4 * r] * inv, acc[h][mb][4 * r + 1] * inv);
+          pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * inv, acc[h][mb][4 * r + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * r + 4 * g) = pk;
+        }
+      if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
+    }
   }
 }
 
@@ -220,8 +452,6 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStrea
 }
 
 }  // namespace
-
-int fwd_query_block() { return kBR; }
 
 hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st) {
   a.nqb = (a.n + kBR - 1) / kBR;

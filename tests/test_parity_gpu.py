@@ -199,3 +199,33 @@ def test_stream_and_repeatability():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_refresh_mid_sweep(dtype, d, causal):
+    """Key rows scaled up along the sequence make every row's maximum rise
+    well past the lazy-refresh margin several times during the sweep, so
+    the accumulator rescale runs on tiles after the first, in both halves of
+    the unrolled loop and in masked and unmasked iterations."""
+    B, H, N = 1, 2, 1100
+    q, k, v, do = workloads.qkvdo(B, H, N, d, dtype, seed=31)
+    ramp = torch.linspace(0.25, 12.0, N).view(1, 1, N, 1)
+    k = (k.float() * ramp).to(k.dtype)
+    cpu = (q, k, v, do)
+    gq, gk, gv, gdo = (t.cuda() for t in cpu)
+    f64 = tuple(t.to(torch.float64).numpy() for t in cpu)
+    s = fp32_scale(d)
+    o, lse = flash.fwd(gq, gk, gv, scale=s, causal=causal)
+    dq, dk, dv = flash.bwd(gq, gk, gv, o, gdo, lse, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    O, L = _oracle_fwd(f64, s, causal)
+    tol = TOL[dtype]
+    compare("O", o, O, tol["o"], REL_RMS[dtype])
+    compare_lse("LSE", lse, L, tol["lse"])
+    gQ, gK, gV = _oracle_bwd(f64, s, causal)
+    # dK and dQ scale with the key magnitudes (up to 12x here)
+    compare("dQ", dq, gQ, 12 * tol["grad"], REL_RMS[dtype])
+    compare("dK", dk, gK, 12 * tol["grad"], REL_RMS[dtype])
+    compare("dV", dv, gV, tol["grad"], REL_RMS[dtype])
