@@ -74,13 +74,19 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
   const int n = a.n;
+  // Causal: workgroup p of a head runs the query blocks nqb-1-p and p one
+  // after the other, so every workgroup has the same number of key tiles
+  // (no long workgroup left running alone at the end of the grid).
+  const int per = CAUSAL ? (a.nqb + 1) / 2 : a.nqb;
   const int lb = xcd_remap(blockIdx.x, a.nblk);
-  const int bh = lb / a.nqb;
-  const int qb = a.nqb - 1 - (lb % a.nqb);  // longest causal rows first
+  const int bh = lb / per;
+  const int pb_ = lb % per;
   const size_t hoff = (size_t)bh * n * D;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
+
+  auto run = [&](const int qb) {
 
   const int q0 = qb * kBR;
   const int qw0 = q0 + w * kWQ;       // the wave's first query; block h starts at qw0 + 32h
@@ -290,30 +296,47 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     int lim[2];
     if constexpr (MASK) limits(j, lim);
     // ---- A
+    // Per element of tile j: mask and running maximum in the first half of
+    // the products (so the refresh test is known early), t = S c - m
+    // spread over all of them (after the element's mask).
     float mx[2] = {-INFINITY, -INFINITY};
-    constexpr int R = 32 / (2 * KS);  // elements per product slot
+    bool grow = false;
+    constexpr int RM = 32 / KS;       // elements per slot, mask and maximum
+    constexpr int R = 32 / (2 * KS);  // elements per slot, t
     // the first V^T fragments of tile jp are read during the last products
     constexpr int kPV = kPD < NF ? kPD : NF;
     const lchar* vtp = v_cols(sp);
     prod_s(std::integral_constant<int, Y>{}, sn, [&](int u) {
       if (u >= 2 * KS - kPV) kq[u - (2 * KS - kPV)] = rd_v(vtp, u - (2 * KS - kPV));
+      if (u < KS) {
 #pragma unroll
-      for (int r = 0; r < R; r += 2) {
-        const int e = u * R + r, h = e >> 4, v = e & 15;
-        if constexpr (MASK) {
-          s[X][h][v] = (8 * (v >> 2) + (v & 3) > lim[h]) ? -INFINITY : s[X][h][v];
-          s[X][h][v + 1] = (8 * ((v + 1) >> 2) + ((v + 1) & 3) > lim[h]) ? -INFINITY : s[X][h][v + 1];
+        for (int r = 0; r < RM; r += 2) {
+          const int e = u * RM + r, h = e >> 4, v = e & 15;
+          if constexpr (MASK) {
+            s[X][h][v] = (8 * (v >> 2) + (v & 3) > lim[h]) ? -INFINITY : s[X][h][v];
+            s[X][h][v + 1] = (8 * ((v + 1) >> 2) + ((v + 1) & 3) > lim[h]) ? -INFINITY : s[X][h][v + 1];
+          }
+          mx[h] = max3(mx[h], s[X][h][v], s[X][h][v + 1]);
         }
-        mx[h] = max3(mx[h], s[X][h][v], s[X][h][v + 1]);
+      }
+      if (u == KS) grow = __builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1]) != 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = u * R + r, h = e >> 4, v = e & 15;
         s[X][h][v] = fmaf(s[X][h][v], cs, nmu[h]);
-        s[X][h][v + 1] = fmaf(s[X][h][v + 1], cs, nmu[h]);
       }
 #pragma unroll
       for (int q = kDB; q < C; ++q)
         if (u == 1 + (q - kDB) * (2 * KS - 2) / (C - kDB)) dma_tile(q);
     });
     dma_advance();
-    const bool grow = __builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1]) != 0;
+    // ---- B, first products (independent of the refresh and the barrier)
+    const lchar* vt = v_cols(sp);
+    auto pv = [&](int f, int h) { mfma32_acc<Tag>(acc[h][f % MB], kq[f % (kPD + 1)], pb[Y][h][f / MB]); };
+    if (kPD < NF) kq[kPD % (kPD + 1)] = rd_v(vt, kPD);
+    pv(0, 0);
+    pv(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
     float alpha[2] = {1.0f, 1.0f};
     if (grow) {  // rare: refresh m for the rows whose maximum outgrew it
 #pragma unroll
@@ -336,10 +359,12 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     const int snn = slot_next(sn);
     vm_wait<C>();      // tile jnn has landed (for this wave's share) ...
     wg_barrier();      // ... for every wave; the slot refilled below is free
-    // ---- B
+    constexpr int kPK = kPD < KS ? kPD : KS;
+    const lchar* krn = k_rows(snn);
+    // ---- B, the rest
     // element e (block e/16, row e%16) of tile j in two stages one slot
     // apart: P = exp2(t), then the row sum; each 8-element group is packed
-    // once summed
+    // once summed.  Slot u (2 .. 2NF-1) takes elements E(u-2) .. E(u-1)-1.
     auto stx = [&](int e) {
       const int h = e >> 4, v = e & 15;
       s[X][h][v] = fast_exp2(s[X][h][v]);
@@ -354,29 +379,33 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
         asm volatile("" : "+v"(pb[X][h][v >> 3]));
       }
     };
-    auto staged = [&](int t) {
-      if (t < 32) stx(t);
-      if (t >= R && t - R < 32) sty(t - R);
+    constexpr int NS = 2 * NF - 2;  // slots carrying element work
+    auto E = [](int k) { return 32 * k / NS; };
+    auto slot_work = [&](int u) {  // u = 2 .. 2NF (2NF: the tail)
+      const int k = u - 2;
+      if (k < NS)
+        for (int e = E(k); e < E(k + 1); ++e) stx(e);
+      if (k >= 1)
+        for (int e = E(k - 1); e < E(k); ++e) sty(e);
     };
-    const lchar* vt = v_cols(sp);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    for (int f = 1; f < NF; ++f) {
       if (f + kPD < NF) kq[(f + kPD) % (kPD + 1)] = rd_v(vt, f + kPD);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        mfma32_acc<Tag>(acc[h][f % MB], kq[f % (kPD + 1)], pb[Y][h][f / MB]);
+        pv(f, h);
+        slot_work(2 * f + h);
+        // the first K fragments of tile jnn (landed: barrier above) are
+        // read during the first products, for the next A phase
         const int u = 2 * f + h;
-#pragma unroll
-        for (int r = 0; r < R; ++r) staged(u * R + r);
+        if (u >= 2 && u < 2 + kPK) fr[u - 2] = rd_k(krn, u - 2);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int q = 0; q < kDB; ++q)
-        if (f == (2 * q + 1) * NF / (2 * kDB)) dma_tile(q);
+        if (f == 1 + (2 * q + 1) * (NF - 1) / (2 * kDB)) dma_tile(q);
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) staged(32 + r);
-    prefetch_k(snn);
+    slot_work(2 * NF);
     if (grow) {
       agpr_drain(acc[0]);
       agpr_drain(acc[1]);
@@ -391,6 +420,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     j = jn;
     jn = jnn;
   };
+
   // Two iterations per trip keep the register sets in fixed roles.  The
   // sweep runs until the PV products of the last tile are done; iterations
   // past it see no tile (all keys masked, slots holding valid reloads).
@@ -436,6 +466,17 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
     }
   }
+  };
+  const int qa = a.nqb - 1 - pb_;  // the longer block first
+  const int nrun = (CAUSAL && pb_ != qa) ? 2 : 1;
+#pragma clang loop unroll(disable)
+  for (int r = 0; r < nrun; ++r) {
+    if (r) {
+      vm_wait<0>();      // the first block's DMA and stores are done ...
+      __syncthreads();   // ... and every wave is out of its LDS tiles
+    }
+    run(r ? pb_ : qa);
+  }
 }
 
 template <typename Tag, int D>
@@ -455,7 +496,7 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStrea
 
 hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st) {
   a.nqb = (a.n + kBR - 1) / kBR;
-  a.nblk = a.nqb * bh;
+  a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)
