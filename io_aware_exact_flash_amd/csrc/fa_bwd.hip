@@ -101,9 +101,13 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
   const int n = a.n;
+  // Causal: workgroup p of a head runs the key blocks p and nkb-1-p one
+  // after the other, so every workgroup sees the same number of query
+  // tiles (low key blocks see the most queries).
+  const int per = CAUSAL ? (a.nkb + 1) / 2 : a.nkb;
   const int lb = xcd_remap(blockIdx.x, a.nblk_kv);
-  const int bh = lb / a.nkb;
-  const int kb = lb % a.nkb;  // low key blocks see the most queries under causal
+  const int bh = lb / per;
+  const int pk_ = lb % per;
   const size_t hoff = (size_t)bh * n * D;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float* __restrict__ Ltg = a.lt + (size_t)bh * n;
   const float* __restrict__ Dg = a.dvec + (size_t)bh * n;
 
+  auto run = [&](const int kb) {
   const int k0 = kb * BKV;
   const int kw0 = k0 + w * 32;
   const int my_k = kw0 + c32;
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int in = next_tile(i);
     const int son = slot_next(so);
     vm_wait<C>();      // tile `in` has landed (for this wave's share) ...
-    __syncthreads();   // ... for every wave; the slot refilled below is free
+    wg_barrier();      // ... for every wave; the slot refilled below is free
     const int q0 = i * BQ;
     const lchar* base = lds_ptr(smem) + so;
     // element v holds query q0 + 4g + 8(v/4) + v%4 (and this lane's key);
@@ -389,6 +394,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
         *reinterpret_cast<u32x2*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
       }
   }
+  };
+  const int kb2 = a.nkb - 1 - pk_;
+  const int nrun = (CAUSAL && pk_ != kb2) ? 2 : 1;
+#pragma clang loop unroll(disable)
+  for (int r = 0; r < nrun; ++r) {
+    if (r) {
+      vm_wait<0>();      // the first block's DMA and stores are done ...
+      __syncthreads();   // ... and every wave is out of its LDS tiles
+    }
+    run(r ? kb2 : pk_);
+  }
 }
 
 // ------------------------------------------------------------ dQ pass
@@ -437,15 +453,19 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
   const int n = a.n;
+  // Causal: workgroup p of a head runs the query blocks nqb-1-p and p one
+  // after the other (equal work for every workgroup).
+  const int per = CAUSAL ? (a.nqb + 1) / 2 : a.nqb;
   const int lb = xcd_remap(blockIdx.x, a.nblk_q);
-  const int bh = lb / a.nqb;
-  const int qb = a.nqb - 1 - (lb % a.nqb);
+  const int bh = lb / per;
+  const int pq_ = lb % per;
   const size_t hoff = (size_t)bh * n * D;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
   const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
 
+  auto run = [&](const int qb) {
   const int q0 = qb * BR;
   const int qw0 = q0 + w * 64;        // the wave's first query; block h starts at qw0 + 32h
 
@@ -501,12 +521,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   VD vd;
   kd.init(w, lane);
   vd.init(w, lane);
-  // DMA instruction i (of C) of tile jt into the slot at byte offset so
-  auto dma = [&](int i, int jt, int so) {
-    char* b = smem + so;
-    if (i < KD::kPer) kd.issue_one(i, Kg + (size_t)jt * BC * D, n - jt * BC, b);
-    else vd.issue_one(i - KD::kPer, Vg + (size_t)jt * BC * D, n - jt * BC, b + KD::kSlot);
-  };
   const int krow = KL::row_base(c32, g);
   const int ktr = KL::tr_base(lane);
   const int vrow = KD::kSlot + VL::row_base(c32, g);
@@ -530,11 +544,31 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   // landed" is always vmcnt <= C at the top of iteration t.
   int jq = j_first;  // next tile to load
   int sq = 0;        // its slot
-  auto dma_tile = [&](int i) { dma(i, jq < j_end ? jq : j_first, sq); };
+  // its addressing, set once per tile: K and V rows, last valid row, LDS
+  // address of this wave's share
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+  const uint16_t* dk = Kg;
+  const uint16_t* dv = Vg;
+  int d_last = 0;
+  uint32_t d_lds = 0;
+  auto dma_set = [&]() {
+    const int jt = jq < j_end ? jq : j_first;
+    dk = Kg + (size_t)jt * BC * D;
+    dv = Vg + (size_t)jt * BC * D;
+    d_last = n - 1 - jt * BC;
+    d_lds = lds_base + sq + 1024 * w;
+  };
+  // DMA instruction i (of C) of the tile
+  auto dma_tile = [&](int i) {
+    if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
+    else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
+  };
   auto dma_advance = [&]() {
     if (jq < j_end) jq = next_tile(jq);
     sq = slot_next(sq);
+    dma_set();
   };
+  dma_set();
   for (int t = 0; t < kRing - 1; ++t) {
 #pragma unroll
     for (int i = 0; i < C; ++i) dma_tile(i);
@@ -621,7 +655,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     const int jn = next_tile(j);
     const int son = slot_next(so);
     vm_wait<C>();      // tile jn has landed (for this wave's share) ...
-    __syncthreads();   // ... for every wave; the slot refilled below is free
+    wg_barrier();      // ... for every wave; the slot refilled below is free
     // dense sweeps compute every tile, the dummy one included: its keys lie
     // past the sequence end, so the mask gives dS = 0, and its slot holds a
     // valid reload; branches here would cost fetch bubbles a lone wave
@@ -761,6 +795,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
         }
     }
   }
+  };
+  const int qa = a.nqb - 1 - pq_;  // the longer block first
+  const int nrun = (CAUSAL && pq_ != qa) ? 2 : 1;
+#pragma clang loop unroll(disable)
+  for (int r = 0; r < nrun; ++r) {
+    if (r) {
+      vm_wait<0>();      // the first block's DMA and stores are done ...
+      __syncthreads();   // ... and every wave is out of its LDS tiles
+    }
+    run(r ? pq_ : qa);
+  }
 }
 
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
@@ -798,9 +843,9 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const BwdArgs& a, hipStrea
 
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st) {
   a.nqb = (a.n + kDqRows - 1) / kDqRows;
-  a.nblk_q = a.nqb * bh;
+  a.nblk_q = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   a.nkb = (a.n + 127) / 128;
-  a.nblk_kv = a.nkb * bh;
+  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * bh;
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)
