@@ -165,16 +165,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // rows start past the end reads the last row instead (those rows are
   // dead); one that straddles the end reads up to 3 floats past it, which
   // the workspace's spare bytes cover.
-  auto dma = [&](int t, int it, int so) {
-    char* b = smem + so;
-    const int valid = n - it * BQ;
-    if (t < QD::kPer) qd.issue_one(t, Qg + (size_t)it * BQ * D, valid, b);
-    else if (t < 2 * QD::kPer) qd.issue_one(t - QD::kPer, dOg + (size_t)it * BQ * D, valid, b + LDO);
-    else if (lane < 16) {
-      const int row = min(it * BQ + 4 * (lane & 7), n - 1);
-      dma16((lane < 8 ? Ltg : Dg) + row, lds_addr(b + LLD));
-    }
-  };
+  // (The addressing of the tile being loaded is set once per tile, in
+  // dma_set() below.)
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+  const uint16_t* d_q = Qg;
+  const uint16_t* d_o = dOg;
+  const float* d_ld = Ltg;  // this lane's L or D source (lanes 0-15)
+  int d_last = 0;
+  uint32_t d_lds = 0, d_slot = 0;
   const int rrow = TL::row_base(c32, g);
   const int rtr = TL::tr_base(lane);
   auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
@@ -184,11 +182,26 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // landed" is always vmcnt <= C at the top of iteration t.
   int iq = i_first;  // next tile to load
   int sq = 0;        // its slot
-  auto dma_tile = [&](int t) { dma(t, iq < n_tiles ? iq : i_first, sq); };
+  auto dma_set = [&]() {
+    const int it = iq < n_tiles ? iq : i_first;
+    d_q = Qg + (size_t)it * BQ * D;
+    d_o = dOg + (size_t)it * BQ * D;
+    d_last = n - 1 - it * BQ;
+    d_slot = lds_base + sq;
+    d_lds = d_slot + 1024 * w;
+    d_ld = (lane < 8 ? Ltg : Dg) + min(it * BQ + 4 * (lane & 7), n - 1);
+  };
+  auto dma_tile = [&](int t) {
+    if (t < QD::kPer) qd.issue_at(t, d_q, d_last, d_lds);
+    else if (t < 2 * QD::kPer) qd.issue_at(t - QD::kPer, d_o, d_last, d_lds + LDO);
+    else if (lane < 16) dma16(d_ld, d_slot + LLD);
+  };
   auto dma_advance = [&]() {
     if (iq < n_tiles) iq = next_tile(iq);
     sq = slot_next(sq);
+    dma_set();
   };
+  dma_set();
   for (int t = 0; t < kRing - 1; ++t) {
 #pragma unroll
     for (int u = 0; u < C; ++u) dma_tile(u);
