@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     pv(0, 1);
     __builtin_amdgcn_sched_barrier(0);
     float alpha[2] = {1.0f, 1.0f};
-    if (grow) {  // rare: refresh m for the rows whose maximum outgrew it
+    if (__builtin_expect(grow, 0)) {  // rare: refresh m for the rows whose maximum outgrew it
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const float mt = half_max(mx[h]) * cs;
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
         if (f == 1 + (2 * q + 1) * (NF - 1) / (2 * kDB)) dma_tile(q);
     }
     slot_work(2 * NF);
-    if (grow) {
+    if (__builtin_expect(grow, 0)) {
       agpr_drain(acc[0]);
       agpr_drain(acc[1]);
 #pragma unroll
