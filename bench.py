@@ -73,10 +73,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, bytes per launch)
-    ("fwd", 4): ("8b0851baab2e60a3", 1573775360),
-    ("bwd_pre", 4): ("74733db6f2f6cb52", 692088832),
-    ("bwd_dkdv", 4): ("74733db6f2f6cb52", 2115784704),
-    ("bwd_dq", 4): ("74733db6f2f6cb52", 2267428864),
+    ("fwd", 4): ("be93282b97dd6192", 1887637504),
+    ("bwd_pre", 4): ("e73a793ec9810a43", 692099072),
+    ("bwd_dkdv", 4): ("e73a793ec9810a43", 2121271296),
+    ("bwd_dq", 4): ("e73a793ec9810a43", 2461702144),
 }
 
 

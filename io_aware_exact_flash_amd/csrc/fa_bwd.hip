@@ -117,25 +117,25 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float* __restrict__ Dg = a.dvec + (size_t)bh * n;
 
   auto run = [&](const int kb) {
-  const int k0 = kb * BKV;
-  const int kw0 = k0 + w * 32;
-  const int my_k = kw0 + c32;
+    const int k0 = kb * BKV;
+    const int kw0 = k0 + w * 32;
+    const int my_k = kw0 + c32;
 
-  u32x4 kreg[KS], vreg[KS];  // K^T, V^T fragments (B operands), in AGPRs
-  {
-    const size_t r = (size_t)min(my_k, n - 1) * D + 8 * g;
+    u32x4 kreg[KS], vreg[KS];  // K^T, V^T fragments (B operands), in AGPRs
+    {
+      const size_t r = (size_t)min(my_k, n - 1) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      gload_agpr(kreg[ks], Kg + r + 16 * ks);
-      gload_agpr(vreg[ks], Vg + r + 16 * ks);
+      for (int ks = 0; ks < KS; ++ks) {
+        gload_agpr(kreg[ks], Kg + r + 16 * ks);
+        gload_agpr(vreg[ks], Vg + r + 16 * ks);
+      }
     }
-  }
-  vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
+    vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
 
-  const int n_tiles = (n + BQ - 1) / BQ;
-  auto tile_live = [&](int i) {
-    if constexpr (SPARSE) return a.mask[(size_t)((i * BQ) / kMaskBlock) * a.mask_t + kb] != 0;
-    return true;
+    const int n_tiles = (n + BQ - 1) / BQ;
+    auto tile_live = [&](int i) {
+      if constexpr (SPARSE) return a.mask[(size_t)((i * BQ) / kMaskBlock) * a.mask_t + kb] != 0;
+      return true;
   };
   auto next_tile = [&](int i) {
     ++i;
@@ -479,48 +479,48 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
 
   auto run = [&](const int qb) {
-  const int q0 = qb * BR;
-  const int qw0 = q0 + w * 64;        // the wave's first query; block h starts at qw0 + 32h
+    const int q0 = qb * BR;
+    const int qw0 = q0 + w * 64;        // the wave's first query; block h starts at qw0 + 32h
 
-  u32x4 qreg[2][KS], oreg[2][KS];     // Q^T and dO^T fragments, in AGPRs
-  float Lq[2], Dq[2];
+    u32x4 qreg[2][KS], oreg[2][KS];     // Q^T and dO^T fragments, in AGPRs
+    float Lq[2], Dq[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int my_q = qw0 + 32 * h + c32;
-    const int qr = min(my_q, n - 1);
-    const size_t r = (size_t)qr * D + 8 * g;
+    for (int h = 0; h < 2; ++h) {
+      const int my_q = qw0 + 32 * h + c32;
+      const int qr = min(my_q, n - 1);
+      const size_t r = (size_t)qr * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
-      gload_agpr(oreg[h][ks], dOg + r + 16 * ks);
+      for (int ks = 0; ks < KS; ++ks) {
+        gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
+        gload_agpr(oreg[h][ks], dOg + r + 16 * ks);
+      }
+      const float l = a.lse[(size_t)bh * n + qr];
+      Lq[h] = (l == -INFINITY || my_q >= n) ? INFINITY : l * kLog2e;
+      Dq[h] = a.dvec[(size_t)bh * n + qr];
     }
-    const float l = a.lse[(size_t)bh * n + qr];
-    Lq[h] = (l == -INFINITY || my_q >= n) ? INFINITY : l * kLog2e;
-    Dq[h] = a.dvec[(size_t)bh * n + qr];
-  }
 
-  f32x16 negD[2];  // -D of each block's query, the dP^T accumulators' starting value
+    f32x16 negD[2];  // -D of each block's query, the dP^T accumulators' starting value
 #pragma unroll
-  for (int h = 0; h < 2; ++h) negD[h] = -Dq[h];
-  const int n_tiles = (n + BC - 1) / BC;
-  int j_end = n_tiles;
-  if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + BR, n) - 1) / BC + 1);
-  // block-sparse: the workgroup spans two 128-query mask rows, each wave one
-  const uint8_t* mrow0 = nullptr;
-  const uint8_t* mrow1 = nullptr;
-  const uint8_t* mwave = nullptr;
-  if constexpr (SPARSE) {
-    const int t0 = q0 / kMaskBlock;
-    const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
-    mrow0 = a.mask + (size_t)t0 * a.mask_t;
-    mrow1 = a.mask + (size_t)t1 * a.mask_t;
-    mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
-  }
-  auto next_tile = [&](int j) {
-    ++j;
-    if constexpr (SPARSE)
-      while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
-    return j;
+    for (int h = 0; h < 2; ++h) negD[h] = -Dq[h];
+    const int n_tiles = (n + BC - 1) / BC;
+    int j_end = n_tiles;
+    if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + BR, n) - 1) / BC + 1);
+    // block-sparse: the workgroup spans two 128-query mask rows, each wave one
+    const uint8_t* mrow0 = nullptr;
+    const uint8_t* mrow1 = nullptr;
+    const uint8_t* mwave = nullptr;
+    if constexpr (SPARSE) {
+      const int t0 = q0 / kMaskBlock;
+      const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
+      mrow0 = a.mask + (size_t)t0 * a.mask_t;
+      mrow1 = a.mask + (size_t)t1 * a.mask_t;
+      mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+    }
+    auto next_tile = [&](int j) {
+      ++j;
+      if constexpr (SPARSE)
+        while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
+      return j;
   };
   // tiles of this wave's queries that have allowed keys
   auto live = [&](int jt) {

@@ -37,17 +37,6 @@ constexpr int kMaskBlock = 128;  // tokens per block-mask entry
 struct bf16_tag {};
 struct f16_tag {};
 
-// 32x32x16 MFMA on packed 16-bit operands (8 per lane in a u32x4).
-template <typename Tag>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (std::is_same<Tag, bf16_tag>::value)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
 // D += A B with D pinned to accumulation registers (AGPRs) for its whole
 // lifetime.  Left to itself the compiler copies long-lived accumulators
 // between register files every iteration once a kernel needs more than 256
@@ -256,7 +245,6 @@ struct Pad {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
-__device__ __forceinline__ u32x4 ld_row(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Value of lane 4*(lane/4) + i in every lane of the quad (DPP quad_perm
 // broadcast; i is a compile-time constant after unrolling).
@@ -287,13 +275,6 @@ __device__ __forceinline__ const lchar* lds_opaque(const lchar* p) {
 __device__ __forceinline__ u32x4 ld_row(const lchar* p) { return *(const lds_u32x4*)p; }
 
 // One MFMA operand (8 slots) by two transpose reads.
-__device__ __forceinline__ u32x4 ld_tr(const char* p0, const char* p1) {
-  typedef short s16x8_t __attribute__((ext_vector_type(8)));
-  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-  const s16x8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(u32x4, ab);
-}
 __device__ __forceinline__ u32x4 ld_tr(const lchar* p0, const lchar* p1) {
   typedef short s16x8_t __attribute__((ext_vector_type(8)));
   const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
@@ -302,60 +283,6 @@ __device__ __forceinline__ u32x4 ld_tr(const lchar* p0, const lchar* p1) {
   return __builtin_bit_cast(u32x4, ab);
 }
 
-// Global -> registers -> LDS staging of a tile of ROWS tokens x D columns.
-// A unit is RPU consecutive tokens (RPU <= 4, inside one 4-row rotation
-// group) x 8 columns; thread tid owns unit tid (threads beyond the unit count
-// idle).  Tokens at or beyond `valid` are clamped to the last valid row so
-// every load stays in bounds; callers mask them.
-template <int ROWS, int D, int NT, bool TR>
-struct Stage {
-  static constexpr int kChunks = ROWS * D / 8;
-  static constexpr int RPU = kChunks >= NT ? kChunks / NT : 1;
-  static constexpr int kUnits = kChunks / RPU;
-  static_assert(RPU <= 4 && kChunks % RPU == 0 && kUnits <= NT, "staging split");
-  u32x4 r[RPU];
-  int goff;   // element offset of this thread's unit inside a tile
-  int soff;   // LDS byte offset of this thread's unit inside a tile
-  int row0;   // first row of the unit
-  bool act;
-
-  __device__ void init(int tid) {
-    act = tid < kUnits;
-    const int dc = tid % (D / 8), tg = tid / (D / 8);
-    row0 = RPU * tg;
-    goff = row0 * D + 8 * dc;
-    soff = row0 * Pad<D, TR>::S + Pad<D, TR>::rot(row0) + 16 * dc;
-  }
-  // tile: first row of the tile (uniform pointer); valid: rows of the tile
-  // that exist (ROWS or fewer on the last tile)
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ tile, int valid) {
-    if (!act) return;
-    if (valid >= ROWS) {
-#pragma unroll
-      for (int j = 0; j < RPU; ++j) r[j] = *reinterpret_cast<const u32x4*>(tile + goff + j * D);
-    } else {
-#pragma unroll
-      for (int j = 0; j < RPU; ++j) {
-        const int row = min(row0 + j, valid - 1);
-        r[j] = *reinterpret_cast<const u32x4*>(tile + (goff - row0 * D) + row * D);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* lds_tile) const {
-    if (!act) return;
-#pragma unroll
-    for (int j = 0; j < RPU; ++j)
-      *reinterpret_cast<u32x4*>(lds_tile + soff + j * Pad<D, TR>::S) = r[j];
-  }
-};
-
-// Global -> LDS staging without registers (global_load_lds_dwordx4: lane i
-// of a wave writes its 16 bytes at M0 + 16*i).  The padded LDS image of a
-// tile is cut into 1 KB blocks; block b is moved by wave b % NW, whose lane i
-// fetches the 16 bytes that belong at block offset 16*i (lanes that fall on
-// row padding or past the tile stay idle).  Rows at or beyond `valid` are
-// clamped to the last valid row so every load stays in bounds.  Completion
-// is awaited with dma_wait() (vmcnt) before the workgroup barrier.
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane.  Issued
 // through asm so the compiler does not track the LDS write: left to itself
 // it makes the next LDS read wait for every outstanding DMA (vmcnt(0)),
@@ -367,7 +294,6 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 #endif
 }
-__device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(uintptr_t)(lchar*)p; }
 // Same, from a wave-uniform base plus a per-lane 32-bit byte offset (no
 // 64-bit address arithmetic per lane).
 __device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds) {
@@ -376,6 +302,16 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t
 #endif
 }
 
+// Global -> LDS staging without registers (global_load_lds_dwordx4: lane i
+// of a wave writes its 16 bytes at M0 + 16*i).  The padded LDS image of a
+// tile is cut into 1 KB blocks; block b is moved by wave b % NW, whose lane i
+// fetches the 16 bytes that belong at block offset 16*i.  Every wave issues
+// exactly kPer instructions per tile with every lane active: a lane whose
+// destination is row padding or lies past the tile (bytes no operand fetch
+// reads) loads the tile's first 16 bytes there, so outstanding-load counts
+// are exact and uniform across waves.  Rows at or beyond the last valid row
+// re-read it, so every load stays in bounds.  Completion is awaited with
+// vm_wait<>() before the workgroup barrier.
 template <int ROWS, int D, bool TR, int NW>
 struct Dma {
   using L = Pad<D, TR>;
@@ -383,68 +319,32 @@ struct Dma {
   static constexpr int kBlocks = (kBytes + 1023) / 1024;
   static constexpr int kPer = (kBlocks + NW - 1) / NW;   // DMA instructions per wave per tile
   static constexpr int kSlot = kPer * NW * 1024;         // LDS bytes reserved per tile
-  int src[kPer];   // element offset inside the tile (0 for padding / past the tile)
-  int row[kPer];   // its row and its column in bytes
-  int colb[kPer];
-  int wave;
+  int row[kPer];   // source row of instruction k's 16 bytes (0 for padding / past the tile)
+  int colb[kPer];  // and its column, in bytes
 
   __device__ void init(int w, int lane) {
-    wave = w;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int off = (w + NW * k) * 1024 + 16 * lane;
-      src[k] = 0;
+      int src = 0;  // element offset inside the tile
       if (off < kBytes) {
         const int r = off / L::S;
         const int p = off - r * L::S - L::rot(r);
-        if (p >= 0 && p < 2 * D) src[k] = r * D + p / 2;
+        if (p >= 0 && p < 2 * D) src = r * D + p / 2;
       }
-      row[k] = src[k] / D;
-      colb[k] = 2 * (src[k] % D);
+      row[k] = src / D;
+      colb[k] = 2 * (src % D);
     }
   }
-  // Every wave issues exactly kPer instructions per tile, with every lane
-  // active: lanes whose destination is row padding or lies past the tile
-  // (bytes no operand fetch reads) load the tile's first 16 bytes there.
-  // Outstanding-load counts are therefore exact and uniform across waves.
-  __device__ __forceinline__ void issue(const uint16_t* __restrict__ t0, int valid, char* l0) const {
-#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass only needs the declaration
-    if (valid >= ROWS) {
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) dma16(t0 + src[k], lds_addr(l0 + (wave + NW * k) * 1024));
-    } else {  // last, partial tile: rows past the end re-read the last row
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        int e = src[k];
-        if (e / D >= valid) e = (valid - 1) * D + (e % D);
-        dma16(t0 + e, lds_addr(l0 + (wave + NW * k) * 1024));
-      }
-    }
-#endif
-  }
-  // Instruction k of issue() alone, so a caller can spread a tile's DMA
-  // between its own products instead of queueing it all at once.
-  __device__ __forceinline__ void issue_one(int k, const uint16_t* __restrict__ t0, int valid, char* l0) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    // rows past the end re-read the last row (branch-free: two VALU ops)
-    const uint32_t off = (uint32_t)min(row[k], valid - 1) * (2 * D) + colb[k];
-    dma16_s(t0, off, lds_addr(l0 + (wave + NW * k) * 1024));
-#endif
-  }
-  // Same, with the tile's addressing hoisted by the caller (once per tile):
-  // t0 its first row, last its last valid row (rows past it re-read it),
-  // lds_w the LDS byte address of the tile plus 1024 * wave.
+  // Instruction k of wave w's share of a tile, with the tile's addressing
+  // hoisted by the caller (once per tile): t0 its first row, last its last
+  // valid row (rows past it re-read it), lds_w the LDS byte address of the
+  // tile plus 1024 * w.
   __device__ __forceinline__ void issue_at(int k, const uint16_t* __restrict__ t0, int last, uint32_t lds_w) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     const uint32_t off = (uint32_t)min(row[k], last) * (2 * D) + colb[k];
     dma16_s(t0, off, lds_w + NW * k * 1024);
 #endif
-  }
-  // Moves two tiles of the same geometry with one set of offsets.
-  __device__ __forceinline__ void issue2(const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
-                                         int valid, char* l0, char* l1) const {
-    issue(t0, valid, l0);
-    issue(t1, valid, l1);
   }
 };
 
@@ -457,7 +357,6 @@ __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ void dma_wait() { vm_wait<0>(); }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // makes every wave first wait for its own outstanding LDS reads, which
@@ -468,17 +367,6 @@ __device__ __forceinline__ void wg_barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_barrier" ::: "memory");
 #endif
-}
-
-// Make the register operands loaded before a loop complete there: the
-// waitcnt pass otherwise keeps them "possibly pending" on some path into the
-// loop and waits on the counter inside it, which also waits for that
-// iteration's global prefetch.  An empty asm that reads the registers forces
-// the wait once, before the loop.
-template <int N>
-__device__ __forceinline__ void settle(const u32x4 (&r)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
 }
 
 // Map a linear workgroup id so that each XCD (ids are dealt round-robin to

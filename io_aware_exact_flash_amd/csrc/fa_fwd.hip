@@ -87,37 +87,36 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
 
   auto run = [&](const int qb) {
+    const int q0 = qb * kBR;
+    const int qw0 = q0 + w * kWQ;       // the wave's first query; block h starts at qw0 + 32h
 
-  const int q0 = qb * kBR;
-  const int qw0 = q0 + w * kWQ;       // the wave's first query; block h starts at qw0 + 32h
-
-  u32x4 qreg[2][KS];                  // Q^T fragments, in AGPRs
+    u32x4 qreg[2][KS];                  // Q^T fragments, in AGPRs
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const size_t r = (size_t)min(qw0 + 32 * h + c32, n - 1) * D + 8 * g;
+    for (int h = 0; h < 2; ++h) {
+      const size_t r = (size_t)min(qw0 + 32 * h + c32, n - 1) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
-  }
+      for (int ks = 0; ks < KS; ++ks) gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
+    }
 
-  const int n_tiles = (n + BC - 1) / BC;
-  int j_end = n_tiles;
-  if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + kBR, n) - 1) / BC + 1);
-  // block-sparse: the workgroup spans two 128-query mask rows, each wave one
-  const uint8_t* mrow0 = nullptr;
-  const uint8_t* mrow1 = nullptr;
-  const uint8_t* mwave = nullptr;
-  if constexpr (SPARSE) {
-    const int t0 = q0 / kMaskBlock;
-    const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
-    mrow0 = a.mask + (size_t)t0 * a.mask_t;
-    mrow1 = a.mask + (size_t)t1 * a.mask_t;
-    mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
-  }
-  auto next_tile = [&](int j) {
-    ++j;
-    if constexpr (SPARSE)
-      while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
-    return j;
+    const int n_tiles = (n + BC - 1) / BC;
+    int j_end = n_tiles;
+    if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + kBR, n) - 1) / BC + 1);
+    // block-sparse: the workgroup spans two 128-query mask rows, each wave one
+    const uint8_t* mrow0 = nullptr;
+    const uint8_t* mrow1 = nullptr;
+    const uint8_t* mwave = nullptr;
+    if constexpr (SPARSE) {
+      const int t0 = q0 / kMaskBlock;
+      const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
+      mrow0 = a.mask + (size_t)t0 * a.mask_t;
+      mrow1 = a.mask + (size_t)t1 * a.mask_t;
+      mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+    }
+    auto next_tile = [&](int j) {
+      ++j;
+      if constexpr (SPARSE)
+        while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
+      return j;
   };
   // tiles of this wave's queries that have allowed keys
   auto live = [&](int jt) {
