@@ -136,277 +136,277 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     auto tile_live = [&](int i) {
       if constexpr (SPARSE) return a.mask[(size_t)((i * BQ) / kMaskBlock) * a.mask_t + kb] != 0;
       return true;
-  };
-  auto next_tile = [&](int i) {
-    ++i;
-    if constexpr (SPARSE)
-      while (i < n_tiles && !tile_live(i)) ++i;
-    return i;
-  };
-  int i_first = CAUSAL ? k0 / BQ : 0;
-  if (!tile_live(i_first)) i_first = next_tile(i_first);
-  if (i_first >= n_tiles) {  // no query sees these keys: dK = dV = 0
+    };
+    auto next_tile = [&](int i) {
+      ++i;
+      if constexpr (SPARSE)
+        while (i < n_tiles && !tile_live(i)) ++i;
+      return i;
+    };
+    int i_first = CAUSAL ? k0 / BQ : 0;
+    if (!tile_live(i_first)) i_first = next_tile(i_first);
+    if (i_first >= n_tiles) {  // no query sees these keys: dK = dV = 0
+      if (my_k < n) {
+        uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
+        uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
+        for (int c = 8 * g; c < D; c += 16) {
+          *reinterpret_cast<u32x4*>(dkp + c) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(dvp + c) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      return;
+    }
+
+    QD qd;  // Q and dO tiles share one geometry
+    qd.init(w, lane);
+    // DMA instruction t (of C) of tile it into the slot at byte offset so:
+    // Q and dO share the tile geometry; the last one moves the tile's base-2
+    // LSE (lanes 0-7) and D (lanes 8-15), four rows per lane.  A lane whose
+    // rows start past the end reads the last row instead (those rows are
+    // dead); one that straddles the end reads up to 3 floats past it, which
+    // the workspace's spare bytes cover.
+    // (The addressing of the tile being loaded is set once per tile, in
+    // dma_set() below.)
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+    const uint16_t* d_q = Qg;
+    const uint16_t* d_o = dOg;
+    const float* d_ld = Ltg;  // this lane's L or D source (lanes 0-15)
+    int d_last = 0;
+    uint32_t d_lds = 0, d_slot = 0;
+    const int rrow = TL::row_base(c32, g);
+    const int rtr = TL::tr_base(lane);
+    auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
+
+    // Every iteration issues exactly C DMA instructions (past the last tile
+    // they reload the first tile into a slot nobody reads), so "tile t+1 has
+    // landed" is always vmcnt <= C at the top of iteration t.
+    int iq = i_first;  // next tile to load
+    int sq = 0;        // its slot
+    auto dma_set = [&]() {
+      const int it = iq < n_tiles ? iq : i_first;
+      d_q = Qg + (size_t)it * BQ * D;
+      d_o = dOg + (size_t)it * BQ * D;
+      d_last = n - 1 - it * BQ;
+      d_slot = lds_base + sq;
+      d_lds = d_slot + 1024 * w;
+      d_ld = (lane < 8 ? Ltg : Dg) + min(it * BQ + 4 * (lane & 7), n - 1);
+    };
+    auto dma_tile = [&](int t) {
+      if (t < QD::kPer) qd.issue_at(t, d_q, d_last, d_lds);
+      else if (t < 2 * QD::kPer) qd.issue_at(t - QD::kPer, d_o, d_last, d_lds + LDO);
+      else if (lane < 16) dma16(d_ld, d_slot + LLD);
+    };
+    auto dma_advance = [&]() {
+      if (iq < n_tiles) iq = next_tile(iq);
+      sq = slot_next(sq);
+      dma_set();
+    };
+    dma_set();
+    for (int t = 0; t < kRing - 1; ++t) {
+#pragma unroll
+      for (int u = 0; u < C; ++u) dma_tile(u);
+      dma_advance();
+    }
+
+    f32x16 dkacc[NB], dvacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      dkacc[nb] = 0.0f;
+      dvacc[nb] = 0.0f;
+    }
+    const float cs = a.c;
+    // S and dP - D for two tiles: set X = the tile whose P, dS are being
+    // formed, set Y = the next tile, whose products run meanwhile
+    f32x16 s[2], dp[2];
+    constexpr int kPD = 3;  // LDS fragments run kPD k-steps ahead of the products
+
+    // S = Q K^T and dP = dO V^T for the tile in slot `so` into set Y, the two
+    // accumulation chains interleaved (a single chain would wait out each
+    // product's latency); vec(u) is vector work after product u (0 .. 2KS-1)
+    auto prod = [&](auto y_c, int so, auto&& vec) {
+      constexpr int Y = decltype(y_c)::value;
+      const lchar* rq = lds_opaque(lds_ptr(smem) + so + rrow);
+      const lchar* ro = lds_opaque(lds_ptr(smem) + so + LDO + rrow);
+      u32x4 fq[kPD + 1], fo[kPD + 1];
+#pragma unroll
+      for (int ks = 0; ks < kPD && ks < KS; ++ks) {
+        fq[ks] = ld_row(rq + TL::row_off(0, ks));
+        fo[ks] = ld_row(ro + TL::row_off(0, ks));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + kPD < KS) {
+          fq[(ks + kPD) % (kPD + 1)] = ld_row(rq + TL::row_off(0, ks + kPD));
+          fo[(ks + kPD) % (kPD + 1)] = ld_row(ro + TL::row_off(0, ks + kPD));
+        }
+        const int r = ks % (kPD + 1);
+        if (ks == 0) mfma32_vd<Tag, true, true>(s[Y], fq[r], kreg[0]);
+        else mfma32_vd<Tag, false, true>(s[Y], fq[r], kreg[ks]);
+        vec(2 * ks);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) mfma32_vd<Tag, true, true>(dp[Y], fo[r], vreg[0]);
+        else mfma32_vd<Tag, false, true>(dp[Y], fo[r], vreg[ks]);
+        vec(2 * ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // the first tile's products, then the pipelined sweep
+    vm_wait<2 * C>();
+    __syncthreads();
+    int i = i_first;
+    int so = 0;  // slot of tile i
+    prod(std::integral_constant<int, 0>{}, so, [](int) {});
+    vgpr_drain(s);
+    vgpr_drain(dp);
+
+    // Iteration over tile i (set X) with the next tile in (set Y = 1 - X):
+    //   part A: S, dP of in                   | P, dS of i, DMA
+    //   part B: dV^T, dK^T += ... of i        | DMA
+    auto step = [&](auto x_c, auto mask_c) {
+      constexpr int X = decltype(x_c)::value;
+      constexpr int Y = 1 - X;
+      constexpr bool MASK = decltype(mask_c)::value;
+      const int in = next_tile(i);
+      const int son = slot_next(so);
+      vm_wait<C>();      // tile `in` has landed (for this wave's share) ...
+      wg_barrier();      // ... for every wave; the slot refilled below is free
+      const int q0 = i * BQ;
+      const lchar* base = lds_ptr(smem) + so;
+      // element v holds query q0 + 4g + 8(v/4) + v%4 (and this lane's key);
+      // it is allowed while that offset lies in [lo, hi)
+      const int lo = CAUSAL ? my_k - q0 - 4 * g : -BQ;
+      const int hi = n - q0 - 4 * g;
+      // element v needs the base-2 LSE and D of query 8(v/4) + 4g + v%4: the
+      // LSE by four LDS reads; D by one read of group c32 % 4, the other groups
+      // coming from the lanes of the quad by DPP broadcast folded into the
+      // subtraction that uses them
+      const lchar* ls = lds_opaque(base + LLD + 16 * g);
+      f32x4 lt4[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) lt4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 32 * r4);
+      const f32x4 dq4 = *(const __attribute__((address_space(3))) f32x4*)(ls + 128 + 32 * (c32 & 3));
+      auto ltv = [&](int v) { return lt4[v >> 2][v & 3]; };
+      auto dv = [&](int v) { return quad_bcast(dq4[v & 3], v >> 2); };
+      // P and dS of element v in three stages, software-pipelined so that the
+      // work after each product is three independent operations (a single
+      // element's chain would stall on its own latencies while the matrix
+      // core idles): t = S c - Lt, P = exp2(t), dS = P (dP - D) (+ mask).
+      // The asm pins each finished element here, between the products.
+      auto st1 = [&](int v) { s[X][v] = fmaf(s[X][v], cs, -ltv(v)); };
+      auto st2 = [&](int v) { s[X][v] = fast_exp2(s[X][v]); };
+      auto st3 = [&](int v) {
+        float pp = s[X][v];
+        float x = pp * (dp[X][v] - dv(v));
+        if constexpr (MASK) {
+          const int o = 8 * (v >> 2) + (v & 3);
+          const bool dead = o < lo || o >= hi;
+          pp = dead ? 0.0f : pp;
+          x = dead ? 0.0f : x;
+        }
+        s[X][v] = pp;
+        dp[X][v] = x;
+        asm volatile("" : "+v"(s[X][v]), "+v"(dp[X][v]));
+      };
+      auto staged = [&](int u) {  // after product u: element u enters, u-2 leaves
+        if (u < 16) st1(u);
+        if (u >= 1 && u - 1 < 16) st2(u - 1);
+        if (u >= 2 && u - 2 < 16) st3(u - 2);
+      };
+      constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
+      // ---- part A (16 elements over 2KS products: 1 or 2 per product)
+      prod(std::integral_constant<int, Y>{}, son, [&](int u) {
+        constexpr int R = 16 / (2 * KS);  // elements entering per product
+#pragma unroll
+        for (int e = 0; e < R; ++e) staged(u * R + e);
+#pragma unroll
+        for (int t = 0; t < kDmaA; ++t)
+          if (u == (2 * t + 1) * 2 * KS / (2 * kDmaA)) dma_tile(t);
+      });
+      staged(16);
+      staged(17);
+      u32x4 pb[PK], db[PK];
+#pragma unroll
+      for (int kk = 0; kk < PK; ++kk) {
+        pb[kk] = pack8<Tag>(s[X], 8 * kk);
+        db[kk] = pack8<Tag>(dp[X], 8 * kk);
+      }
+      valu_to_mfma(pb);
+      valu_to_mfma(db);
+      // ---- part B: dV^T += dO^T P, dK^T += Q^T dS (transpose fragments of tile i)
+      const lchar* ot = lds_opaque(base + LDO + rtr);
+      const lchar* qt = lds_opaque(base + rtr);
+      auto trf = [&](const lchar* t, int f) {
+        return ld_tr(t + TL::tr_off(0, f / NB, 0, f % NB), t + TL::tr_off(0, f / NB, 1, f % NB));
+      };
+      u32x4 fo[kPD + 1], fq[kPD + 1];
+#pragma unroll
+      for (int f = 0; f < kPD && f < NF; ++f) {
+        fo[f] = trf(ot, f);
+        fq[f] = trf(qt, f);
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + kPD < NF) {
+          fo[(f + kPD) % (kPD + 1)] = trf(ot, f + kPD);
+          fq[(f + kPD) % (kPD + 1)] = trf(qt, f + kPD);
+        }
+        mfma32_acc<Tag>(dvacc[f % NB], fo[f % (kPD + 1)], pb[f / NB]);
+        mfma32_acc<Tag>(dkacc[f % NB], fq[f % (kPD + 1)], db[f / NB]);
+#pragma unroll
+        for (int t = kDmaA; t < C; ++t)
+          if (f == (2 * (t - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dma_advance();
+      i = in;
+      so = son;
+    };
+
+    // Dense sweeps: the tiles crossing this wave's diagonal come first (an
+    // even number, masked), then an even number without any per-element test,
+    // then the rest (the sequence end), masked and padded to an even count
+    // with a tile past the end (every row dead).  The total is the same for
+    // every wave; two iterations per trip keep the sets X/Y in fixed roles
+    // and the accumulators out of any branch.
+    int n_pre = 0, n_plain = 0;
+    if constexpr (!SPARSE) {
+      const int T = n_tiles - i_first;
+      if constexpr (CAUSAL) n_pre = min((w + 2) & ~1, (T + 1) & ~1);
+      n_plain = max(n / BQ - (i_first + n_pre), 0) & ~1;
+    }
+    for (int t = 0; t < n_pre; t += 2) {
+      step(std::integral_constant<int, 0>{}, std::true_type{});
+      step(std::integral_constant<int, 1>{}, std::true_type{});
+    }
+    for (int t = 0; t < n_plain; t += 2) {
+      step(std::integral_constant<int, 0>{}, std::false_type{});
+      step(std::integral_constant<int, 1>{}, std::false_type{});
+    }
+    while (i < n_tiles) {
+      step(std::integral_constant<int, 0>{}, std::true_type{});
+      step(std::integral_constant<int, 1>{}, std::true_type{});
+    }
+
+    agpr_drain(dkacc);
+    agpr_drain(dvacc);
     if (my_k < n) {
       uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
       uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
-      for (int c = 8 * g; c < D; c += 16) {
-        *reinterpret_cast<u32x4*>(dkp + c) = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(dvp + c) = u32x4{0u, 0u, 0u, 0u};
-      }
+      const float sc = a.scale;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 pk, pv;
+          pk[0] = pack2<Tag>(dkacc[nb][4 * r] * sc, dkacc[nb][4 * r + 1] * sc);
+          pk[1] = pack2<Tag>(dkacc[nb][4 * r + 2] * sc, dkacc[nb][4 * r + 3] * sc);
+          pv[0] = pack2<Tag>(dvacc[nb][4 * r], dvacc[nb][4 * r + 1]);
+          pv[1] = pack2<Tag>(dvacc[nb][4 * r + 2], dvacc[nb][4 * r + 3]);
+          *reinterpret_cast<u32x2*>(dkp + 32 * nb + 8 * r + 4 * g) = pk;
+          *reinterpret_cast<u32x2*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
+        }
     }
-    return;
-  }
-
-  QD qd;  // Q and dO tiles share one geometry
-  qd.init(w, lane);
-  // DMA instruction t (of C) of tile it into the slot at byte offset so:
-  // Q and dO share the tile geometry; the last one moves the tile's base-2
-  // LSE (lanes 0-7) and D (lanes 8-15), four rows per lane.  A lane whose
-  // rows start past the end reads the last row instead (those rows are
-  // dead); one that straddles the end reads up to 3 floats past it, which
-  // the workspace's spare bytes cover.
-  // (The addressing of the tile being loaded is set once per tile, in
-  // dma_set() below.)
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
-  const uint16_t* d_q = Qg;
-  const uint16_t* d_o = dOg;
-  const float* d_ld = Ltg;  // this lane's L or D source (lanes 0-15)
-  int d_last = 0;
-  uint32_t d_lds = 0, d_slot = 0;
-  const int rrow = TL::row_base(c32, g);
-  const int rtr = TL::tr_base(lane);
-  auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
-
-  // Every iteration issues exactly C DMA instructions (past the last tile
-  // they reload the first tile into a slot nobody reads), so "tile t+1 has
-  // landed" is always vmcnt <= C at the top of iteration t.
-  int iq = i_first;  // next tile to load
-  int sq = 0;        // its slot
-  auto dma_set = [&]() {
-    const int it = iq < n_tiles ? iq : i_first;
-    d_q = Qg + (size_t)it * BQ * D;
-    d_o = dOg + (size_t)it * BQ * D;
-    d_last = n - 1 - it * BQ;
-    d_slot = lds_base + sq;
-    d_lds = d_slot + 1024 * w;
-    d_ld = (lane < 8 ? Ltg : Dg) + min(it * BQ + 4 * (lane & 7), n - 1);
-  };
-  auto dma_tile = [&](int t) {
-    if (t < QD::kPer) qd.issue_at(t, d_q, d_last, d_lds);
-    else if (t < 2 * QD::kPer) qd.issue_at(t - QD::kPer, d_o, d_last, d_lds + LDO);
-    else if (lane < 16) dma16(d_ld, d_slot + LLD);
-  };
-  auto dma_advance = [&]() {
-    if (iq < n_tiles) iq = next_tile(iq);
-    sq = slot_next(sq);
-    dma_set();
-  };
-  dma_set();
-  for (int t = 0; t < kRing - 1; ++t) {
-#pragma unroll
-    for (int u = 0; u < C; ++u) dma_tile(u);
-    dma_advance();
-  }
-
-  f32x16 dkacc[NB], dvacc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    dkacc[nb] = 0.0f;
-    dvacc[nb] = 0.0f;
-  }
-  const float cs = a.c;
-  // S and dP - D for two tiles: set X = the tile whose P, dS are being
-  // formed, set Y = the next tile, whose products run meanwhile
-  f32x16 s[2], dp[2];
-  constexpr int kPD = 3;  // LDS fragments run kPD k-steps ahead of the products
-
-  // S = Q K^T and dP = dO V^T for the tile in slot `so` into set Y, the two
-  // accumulation chains interleaved (a single chain would wait out each
-  // product's latency); vec(u) is vector work after product u (0 .. 2KS-1)
-  auto prod = [&](auto y_c, int so, auto&& vec) {
-    constexpr int Y = decltype(y_c)::value;
-    const lchar* rq = lds_opaque(lds_ptr(smem) + so + rrow);
-    const lchar* ro = lds_opaque(lds_ptr(smem) + so + LDO + rrow);
-    u32x4 fq[kPD + 1], fo[kPD + 1];
-#pragma unroll
-    for (int ks = 0; ks < kPD && ks < KS; ++ks) {
-      fq[ks] = ld_row(rq + TL::row_off(0, ks));
-      fo[ks] = ld_row(ro + TL::row_off(0, ks));
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + kPD < KS) {
-        fq[(ks + kPD) % (kPD + 1)] = ld_row(rq + TL::row_off(0, ks + kPD));
-        fo[(ks + kPD) % (kPD + 1)] = ld_row(ro + TL::row_off(0, ks + kPD));
-      }
-      const int r = ks % (kPD + 1);
-      if (ks == 0) mfma32_vd<Tag, true, true>(s[Y], fq[r], kreg[0]);
-      else mfma32_vd<Tag, false, true>(s[Y], fq[r], kreg[ks]);
-      vec(2 * ks);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks == 0) mfma32_vd<Tag, true, true>(dp[Y], fo[r], vreg[0]);
-      else mfma32_vd<Tag, false, true>(dp[Y], fo[r], vreg[ks]);
-      vec(2 * ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // the first tile's products, then the pipelined sweep
-  vm_wait<2 * C>();
-  __syncthreads();
-  int i = i_first;
-  int so = 0;  // slot of tile i
-  prod(std::integral_constant<int, 0>{}, so, [](int) {});
-  vgpr_drain(s);
-  vgpr_drain(dp);
-
-  // Iteration over tile i (set X) with the next tile in (set Y = 1 - X):
-  //   part A: S, dP of in                   | P, dS of i, DMA
-  //   part B: dV^T, dK^T += ... of i        | DMA
-  auto step = [&](auto x_c, auto mask_c) {
-    constexpr int X = decltype(x_c)::value;
-    constexpr int Y = 1 - X;
-    constexpr bool MASK = decltype(mask_c)::value;
-    const int in = next_tile(i);
-    const int son = slot_next(so);
-    vm_wait<C>();      // tile `in` has landed (for this wave's share) ...
-    wg_barrier();      // ... for every wave; the slot refilled below is free
-    const int q0 = i * BQ;
-    const lchar* base = lds_ptr(smem) + so;
-    // element v holds query q0 + 4g + 8(v/4) + v%4 (and this lane's key);
-    // it is allowed while that offset lies in [lo, hi)
-    const int lo = CAUSAL ? my_k - q0 - 4 * g : -BQ;
-    const int hi = n - q0 - 4 * g;
-    // element v needs the base-2 LSE and D of query 8(v/4) + 4g + v%4: the
-    // LSE by four LDS reads; D by one read of group c32 % 4, the other groups
-    // coming from the lanes of the quad by DPP broadcast folded into the
-    // subtraction that uses them
-    const lchar* ls = lds_opaque(base + LLD + 16 * g);
-    f32x4 lt4[4];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) lt4[r4] = *(const __attribute__((address_space(3))) f32x4*)(ls + 32 * r4);
-    const f32x4 dq4 = *(const __attribute__((address_space(3))) f32x4*)(ls + 128 + 32 * (c32 & 3));
-    auto ltv = [&](int v) { return lt4[v >> 2][v & 3]; };
-    auto dv = [&](int v) { return quad_bcast(dq4[v & 3], v >> 2); };
-    // P and dS of element v in three stages, software-pipelined so that the
-    // work after each product is three independent operations (a single
-    // element's chain would stall on its own latencies while the matrix
-    // core idles): t = S c - Lt, P = exp2(t), dS = P (dP - D) (+ mask).
-    // The asm pins each finished element here, between the products.
-    auto st1 = [&](int v) { s[X][v] = fmaf(s[X][v], cs, -ltv(v)); };
-    auto st2 = [&](int v) { s[X][v] = fast_exp2(s[X][v]); };
-    auto st3 = [&](int v) {
-      float pp = s[X][v];
-      float x = pp * (dp[X][v] - dv(v));
-      if constexpr (MASK) {
-        const int o = 8 * (v >> 2) + (v & 3);
-        const bool dead = o < lo || o >= hi;
-        pp = dead ? 0.0f : pp;
-        x = dead ? 0.0f : x;
-      }
-      s[X][v] = pp;
-      dp[X][v] = x;
-      asm volatile("" : "+v"(s[X][v]), "+v"(dp[X][v]));
-    };
-    auto staged = [&](int u) {  // after product u: element u enters, u-2 leaves
-      if (u < 16) st1(u);
-      if (u >= 1 && u - 1 < 16) st2(u - 1);
-      if (u >= 2 && u - 2 < 16) st3(u - 2);
-    };
-    constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
-    // ---- part A (16 elements over 2KS products: 1 or 2 per product)
-    prod(std::integral_constant<int, Y>{}, son, [&](int u) {
-      constexpr int R = 16 / (2 * KS);  // elements entering per product
-#pragma unroll
-      for (int e = 0; e < R; ++e) staged(u * R + e);
-#pragma unroll
-      for (int t = 0; t < kDmaA; ++t)
-        if (u == (2 * t + 1) * 2 * KS / (2 * kDmaA)) dma_tile(t);
-    });
-    staged(16);
-    staged(17);
-    u32x4 pb[PK], db[PK];
-#pragma unroll
-    for (int kk = 0; kk < PK; ++kk) {
-      pb[kk] = pack8<Tag>(s[X], 8 * kk);
-      db[kk] = pack8<Tag>(dp[X], 8 * kk);
-    }
-    valu_to_mfma(pb);
-    valu_to_mfma(db);
-    // ---- part B: dV^T += dO^T P, dK^T += Q^T dS (transpose fragments of tile i)
-    const lchar* ot = lds_opaque(base + LDO + rtr);
-    const lchar* qt = lds_opaque(base + rtr);
-    auto trf = [&](const lchar* t, int f) {
-      return ld_tr(t + TL::tr_off(0, f / NB, 0, f % NB), t + TL::tr_off(0, f / NB, 1, f % NB));
-    };
-    u32x4 fo[kPD + 1], fq[kPD + 1];
-#pragma unroll
-    for (int f = 0; f < kPD && f < NF; ++f) {
-      fo[f] = trf(ot, f);
-      fq[f] = trf(qt, f);
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f + kPD < NF) {
-        fo[(f + kPD) % (kPD + 1)] = trf(ot, f + kPD);
-        fq[(f + kPD) % (kPD + 1)] = trf(qt, f + kPD);
-      }
-      mfma32_acc<Tag>(dvacc[f % NB], fo[f % (kPD + 1)], pb[f / NB]);
-      mfma32_acc<Tag>(dkacc[f % NB], fq[f % (kPD + 1)], db[f / NB]);
-#pragma unroll
-      for (int t = kDmaA; t < C; ++t)
-        if (f == (2 * (t - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    dma_advance();
-    i = in;
-    so = son;
-  };
-
-  // Dense sweeps: the tiles crossing this wave's diagonal come first (an
-  // even number, masked), then an even number without any per-element test,
-  // then the rest (the sequence end), masked and padded to an even count
-  // with a tile past the end (every row dead).  The total is the same for
-  // every wave; two iterations per trip keep the sets X/Y in fixed roles
-  // and the accumulators out of any branch.
-  int n_pre = 0, n_plain = 0;
-  if constexpr (!SPARSE) {
-    const int T = n_tiles - i_first;
-    if constexpr (CAUSAL) n_pre = min((w + 2) & ~1, (T + 1) & ~1);
-    n_plain = max(n / BQ - (i_first + n_pre), 0) & ~1;
-  }
-  for (int t = 0; t < n_pre; t += 2) {
-    step(std::integral_constant<int, 0>{}, std::true_type{});
-    step(std::integral_constant<int, 1>{}, std::true_type{});
-  }
-  for (int t = 0; t < n_plain; t += 2) {
-    step(std::integral_constant<int, 0>{}, std::false_type{});
-    step(std::integral_constant<int, 1>{}, std::false_type{});
-  }
-  while (i < n_tiles) {
-    step(std::integral_constant<int, 0>{}, std::true_type{});
-    step(std::integral_constant<int, 1>{}, std::true_type{});
-  }
-
-  agpr_drain(dkacc);
-  agpr_drain(dvacc);
-  if (my_k < n) {
-    uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
-    uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
-    const float sc = a.scale;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 pk, pv;
-        pk[0] = pack2<Tag>(dkacc[nb][4 * r] * sc, dkacc[nb][4 * r + 1] * sc);
-        pk[1] = pack2<Tag>(dkacc[nb][4 * r + 2] * sc, dkacc[nb][4 * r + 3] * sc);
-        pv[0] = pack2<Tag>(dvacc[nb][4 * r], dvacc[nb][4 * r + 1]);
-        pv[1] = pack2<Tag>(dvacc[nb][4 * r + 2], dvacc[nb][4 * r + 3]);
-        *reinterpret_cast<u32x2*>(dkp + 32 * nb + 8 * r + 4 * g) = pk;
-        *reinterpret_cast<u32x2*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
-      }
-  }
   };
   const int kb2 = a.nkb - 1 - pk_;
   const int nrun = (CAUSAL && pk_ != kb2) ? 2 : 1;
@@ -521,293 +521,293 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       if constexpr (SPARSE)
         while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
       return j;
-  };
-  // tiles of this wave's queries that have allowed keys
-  auto live = [&](int jt) {
-    bool l = jt < j_end;
-    if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + 63);
-    if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
-    return l;
-  };
+    };
+    // tiles of this wave's queries that have allowed keys
+    auto live = [&](int jt) {
+      bool l = jt < j_end;
+      if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + 63);
+      if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
+      return l;
+    };
 
-  KD kd;
-  VD vd;
-  kd.init(w, lane);
-  vd.init(w, lane);
-  const int krow = KL::row_base(c32, g);
-  const int ktr = KL::tr_base(lane);
-  const int vrow = KD::kSlot + VL::row_base(c32, g);
-  auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
+    KD kd;
+    VD vd;
+    kd.init(w, lane);
+    vd.init(w, lane);
+    const int krow = KL::row_base(c32, g);
+    const int ktr = KL::tr_base(lane);
+    const int vrow = KD::kSlot + VL::row_base(c32, g);
+    auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
 
-  vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
+    vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
 
-  const int j_first = SPARSE ? next_tile(-1) : 0;
-  if (j_first >= j_end) {  // no key tile at all: dQ = 0
+    const int j_first = SPARSE ? next_tile(-1) : 0;
+    if (j_first >= j_end) {  // no key tile at all: dQ = 0
+      for (int h = 0; h < 2; ++h) {
+        const int my_q = qw0 + 32 * h + c32;
+        if (my_q < n) {
+          uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
+          for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(dqp + c) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      return;
+    }
+    // Every iteration issues exactly C DMA instructions (past the last tile
+    // they reload the first tile into a slot nobody reads), so "tile t+1 has
+    // landed" is always vmcnt <= C at the top of iteration t.
+    int jq = j_first;  // next tile to load
+    int sq = 0;        // its slot
+    // its addressing, set once per tile: K and V rows, last valid row, LDS
+    // address of this wave's share
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+    const uint16_t* dk = Kg;
+    const uint16_t* dv = Vg;
+    int d_last = 0;
+    uint32_t d_lds = 0;
+    auto dma_set = [&]() {
+      const int jt = jq < j_end ? jq : j_first;
+      dk = Kg + (size_t)jt * BC * D;
+      dv = Vg + (size_t)jt * BC * D;
+      d_last = n - 1 - jt * BC;
+      d_lds = lds_base + sq + 1024 * w;
+    };
+    // DMA instruction i (of C) of the tile
+    auto dma_tile = [&](int i) {
+      if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
+      else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
+    };
+    auto dma_advance = [&]() {
+      if (jq < j_end) jq = next_tile(jq);
+      sq = slot_next(sq);
+      dma_set();
+    };
+    dma_set();
+    for (int t = 0; t < kRing - 1; ++t) {
+#pragma unroll
+      for (int i = 0; i < C; ++i) dma_tile(i);
+      dma_advance();
+    }
+
+    f32x16 acc[2][MB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
+    const float cs = a.c;
+    // S^T and dP^T - D of both blocks for two tiles: set X = the tile whose
+    // dS is being formed, set Y = the next tile, whose products run meanwhile
+    f32x16 s[2][2], dp[2][2];
+    constexpr int kPD = 6;  // LDS fragments run kPD k-steps ahead of the products
+
+    // One product of both blocks for the tile in slot `so` into set Y: S^T =
+    // K Q^T (P = false, K rows) or dP^T - D = V dO^T (P = true, V rows).
+    // Each fragment feeds both blocks; vec(ks) is vector work interleaved per
+    // k-step.  S^T and dP^T run as two sweeps so that set Y's dP^T registers
+    // are only needed once half of set X has been consumed.
+    auto prod = [&](auto y_c, auto p_c, int so, bool on, auto&& vec) {
+      constexpr int Y = decltype(y_c)::value;
+      constexpr bool P = decltype(p_c)::value;
+      const lchar* rows = lds_opaque(lds_ptr(smem) + so + (P ? vrow : krow));
+      u32x4 fr[kPD + 1];
+      auto rd = [&](int ks) { return P ? ld_row(rows + VL::row_off(0, ks)) : ld_row(rows + KL::row_off(0, ks)); };
+      if (on) {
+#pragma unroll
+        for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd(ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (on) {
+          if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd(ks + kPD);
+          const u32x4 f = fr[ks % (kPD + 1)];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            f32x16& d = P ? dp[Y][h] : s[Y][h];
+            const u32x4 b = P ? oreg[h][ks] : qreg[h][ks];
+            if (ks == 0) {
+              if (P) mfma32_vc<Tag>(d, f, b, negD[h]);  // dP^T - D accumulates from -D
+              else mfma32_vd<Tag, true, true>(d, f, b);
+            } else {
+              mfma32_vd<Tag, false, true>(d, f, b);
+            }
+            // each product is followed by its share of vector work, so the
+            // next product issues as the matrix core frees up
+            vec(2 * ks + h);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          vec(2 * ks);
+          vec(2 * ks + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    auto sdp = [&](auto y_c, int so, bool on) {
+      prod(y_c, std::false_type{}, so, on, [](int) {});
+      prod(y_c, std::true_type{}, so, on, [](int) {});
+    };
+
+    // the first tile's products, then the pipelined sweep
+    vm_wait<2 * C>();
+    __syncthreads();
+    int j = j_first;
+    int so = 0;  // slot of tile j
+    sdp(std::integral_constant<int, 0>{}, so, !SPARSE || live(j));
+    vgpr_drain(s[0]);
+    vgpr_drain(dp[0]);
+
+    // Iteration over tile j (set X) with the next tile jn (set Y = 1 - X):
+    //   part A: S^T, dP^T of (jn, both blocks)  | dS of (j, both blocks), DMA
+    //   part B: dQ^T += K^T dS^T of (j, both blocks), DMA
+    // The body is unrolled for X = 0 and X = 1.  The tile count is the
+    // workgroup's, so every wave runs every iteration (barrier per iteration):
+    // keys past a query's diagonal or the sequence end get dS = 0.
+    auto step = [&](auto x_c, auto mask_c) {
+      constexpr int X = decltype(x_c)::value;
+      constexpr int Y = 1 - X;
+      constexpr bool MASK = decltype(mask_c)::value;
+      const int jn = next_tile(j);
+      const int son = slot_next(so);
+      vm_wait<C>();      // tile jn has landed (for this wave's share) ...
+      wg_barrier();      // ... for every wave; the slot refilled below is free
+      // dense sweeps compute every tile, the dummy one included: its keys lie
+      // past the sequence end, so the mask gives dS = 0, and its slot holds a
+      // valid reload; branches here would cost fetch bubbles a lone wave
+      // cannot hide
+      const bool live_j = SPARSE ? live(j) : true;
+      const bool live_n = SPARSE ? live(jn) : true;
+      const int k0 = j * BC;
+      // element v of block h holds key k0 + 4g + 8(v/4) + v%4; it is allowed
+      // while that offset is at most lim[h]
+      int lim[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int last = n - 1;
+        if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+        lim[h] = last - k0 - 4 * g;
+      }
+      constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
+      // ---- part A
+      u32x4 db[2][PK];
+      // dS^T of block h, elements v0..v1-1, then packed once the block is done
+      // dS^T of element e (block e/16, row e%16) in three stages, software-
+      // pipelined so the vector work after each product is independent
+      // operations (one element's chain alone would stall on its latencies
+      // while the matrix core idles): t = S^T c - L, P = exp2(t),
+      // dS = P (dP^T - D) (+ mask).  The asm pins each finished element here,
+      // between the products; a block's dS^T is packed once complete.
+      auto st1 = [&](int e) { s[X][e >> 4][e & 15] = fmaf(s[X][e >> 4][e & 15], cs, -Lq[e >> 4]); };
+      auto st2 = [&](int e) { s[X][e >> 4][e & 15] = fast_exp2(s[X][e >> 4][e & 15]); };
+      auto st3 = [&](int e) {
+        const int h = e >> 4, v = e & 15;
+        float x = s[X][h][v] * dp[X][h][v];
+        if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
+        dp[X][h][v] = x;
+        asm volatile("" : "+v"(dp[X][h][v]));
+        if (v == 15) {
+#pragma unroll
+          for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[X][h], 8 * kk);
+        }
+      };
+      // (runs whether or not the tile is live: a skipped tile's registers hold
+      // stale finite values and its dS^T is replaced by zeros below, which
+      // keeps branches out of the product sequence)
+      auto staged = [&](int t) {  // element t enters, t-2 leaves
+        if (t < 32) st1(t);
+        if (t >= 1 && t - 1 < 32) st2(t - 1);
+        if (t >= 2 && t - 2 < 32) st3(t - 2);
+      };
+      // slot u = 0 .. 2KS-1 of a sweep: the product of k-step u/2, block u%2
+      auto dma_a = [&](int u, int half) {
+#pragma unroll
+        for (int q = 0; q < kDmaA; ++q)
+          if (half * 2 * KS + u == (2 * q + 1) * 2 * KS / kDmaA) dma_tile(q);
+      };
+      constexpr int R = 32 / (4 * KS);  // elements entering per product
+      prod(std::integral_constant<int, Y>{}, std::false_type{}, son, live_n, [&](int u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) staged(u * R + r);
+        dma_a(u, 0);
+      });
+      prod(std::integral_constant<int, Y>{}, std::true_type{}, son, live_n, [&](int u) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) staged((2 * KS + u) * R + r);
+        dma_a(u, 1);
+      });
+      staged(32);
+      staged(33);
+      if (!live_j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int kk = 0; kk < PK; ++kk) db[h][kk] = u32x4{0u, 0u, 0u, 0u};
+      }
+      valu_to_mfma(db[0]);
+      valu_to_mfma(db[1]);
+      // ---- part B
+      const lchar* kt = lds_opaque(lds_ptr(smem) + so + ktr);
+      u32x4 kq[kPD + 1];
+#pragma unroll
+      for (int f = 0; f < kPD && f < NF; ++f)
+        kq[f] = ld_tr(kt + KL::tr_off(0, f / MB, 0, f % MB), kt + KL::tr_off(0, f / MB, 1, f % MB));
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + kPD < NF) {
+          const int fn = f + kPD;
+          kq[fn % (kPD + 1)] = ld_tr(kt + KL::tr_off(0, fn / MB, 0, fn % MB), kt + KL::tr_off(0, fn / MB, 1, fn % MB));
+        }
+        mfma32_acc<Tag>(acc[0][f % MB], kq[f % (kPD + 1)], db[0][f / MB]);
+        mfma32_acc<Tag>(acc[1][f % MB], kq[f % (kPD + 1)], db[1][f / MB]);
+#pragma unroll
+        for (int q = kDmaA; q < C; ++q)
+          if (f == (2 * (q - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dma_advance();
+      j = jn;
+      so = son;
+    };
+    // Two iterations per trip: with an odd tile count the last iteration runs
+    // on no tile (dS = 0, its slot holds a valid reload), so the register sets
+    // X/Y keep fixed roles and the accumulators never sit in a branch (which
+    // would make the register allocator copy them every iteration).
+    // Dense sweeps start with the tiles no key of which is masked for this
+    // wave (keys below its diagonal and inside the sequence), an even number
+    // of them, without any per-element test; the rest, padded to an even
+    // count, run with the mask.  The total is the same for every wave.
+    int n_plain = 0;
+    if constexpr (!SPARSE) {
+      int jm = n / BC;                       // first tile reaching past the sequence end
+      if constexpr (CAUSAL) jm = min(jm, qw0 / BC);  // first tile crossing the diagonal
+      n_plain = max(jm - j_first, 0) & ~1;
+    }
+    for (int t = 0; t < n_plain; t += 2) {
+      step(std::integral_constant<int, 0>{}, std::false_type{});
+      step(std::integral_constant<int, 1>{}, std::false_type{});
+    }
+    while (j < j_end) {
+      step(std::integral_constant<int, 0>{}, std::true_type{});
+      step(std::integral_constant<int, 1>{}, std::true_type{});
+    }
+
+    agpr_drain(acc[0]);
+    agpr_drain(acc[1]);
+    const float sc = a.scale;
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int my_q = qw0 + 32 * h + c32;
       if (my_q < n) {
         uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
-        for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(dqp + c) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    return;
-  }
-  // Every iteration issues exactly C DMA instructions (past the last tile
-  // they reload the first tile into a slot nobody reads), so "tile t+1 has
-  // landed" is always vmcnt <= C at the top of iteration t.
-  int jq = j_first;  // next tile to load
-  int sq = 0;        // its slot
-  // its addressing, set once per tile: K and V rows, last valid row, LDS
-  // address of this wave's share
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
-  const uint16_t* dk = Kg;
-  const uint16_t* dv = Vg;
-  int d_last = 0;
-  uint32_t d_lds = 0;
-  auto dma_set = [&]() {
-    const int jt = jq < j_end ? jq : j_first;
-    dk = Kg + (size_t)jt * BC * D;
-    dv = Vg + (size_t)jt * BC * D;
-    d_last = n - 1 - jt * BC;
-    d_lds = lds_base + sq + 1024 * w;
-  };
-  // DMA instruction i (of C) of the tile
-  auto dma_tile = [&](int i) {
-    if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
-    else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
-  };
-  auto dma_advance = [&]() {
-    if (jq < j_end) jq = next_tile(jq);
-    sq = slot_next(sq);
-    dma_set();
-  };
-  dma_set();
-  for (int t = 0; t < kRing - 1; ++t) {
 #pragma unroll
-    for (int i = 0; i < C; ++i) dma_tile(i);
-    dma_advance();
-  }
-
-  f32x16 acc[2][MB];
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
-  const float cs = a.c;
-  // S^T and dP^T - D of both blocks for two tiles: set X = the tile whose
-  // dS is being formed, set Y = the next tile, whose products run meanwhile
-  f32x16 s[2][2], dp[2][2];
-  constexpr int kPD = 6;  // LDS fragments run kPD k-steps ahead of the products
-
-  // One product of both blocks for the tile in slot `so` into set Y: S^T =
-  // K Q^T (P = false, K rows) or dP^T - D = V dO^T (P = true, V rows).
-  // Each fragment feeds both blocks; vec(ks) is vector work interleaved per
-  // k-step.  S^T and dP^T run as two sweeps so that set Y's dP^T registers
-  // are only needed once half of set X has been consumed.
-  auto prod = [&](auto y_c, auto p_c, int so, bool on, auto&& vec) {
-    constexpr int Y = decltype(y_c)::value;
-    constexpr bool P = decltype(p_c)::value;
-    const lchar* rows = lds_opaque(lds_ptr(smem) + so + (P ? vrow : krow));
-    u32x4 fr[kPD + 1];
-    auto rd = [&](int ks) { return P ? ld_row(rows + VL::row_off(0, ks)) : ld_row(rows + KL::row_off(0, ks)); };
-    if (on) {
-#pragma unroll
-      for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd(ks);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (on) {
-        if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd(ks + kPD);
-        const u32x4 f = fr[ks % (kPD + 1)];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x16& d = P ? dp[Y][h] : s[Y][h];
-          const u32x4 b = P ? oreg[h][ks] : qreg[h][ks];
-          if (ks == 0) {
-            if (P) mfma32_vc<Tag>(d, f, b, negD[h]);  // dP^T - D accumulates from -D
-            else mfma32_vd<Tag, true, true>(d, f, b);
-          } else {
-            mfma32_vd<Tag, false, true>(d, f, b);
+          for (int r = 0; r < 4; ++r) {
+            u32x2 pk;
+            pk[0] = pack2<Tag>(acc[h][mb][4 * r] * sc, acc[h][mb][4 * r + 1] * sc);
+            pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * sc, acc[h][mb][4 * r + 3] * sc);
+            *reinterpret_cast<u32x2*>(dqp + 32 * mb + 8 * r + 4 * g) = pk;
           }
-          // each product is followed by its share of vector work, so the
-          // next product issues as the matrix core frees up
-          vec(2 * ks + h);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        vec(2 * ks);
-        vec(2 * ks + 1);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  };
-  auto sdp = [&](auto y_c, int so, bool on) {
-    prod(y_c, std::false_type{}, so, on, [](int) {});
-    prod(y_c, std::true_type{}, so, on, [](int) {});
-  };
-
-  // the first tile's products, then the pipelined sweep
-  vm_wait<2 * C>();
-  __syncthreads();
-  int j = j_first;
-  int so = 0;  // slot of tile j
-  sdp(std::integral_constant<int, 0>{}, so, !SPARSE || live(j));
-  vgpr_drain(s[0]);
-  vgpr_drain(dp[0]);
-
-  // Iteration over tile j (set X) with the next tile jn (set Y = 1 - X):
-  //   part A: S^T, dP^T of (jn, both blocks)  | dS of (j, both blocks), DMA
-  //   part B: dQ^T += K^T dS^T of (j, both blocks), DMA
-  // The body is unrolled for X = 0 and X = 1.  The tile count is the
-  // workgroup's, so every wave runs every iteration (barrier per iteration):
-  // keys past a query's diagonal or the sequence end get dS = 0.
-  auto step = [&](auto x_c, auto mask_c) {
-    constexpr int X = decltype(x_c)::value;
-    constexpr int Y = 1 - X;
-    constexpr bool MASK = decltype(mask_c)::value;
-    const int jn = next_tile(j);
-    const int son = slot_next(so);
-    vm_wait<C>();      // tile jn has landed (for this wave's share) ...
-    wg_barrier();      // ... for every wave; the slot refilled below is free
-    // dense sweeps compute every tile, the dummy one included: its keys lie
-    // past the sequence end, so the mask gives dS = 0, and its slot holds a
-    // valid reload; branches here would cost fetch bubbles a lone wave
-    // cannot hide
-    const bool live_j = SPARSE ? live(j) : true;
-    const bool live_n = SPARSE ? live(jn) : true;
-    const int k0 = j * BC;
-    // element v of block h holds key k0 + 4g + 8(v/4) + v%4; it is allowed
-    // while that offset is at most lim[h]
-    int lim[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int last = n - 1;
-      if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
-      lim[h] = last - k0 - 4 * g;
-    }
-    constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
-    // ---- part A
-    u32x4 db[2][PK];
-    // dS^T of block h, elements v0..v1-1, then packed once the block is done
-    // dS^T of element e (block e/16, row e%16) in three stages, software-
-    // pipelined so the vector work after each product is independent
-    // operations (one element's chain alone would stall on its latencies
-    // while the matrix core idles): t = S^T c - L, P = exp2(t),
-    // dS = P (dP^T - D) (+ mask).  The asm pins each finished element here,
-    // between the products; a block's dS^T is packed once complete.
-    auto st1 = [&](int e) { s[X][e >> 4][e & 15] = fmaf(s[X][e >> 4][e & 15], cs, -Lq[e >> 4]); };
-    auto st2 = [&](int e) { s[X][e >> 4][e & 15] = fast_exp2(s[X][e >> 4][e & 15]); };
-    auto st3 = [&](int e) {
-      const int h = e >> 4, v = e & 15;
-      float x = s[X][h][v] * dp[X][h][v];
-      if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
-      dp[X][h][v] = x;
-      asm volatile("" : "+v"(dp[X][h][v]));
-      if (v == 15) {
-#pragma unroll
-        for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[X][h], 8 * kk);
-      }
-    };
-    // (runs whether or not the tile is live: a skipped tile's registers hold
-    // stale finite values and its dS^T is replaced by zeros below, which
-    // keeps branches out of the product sequence)
-    auto staged = [&](int t) {  // element t enters, t-2 leaves
-      if (t < 32) st1(t);
-      if (t >= 1 && t - 1 < 32) st2(t - 1);
-      if (t >= 2 && t - 2 < 32) st3(t - 2);
-    };
-    // slot u = 0 .. 2KS-1 of a sweep: the product of k-step u/2, block u%2
-    auto dma_a = [&](int u, int half) {
-#pragma unroll
-      for (int q = 0; q < kDmaA; ++q)
-        if (half * 2 * KS + u == (2 * q + 1) * 2 * KS / kDmaA) dma_tile(q);
-    };
-    constexpr int R = 32 / (4 * KS);  // elements entering per product
-    prod(std::integral_constant<int, Y>{}, std::false_type{}, son, live_n, [&](int u) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) staged(u * R + r);
-      dma_a(u, 0);
-    });
-    prod(std::integral_constant<int, Y>{}, std::true_type{}, son, live_n, [&](int u) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) staged((2 * KS + u) * R + r);
-      dma_a(u, 1);
-    });
-    staged(32);
-    staged(33);
-    if (!live_j) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kk = 0; kk < PK; ++kk) db[h][kk] = u32x4{0u, 0u, 0u, 0u};
-    }
-    valu_to_mfma(db[0]);
-    valu_to_mfma(db[1]);
-    // ---- part B
-    const lchar* kt = lds_opaque(lds_ptr(smem) + so + ktr);
-    u32x4 kq[kPD + 1];
-#pragma unroll
-    for (int f = 0; f < kPD && f < NF; ++f)
-      kq[f] = ld_tr(kt + KL::tr_off(0, f / MB, 0, f % MB), kt + KL::tr_off(0, f / MB, 1, f % MB));
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f + kPD < NF) {
-        const int fn = f + kPD;
-        kq[fn % (kPD + 1)] = ld_tr(kt + KL::tr_off(0, fn / MB, 0, fn % MB), kt + KL::tr_off(0, fn / MB, 1, fn % MB));
-      }
-      mfma32_acc<Tag>(acc[0][f % MB], kq[f % (kPD + 1)], db[0][f / MB]);
-      mfma32_acc<Tag>(acc[1][f % MB], kq[f % (kPD + 1)], db[1][f / MB]);
-#pragma unroll
-      for (int q = kDmaA; q < C; ++q)
-        if (f == (2 * (q - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    dma_advance();
-    j = jn;
-    so = son;
-  };
-  // Two iterations per trip: with an odd tile count the last iteration runs
-  // on no tile (dS = 0, its slot holds a valid reload), so the register sets
-  // X/Y keep fixed roles and the accumulators never sit in a branch (which
-  // would make the register allocator copy them every iteration).
-  // Dense sweeps start with the tiles no key of which is masked for this
-  // wave (keys below its diagonal and inside the sequence), an even number
-  // of them, without any per-element test; the rest, padded to an even
-  // count, run with the mask.  The total is the same for every wave.
-  int n_plain = 0;
-  if constexpr (!SPARSE) {
-    int jm = n / BC;                       // first tile reaching past the sequence end
-    if constexpr (CAUSAL) jm = min(jm, qw0 / BC);  // first tile crossing the diagonal
-    n_plain = max(jm - j_first, 0) & ~1;
-  }
-  for (int t = 0; t < n_plain; t += 2) {
-    step(std::integral_constant<int, 0>{}, std::false_type{});
-    step(std::integral_constant<int, 1>{}, std::false_type{});
-  }
-  while (j < j_end) {
-    step(std::integral_constant<int, 0>{}, std::true_type{});
-    step(std::integral_constant<int, 1>{}, std::true_type{});
-  }
-
-  agpr_drain(acc[0]);
-  agpr_drain(acc[1]);
-  const float sc = a.scale;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int my_q = qw0 + 32 * h + c32;
-    if (my_q < n) {
-      uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x2 pk;
-          pk[0] = pack2<Tag>(acc[h][mb][4 * r] * sc, acc[h][mb][4 * r + 1] * sc);
-          pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * sc, acc[h][mb][4 * r + 3] * sc);
-          *reinterpret_cast<u32x2*>(dqp + 32 * mb + 8 * r + 4 * g) = pk;
-        }
-    }
-  }
   };
   const int qa = a.nqb - 1 - pq_;  // the longer block first
   const int nrun = (CAUSAL && pq_ != qa) ? 2 : 1;

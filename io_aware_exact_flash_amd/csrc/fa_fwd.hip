@@ -117,354 +117,354 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       if constexpr (SPARSE)
         while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
       return j;
-  };
-  // tiles of this wave's queries that have allowed keys
-  auto live = [&](int jt) {
-    bool l = jt < j_end;
-    if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + kWQ - 1);
-    if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
-    return l;
-  };
-  // Element v of block h of tile jt holds key jt*BC + 4g + 8(v/4) + v%4; it
-  // is allowed while 8(v/4) + v%4 is at most lim[h].
-  auto limits = [&](int jt, int (&lim)[2]) {
-    const bool lv = SPARSE ? live(jt) : true;
+    };
+    // tiles of this wave's queries that have allowed keys
+    auto live = [&](int jt) {
+      bool l = jt < j_end;
+      if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + kWQ - 1);
+      if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
+      return l;
+    };
+    // Element v of block h of tile jt holds key jt*BC + 4g + 8(v/4) + v%4; it
+    // is allowed while 8(v/4) + v%4 is at most lim[h].
+    auto limits = [&](int jt, int (&lim)[2]) {
+      const bool lv = SPARSE ? live(jt) : true;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int last = n - 1;
-      if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
-      lim[h] = lv ? last - jt * BC - 4 * g : -1;
+      for (int h = 0; h < 2; ++h) {
+        int last = n - 1;
+        if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+        lim[h] = lv ? last - jt * BC - 4 * g : -1;
+      }
+    };
+
+    KD kd;
+    VD vd;
+    kd.init(w, lane);
+    vd.init(w, lane);
+    const int krow = KL::row_base(c32, g);
+    const int vtr = KD::kSlot + VL::tr_base(lane);
+    auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
+
+    vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
+
+    const int j_first = SPARSE ? next_tile(-1) : 0;
+    if (j_first >= j_end) {  // no key tile at all: O = 0, L = -inf
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int my_q = qw0 + 32 * h + c32;
+        if (my_q < n) {
+          uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
+          for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(op + c) = u32x4{0u, 0u, 0u, 0u};
+          if (g == 0) a.lse[(size_t)bh * n + my_q] = -INFINITY;
+        }
+      }
+      return;
     }
-  };
+    // Every iteration issues exactly C DMA instructions (past the last tile
+    // they reload the first tile into a slot nobody reads), so the tile after
+    // the next one has landed once vmcnt <= C at the barrier.
+    int jq = j_first;  // next tile to load
+    int sq = 0;        // its slot
+    // its addressing, set once per tile: K and V rows, last valid row, LDS
+    // address of this wave's share
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+    const uint16_t* dk = Kg;
+    const uint16_t* dv = Vg;
+    int d_last = 0;
+    uint32_t d_lds = 0;
+    auto dma_set = [&]() {
+      const int jt = jq < j_end ? jq : j_first;
+      dk = Kg + (size_t)jt * BC * D;
+      dv = Vg + (size_t)jt * BC * D;
+      d_last = n - 1 - jt * BC;
+      d_lds = lds_base + sq + 1024 * w;
+    };
+    // DMA instruction i (of C) of the tile
+    auto dma_tile = [&](int i) {
+      if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
+      else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
+    };
+    auto dma_advance = [&]() {
+      if (jq < j_end) jq = next_tile(jq);
+      sq = slot_next(sq);
+      dma_set();
+    };
+    dma_set();
+    // A tile's DMA is split: instructions 0..kDB-1 are issued in the B
+    // phase of one iteration, the rest in the A phase of the next (spreading
+    // the address work of the four waves over the whole iteration)
+    constexpr int kDB = C / 2;
+    for (int t = 0; t < 3; ++t) {
+#pragma unroll
+      for (int i = 0; i < C; ++i) dma_tile(i);
+      dma_advance();
+    }
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) dma_tile(i);
 
-  KD kd;
-  VD vd;
-  kd.init(w, lane);
-  vd.init(w, lane);
-  const int krow = KL::row_base(c32, g);
-  const int vtr = KD::kSlot + VL::tr_base(lane);
-  auto slot_next = [&](int so) { return so + SLOT == kRing * SLOT ? 0 : so + SLOT; };
+    f32x16 acc[2][MB];  // O^T of both blocks, in AGPRs
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
+    const float cs = a.c;  // scale * log2(e): scores in exp2 units
+    const float inv_cs = 1.0f / cs;
+    // S^T of both blocks for two tiles, register sets 0 and 1 by tile parity
+    f32x16 s[2][2];
+    // packed P^T (B operands of the PV products) for two tiles
+    u32x4 pb[2][2][PK];
+    constexpr int kPD = 6;  // LDS fragments run kPD products ahead
+    u32x4 fr[kPD + 1];      // K row fragments (ring)
+    u32x4 kq[kPD + 1];      // V^T fragments (ring)
+    auto rd_k = [&](const lchar* rows, int ks) { return ld_row(rows + KL::row_off(0, ks)); };
+    auto rd_v = [&](const lchar* vt, int f) {
+      return ld_tr(vt + VL::tr_off(0, f / MB, 0, f % MB), vt + VL::tr_off(0, f / MB, 1, f % MB));
+    };
+    auto k_rows = [&](int so) { return lds_opaque(lds_ptr(smem) + so + krow); };
+    auto v_cols = [&](int so) { return lds_opaque(lds_ptr(smem) + so + vtr); };
+    auto prefetch_k = [&](int so) {
+      const lchar* rows = k_rows(so);
+#pragma unroll
+      for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd_k(rows, ks);
+    };
 
-  vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
 
-  const int j_first = SPARSE ? next_tile(-1) : 0;
-  if (j_first >= j_end) {  // no key tile at all: O = 0, L = -inf
+    // S^T = K Q^T of both blocks for the tile in slot `so` into set Y (its
+    // first kPD K fragments already in flight), with vec(u) = vector work
+    // after product u = 2 ks + h.
+    // (No VALU instruction writes their operands: K fragments come from LDS,
+    // Q^T from memory, and the accumulators only from the products.)
+    auto prod_s = [&](auto y_c, int so, auto&& vec) {
+      constexpr int Y = decltype(y_c)::value;
+      const lchar* rows = k_rows(so);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd_k(rows, ks + kPD);
+        const u32x4 f = fr[ks % (kPD + 1)];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (ks == 0) mfma32_vd<Tag, true, true, false>(s[Y][h], f, qreg[h][ks]);
+          else mfma32_vd<Tag, false, true, false>(s[Y][h], f, qreg[h][ks]);
+          vec(2 * ks + h);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    // Row statistics.  m_run[h] is the stale maximum every P of block h is
+    // taken against (exp2 units, -inf until a row sees its first key); nmu is
+    // -m_run, or 0 while m_run = -inf so that masked scores give exp2(-inf);
+    // thr is the raw score above which a row's maximum has outgrown m_run by
+    // more than the lazy margin.
+    float m_run[2] = {-INFINITY, -INFINITY}, nmu[2] = {0.0f, 0.0f};
+    float thr[2] = {-INFINITY, -INFINITY};
+    float l_part[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};  // two partial sums per block (independent add chains)
+
+    // the first tile's products; its P^T "predecessor" is zero
+    vm_wait<C + kDB>();  // tiles 0 and 1 have landed (for this wave's share) ...
+    __syncthreads();   // ... for every wave
+    int j = j_first;
+    int so = 0;        // slot of tile j
+    int sp = 0;        // slot of the tile whose PV products run next (none yet: any landed slot)
+    prefetch_k(so);
+    prod_s(std::integral_constant<int, 0>{}, so, [](int) {});
+    vgpr_drain(s[0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kk = 0; kk < PK; ++kk) pb[1][h][kk] = u32x4{0u, 0u, 0u, 0u};
+    int jn = next_tile(j);
+    int sn = slot_next(so);
+    prefetch_k(sn);
+
+    // Iteration i (tile j = set X, its successor jn = set Y, its predecessor
+    // jp in slot sp):
+    //   A: S^T of jn (matrix products into VGPRs)
+    //      | mask, running-row maximum and t = S^T c - m of j
+    //   barrier (the tile after jn has landed; every wave is past A)
+    //   B: O^T += V^T P^T of jp (products into AGPRs)
+    //      | P = exp2(t), row sums and packing of j, DMA
+    // If a row's maximum outgrew the lazy margin in A, m is refreshed right
+    // after A (l and the t values of j rescaled) and O^T right after B.  The
+    // exponentials run beside the AGPR-destination products only: next to
+    // products that write VGPRs they issue markedly slower.
+    auto step = [&](auto x_c, auto mask_c) {
+      constexpr int X = decltype(x_c)::value;
+      constexpr int Y = 1 - X;
+      constexpr bool MASK = decltype(mask_c)::value;
+      int lim[2];
+      if constexpr (MASK) limits(j, lim);
+      // ---- A
+      // Per element of tile j: mask and running maximum in the first half of
+      // the products (so the refresh test is known early), t = S c - m
+      // spread over all of them (after the element's mask).
+      float mx[2] = {-INFINITY, -INFINITY};
+      bool grow = false;
+      constexpr int RM = 32 / KS;       // elements per slot, mask and maximum
+      constexpr int R = 32 / (2 * KS);  // elements per slot, t
+      // the first V^T fragments of tile jp are read during the last products
+      constexpr int kPV = kPD < NF ? kPD : NF;
+      const lchar* vtp = v_cols(sp);
+      prod_s(std::integral_constant<int, Y>{}, sn, [&](int u) {
+        if (u >= 2 * KS - kPV) kq[u - (2 * KS - kPV)] = rd_v(vtp, u - (2 * KS - kPV));
+        if (u < KS) {
+#pragma unroll
+          for (int r = 0; r < RM; r += 2) {
+            const int e = u * RM + r, h = e >> 4, v = e & 15;
+            if constexpr (MASK) {
+              s[X][h][v] = (8 * (v >> 2) + (v & 3) > lim[h]) ? -INFINITY : s[X][h][v];
+              s[X][h][v + 1] = (8 * ((v + 1) >> 2) + ((v + 1) & 3) > lim[h]) ? -INFINITY : s[X][h][v + 1];
+            }
+            mx[h] = max3(mx[h], s[X][h][v], s[X][h][v + 1]);
+          }
+        }
+        if (u == KS) grow = __builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1]) != 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int e = u * R + r, h = e >> 4, v = e & 15;
+          s[X][h][v] = fmaf(s[X][h][v], cs, nmu[h]);
+        }
+#pragma unroll
+        for (int q = kDB; q < C; ++q)
+          if (u == 1 + (q - kDB) * (2 * KS - 2) / (C - kDB)) dma_tile(q);
+      });
+      dma_advance();
+      // ---- B, first products (independent of the refresh and the barrier)
+      const lchar* vt = v_cols(sp);
+      auto pv = [&](int f, int h) { mfma32_acc<Tag>(acc[h][f % MB], kq[f % (kPD + 1)], pb[Y][h][f / MB]); };
+      if (kPD < NF) kq[kPD % (kPD + 1)] = rd_v(vt, kPD);
+      pv(0, 0);
+      pv(0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      float alpha[2] = {1.0f, 1.0f};
+      if (__builtin_expect(grow, 0)) {  // rare: refresh m for the rows whose maximum outgrew it
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float mt = half_max(mx[h]) * cs;
+          const bool gr = mt > m_run[h] + kLazy;
+          alpha[h] = gr ? fast_exp2(m_run[h] - mt) : 1.0f;
+          const float nmu_new = gr ? -mt : nmu[h];
+          const float delta = nmu_new - nmu[h];
+          m_run[h] = gr ? mt : m_run[h];
+          nmu[h] = nmu_new;
+          thr[h] = (m_run[h] + kLazy) * inv_cs;
+          l_part[h][0] *= alpha[h];
+          l_part[h][1] *= alpha[h];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[X][h][v] += delta;
+        }
+      }
+      const int jnn = next_tile(jn);
+      const int snn = slot_next(sn);
+      vm_wait<C>();      // tile jnn has landed (for this wave's share) ...
+      wg_barrier();      // ... for every wave; the slot refilled below is free
+      constexpr int kPK = kPD < KS ? kPD : KS;
+      const lchar* krn = k_rows(snn);
+      // ---- B, the rest
+      // element e (block e/16, row e%16) of tile j in two stages one slot
+      // apart: P = exp2(t), then the row sum; each 8-element group is packed
+      // once summed.  Slot u (2 .. 2NF-1) takes elements E(u-2) .. E(u-1)-1.
+      auto stx = [&](int e) {
+        const int h = e >> 4, v = e & 15;
+        s[X][h][v] = fast_exp2(s[X][h][v]);
+        asm volatile("" : "+v"(s[X][h][v]));
+      };
+      auto sty = [&](int e) {
+        const int h = e >> 4, v = e & 15;
+        l_part[h][v & 1] += s[X][h][v];
+        asm volatile("" : "+v"(l_part[h][v & 1]));
+        if ((v & 7) == 7) {
+          pb[X][h][v >> 3] = pack8<Tag>(s[X][h], v & 8);
+          asm volatile("" : "+v"(pb[X][h][v >> 3]));
+        }
+      };
+      constexpr int NS = 2 * NF - 2;  // slots carrying element work
+      auto E = [](int k) { return 32 * k / NS; };
+      auto slot_work = [&](int u) {  // u = 2 .. 2NF (2NF: the tail)
+        const int k = u - 2;
+        if (k < NS)
+          for (int e = E(k); e < E(k + 1); ++e) stx(e);
+        if (k >= 1)
+          for (int e = E(k - 1); e < E(k); ++e) sty(e);
+      };
+#pragma unroll
+      for (int f = 1; f < NF; ++f) {
+        if (f + kPD < NF) kq[(f + kPD) % (kPD + 1)] = rd_v(vt, f + kPD);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          pv(f, h);
+          slot_work(2 * f + h);
+          // the first K fragments of tile jnn (landed: barrier above) are
+          // read during the first products, for the next A phase
+          const int u = 2 * f + h;
+          if (u >= 2 && u < 2 + kPK) fr[u - 2] = rd_k(krn, u - 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < kDB; ++q)
+          if (f == 1 + (2 * q + 1) * (NF - 1) / (2 * kDB)) dma_tile(q);
+      }
+      slot_work(2 * NF);
+      if (__builtin_expect(grow, 0)) {
+        agpr_drain(acc[0]);
+        agpr_drain(acc[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[h][mb] *= alpha[h];
+      }
+      sp = so;
+      so = sn;
+      sn = snn;
+      j = jn;
+      jn = jnn;
+    };
+
+    // Two iterations per trip keep the register sets in fixed roles.  The
+    // sweep runs until the PV products of the last tile are done; iterations
+    // past it see no tile (all keys masked, slots holding valid reloads).
+    // Dense sweeps start with the iterations whose tile j has no masked key
+    // for this wave (keys below its diagonal and inside the sequence), an
+    // even number of them, without any per-element test; the rest run with
+    // the mask.  The total is the same for every wave.
+    int n_plain = 0;
+    if constexpr (!SPARSE) {
+      int jm = n / BC;                                   // first tile reaching past the sequence end
+      if constexpr (CAUSAL) jm = min(jm, qw0 / BC);     // first tile crossing the diagonal
+      n_plain = max(jm - j_first, 0) & ~1;
+    }
+    for (int t = 0; t < n_plain; t += 2) {
+      step(std::integral_constant<int, 0>{}, std::false_type{});
+      step(std::integral_constant<int, 1>{}, std::false_type{});
+    }
+    // The iteration of tile j_end (the first past the last) runs the PV
+    // products of the last tile; the trip containing it is the last.
+    do {
+      step(std::integral_constant<int, 0>{}, std::true_type{});
+      step(std::integral_constant<int, 1>{}, std::true_type{});
+    } while (j <= j_end);
+
+    agpr_drain(acc[0]);
+    agpr_drain(acc[1]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const float l = half_sum(l_part[h][0] + l_part[h][1]);
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       const int my_q = qw0 + 32 * h + c32;
       if (my_q < n) {
         uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
-        for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(op + c) = u32x4{0u, 0u, 0u, 0u};
-        if (g == 0) a.lse[(size_t)bh * n + my_q] = -INFINITY;
-      }
-    }
-    return;
-  }
-  // Every iteration issues exactly C DMA instructions (past the last tile
-  // they reload the first tile into a slot nobody reads), so the tile after
-  // the next one has landed once vmcnt <= C at the barrier.
-  int jq = j_first;  // next tile to load
-  int sq = 0;        // its slot
-  // its addressing, set once per tile: K and V rows, last valid row, LDS
-  // address of this wave's share
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
-  const uint16_t* dk = Kg;
-  const uint16_t* dv = Vg;
-  int d_last = 0;
-  uint32_t d_lds = 0;
-  auto dma_set = [&]() {
-    const int jt = jq < j_end ? jq : j_first;
-    dk = Kg + (size_t)jt * BC * D;
-    dv = Vg + (size_t)jt * BC * D;
-    d_last = n - 1 - jt * BC;
-    d_lds = lds_base + sq + 1024 * w;
-  };
-  // DMA instruction i (of C) of the tile
-  auto dma_tile = [&](int i) {
-    if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
-    else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
-  };
-  auto dma_advance = [&]() {
-    if (jq < j_end) jq = next_tile(jq);
-    sq = slot_next(sq);
-    dma_set();
-  };
-  dma_set();
-  // A tile's DMA is split: instructions 0..kDB-1 are issued in the B
-  // phase of one iteration, the rest in the A phase of the next (spreading
-  // the address work of the four waves over the whole iteration)
-  constexpr int kDB = C / 2;
-  for (int t = 0; t < 3; ++t) {
 #pragma unroll
-    for (int i = 0; i < C; ++i) dma_tile(i);
-    dma_advance();
-  }
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-  for (int i = 0; i < kDB; ++i) dma_tile(i);
-
-  f32x16 acc[2][MB];  // O^T of both blocks, in AGPRs
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
-  const float cs = a.c;  // scale * log2(e): scores in exp2 units
-  const float inv_cs = 1.0f / cs;
-  // S^T of both blocks for two tiles, register sets 0 and 1 by tile parity
-  f32x16 s[2][2];
-  // packed P^T (B operands of the PV products) for two tiles
-  u32x4 pb[2][2][PK];
-  constexpr int kPD = 6;  // LDS fragments run kPD products ahead
-  u32x4 fr[kPD + 1];      // K row fragments (ring)
-  u32x4 kq[kPD + 1];      // V^T fragments (ring)
-  auto rd_k = [&](const lchar* rows, int ks) { return ld_row(rows + KL::row_off(0, ks)); };
-  auto rd_v = [&](const lchar* vt, int f) {
-    return ld_tr(vt + VL::tr_off(0, f / MB, 0, f % MB), vt + VL::tr_off(0, f / MB, 1, f % MB));
-  };
-  auto k_rows = [&](int so) { return lds_opaque(lds_ptr(smem) + so + krow); };
-  auto v_cols = [&](int so) { return lds_opaque(lds_ptr(smem) + so + vtr); };
-  auto prefetch_k = [&](int so) {
-    const lchar* rows = k_rows(so);
-#pragma unroll
-    for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd_k(rows, ks);
-  };
-
-
-  // S^T = K Q^T of both blocks for the tile in slot `so` into set Y (its
-  // first kPD K fragments already in flight), with vec(u) = vector work
-  // after product u = 2 ks + h.
-  // (No VALU instruction writes their operands: K fragments come from LDS,
-  // Q^T from memory, and the accumulators only from the products.)
-  auto prod_s = [&](auto y_c, int so, auto&& vec) {
-    constexpr int Y = decltype(y_c)::value;
-    const lchar* rows = k_rows(so);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd_k(rows, ks + kPD);
-      const u32x4 f = fr[ks % (kPD + 1)];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (ks == 0) mfma32_vd<Tag, true, true, false>(s[Y][h], f, qreg[h][ks]);
-        else mfma32_vd<Tag, false, true, false>(s[Y][h], f, qreg[h][ks]);
-        vec(2 * ks + h);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // Row statistics.  m_run[h] is the stale maximum every P of block h is
-  // taken against (exp2 units, -inf until a row sees its first key); nmu is
-  // -m_run, or 0 while m_run = -inf so that masked scores give exp2(-inf);
-  // thr is the raw score above which a row's maximum has outgrown m_run by
-  // more than the lazy margin.
-  float m_run[2] = {-INFINITY, -INFINITY}, nmu[2] = {0.0f, 0.0f};
-  float thr[2] = {-INFINITY, -INFINITY};
-  float l_part[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};  // two partial sums per block (independent add chains)
-
-  // the first tile's products; its P^T "predecessor" is zero
-  vm_wait<C + kDB>();  // tiles 0 and 1 have landed (for this wave's share) ...
-  __syncthreads();   // ... for every wave
-  int j = j_first;
-  int so = 0;        // slot of tile j
-  int sp = 0;        // slot of the tile whose PV products run next (none yet: any landed slot)
-  prefetch_k(so);
-  prod_s(std::integral_constant<int, 0>{}, so, [](int) {});
-  vgpr_drain(s[0]);
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int kk = 0; kk < PK; ++kk) pb[1][h][kk] = u32x4{0u, 0u, 0u, 0u};
-  int jn = next_tile(j);
-  int sn = slot_next(so);
-  prefetch_k(sn);
-
-  // Iteration i (tile j = set X, its successor jn = set Y, its predecessor
-  // jp in slot sp):
-  //   A: S^T of jn (matrix products into VGPRs)
-  //      | mask, running-row maximum and t = S^T c - m of j
-  //   barrier (the tile after jn has landed; every wave is past A)
-  //   B: O^T += V^T P^T of jp (products into AGPRs)
-  //      | P = exp2(t), row sums and packing of j, DMA
-  // If a row's maximum outgrew the lazy margin in A, m is refreshed right
-  // after A (l and the t values of j rescaled) and O^T right after B.  The
-  // exponentials run beside the AGPR-destination products only: next to
-  // products that write VGPRs they issue markedly slower.
-  auto step = [&](auto x_c, auto mask_c) {
-    constexpr int X = decltype(x_c)::value;
-    constexpr int Y = 1 - X;
-    constexpr bool MASK = decltype(mask_c)::value;
-    int lim[2];
-    if constexpr (MASK) limits(j, lim);
-    // ---- A
-    // Per element of tile j: mask and running maximum in the first half of
-    // the products (so the refresh test is known early), t = S c - m
-    // spread over all of them (after the element's mask).
-    float mx[2] = {-INFINITY, -INFINITY};
-    bool grow = false;
-    constexpr int RM = 32 / KS;       // elements per slot, mask and maximum
-    constexpr int R = 32 / (2 * KS);  // elements per slot, t
-    // the first V^T fragments of tile jp are read during the last products
-    constexpr int kPV = kPD < NF ? kPD : NF;
-    const lchar* vtp = v_cols(sp);
-    prod_s(std::integral_constant<int, Y>{}, sn, [&](int u) {
-      if (u >= 2 * KS - kPV) kq[u - (2 * KS - kPV)] = rd_v(vtp, u - (2 * KS - kPV));
-      if (u < KS) {
-#pragma unroll
-        for (int r = 0; r < RM; r += 2) {
-          const int e = u * RM + r, h = e >> 4, v = e & 15;
-          if constexpr (MASK) {
-            s[X][h][v] = (8 * (v >> 2) + (v & 3) > lim[h]) ? -INFINITY : s[X][h][v];
-            s[X][h][v + 1] = (8 * ((v + 1) >> 2) + ((v + 1) & 3) > lim[h]) ? -INFINITY : s[X][h][v + 1];
+          for (int r = 0; r < 4; ++r) {
+            u32x2 pk;
+            pk[0] = pack2<Tag>(acc[h][mb][4 * r] * inv, acc[h][mb][4 * r + 1] * inv);
+            pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * inv, acc[h][mb][4 * r + 3] * inv);
+            *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * r + 4 * g) = pk;
           }
-          mx[h] = max3(mx[h], s[X][h][v], s[X][h][v + 1]);
-        }
-      }
-      if (u == KS) grow = __builtin_amdgcn_ballot_w64(mx[0] > thr[0] || mx[1] > thr[1]) != 0;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int e = u * R + r, h = e >> 4, v = e & 15;
-        s[X][h][v] = fmaf(s[X][h][v], cs, nmu[h]);
-      }
-#pragma unroll
-      for (int q = kDB; q < C; ++q)
-        if (u == 1 + (q - kDB) * (2 * KS - 2) / (C - kDB)) dma_tile(q);
-    });
-    dma_advance();
-    // ---- B, first products (independent of the refresh and the barrier)
-    const lchar* vt = v_cols(sp);
-    auto pv = [&](int f, int h) { mfma32_acc<Tag>(acc[h][f % MB], kq[f % (kPD + 1)], pb[Y][h][f / MB]); };
-    if (kPD < NF) kq[kPD % (kPD + 1)] = rd_v(vt, kPD);
-    pv(0, 0);
-    pv(0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    float alpha[2] = {1.0f, 1.0f};
-    if (__builtin_expect(grow, 0)) {  // rare: refresh m for the rows whose maximum outgrew it
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float mt = half_max(mx[h]) * cs;
-        const bool gr = mt > m_run[h] + kLazy;
-        alpha[h] = gr ? fast_exp2(m_run[h] - mt) : 1.0f;
-        const float nmu_new = gr ? -mt : nmu[h];
-        const float delta = nmu_new - nmu[h];
-        m_run[h] = gr ? mt : m_run[h];
-        nmu[h] = nmu_new;
-        thr[h] = (m_run[h] + kLazy) * inv_cs;
-        l_part[h][0] *= alpha[h];
-        l_part[h][1] *= alpha[h];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[X][h][v] += delta;
+        if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
       }
     }
-    const int jnn = next_tile(jn);
-    const int snn = slot_next(sn);
-    vm_wait<C>();      // tile jnn has landed (for this wave's share) ...
-    wg_barrier();      // ... for every wave; the slot refilled below is free
-    constexpr int kPK = kPD < KS ? kPD : KS;
-    const lchar* krn = k_rows(snn);
-    // ---- B, the rest
-    // element e (block e/16, row e%16) of tile j in two stages one slot
-    // apart: P = exp2(t), then the row sum; each 8-element group is packed
-    // once summed.  Slot u (2 .. 2NF-1) takes elements E(u-2) .. E(u-1)-1.
-    auto stx = [&](int e) {
-      const int h = e >> 4, v = e & 15;
-      s[X][h][v] = fast_exp2(s[X][h][v]);
-      asm volatile("" : "+v"(s[X][h][v]));
-    };
-    auto sty = [&](int e) {
-      const int h = e >> 4, v = e & 15;
-      l_part[h][v & 1] += s[X][h][v];
-      asm volatile("" : "+v"(l_part[h][v & 1]));
-      if ((v & 7) == 7) {
-        pb[X][h][v >> 3] = pack8<Tag>(s[X][h], v & 8);
-        asm volatile("" : "+v"(pb[X][h][v >> 3]));
-      }
-    };
-    constexpr int NS = 2 * NF - 2;  // slots carrying element work
-    auto E = [](int k) { return 32 * k / NS; };
-    auto slot_work = [&](int u) {  // u = 2 .. 2NF (2NF: the tail)
-      const int k = u - 2;
-      if (k < NS)
-        for (int e = E(k); e < E(k + 1); ++e) stx(e);
-      if (k >= 1)
-        for (int e = E(k - 1); e < E(k); ++e) sty(e);
-    };
-#pragma unroll
-    for (int f = 1; f < NF; ++f) {
-      if (f + kPD < NF) kq[(f + kPD) % (kPD + 1)] = rd_v(vt, f + kPD);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        pv(f, h);
-        slot_work(2 * f + h);
-        // the first K fragments of tile jnn (landed: barrier above) are
-        // read during the first products, for the next A phase
-        const int u = 2 * f + h;
-        if (u >= 2 && u < 2 + kPK) fr[u - 2] = rd_k(krn, u - 2);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int q = 0; q < kDB; ++q)
-        if (f == 1 + (2 * q + 1) * (NF - 1) / (2 * kDB)) dma_tile(q);
-    }
-    slot_work(2 * NF);
-    if (__builtin_expect(grow, 0)) {
-      agpr_drain(acc[0]);
-      agpr_drain(acc[1]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[h][mb] *= alpha[h];
-    }
-    sp = so;
-    so = sn;
-    sn = snn;
-    j = jn;
-    jn = jnn;
-  };
-
-  // Two iterations per trip keep the register sets in fixed roles.  The
-  // sweep runs until the PV products of the last tile are done; iterations
-  // past it see no tile (all keys masked, slots holding valid reloads).
-  // Dense sweeps start with the iterations whose tile j has no masked key
-  // for this wave (keys below its diagonal and inside the sequence), an
-  // even number of them, without any per-element test; the rest run with
-  // the mask.  The total is the same for every wave.
-  int n_plain = 0;
-  if constexpr (!SPARSE) {
-    int jm = n / BC;                                   // first tile reaching past the sequence end
-    if constexpr (CAUSAL) jm = min(jm, qw0 / BC);     // first tile crossing the diagonal
-    n_plain = max(jm - j_first, 0) & ~1;
-  }
-  for (int t = 0; t < n_plain; t += 2) {
-    step(std::integral_constant<int, 0>{}, std::false_type{});
-    step(std::integral_constant<int, 1>{}, std::false_type{});
-  }
-  // The iteration of tile j_end (the first past the last) runs the PV
-  // products of the last tile; the trip containing it is the last.
-  do {
-    step(std::integral_constant<int, 0>{}, std::true_type{});
-    step(std::integral_constant<int, 1>{}, std::true_type{});
-  } while (j <= j_end);
-
-  agpr_drain(acc[0]);
-  agpr_drain(acc[1]);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float l = half_sum(l_part[h][0] + l_part[h][1]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const int my_q = qw0 + 32 * h + c32;
-    if (my_q < n) {
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x2 pk;
-          pk[0] = pack2<Tag>(acc[h][mb][4 * r] * inv, acc[h][mb][4 * r + 1] * inv);
-          pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * inv, acc[h][mb][4 * r + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * r + 4 * g) = pk;
-        }
-      if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
-    }
-  }
   };
   const int qa = a.nqb - 1 - pb_;  // the longer block first
   const int nrun = (CAUSAL && pb_ != qa) ? 2 : 1;
