@@ -450,14 +450,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int MB = D / 32;          // 32-row blocks of dQ^T
   constexpr int PK = BC / 16;         // k-steps of the dQ products
   constexpr int NF = PK * MB;         // K^T fragments per tile
-  constexpr int kRing = 4;
+  constexpr int kRing = 6;            // LDS tile slots
   using KL = Pad<D, true>;            // K: row reads (S^T) and transpose reads (dQ^T)
   using VL = Pad<D, false>;           // V: row reads (dP^T)
   using KD = Dma<BC, D, true, kNT / 64>;
   using VD = Dma<BC, D, false, kNT / 64>;
   constexpr int SLOT = KD::kSlot + VD::kSlot;
   constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
-  static_assert(3 * C < 64, "vmcnt range");
+  static_assert(4 * C < 64, "vmcnt range");
   static_assert(C <= NF, "DMA issue slots");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
@@ -553,8 +553,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       return;
     }
     // Every iteration issues exactly C DMA instructions (past the last tile
-    // they reload the first tile into a slot nobody reads), so "tile t+1 has
-    // landed" is always vmcnt <= C at the top of iteration t.
+    // they reload the first tile into a slot nobody reads), so the tile
+    // after the next one has landed once vmcnt <= C at the barrier.
     int jq = j_first;  // next tile to load
     int sq = 0;        // its slot
     // its addressing, set once per tile: K and V rows, last valid row, LDS
@@ -581,12 +581,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       sq = slot_next(sq);
       dma_set();
     };
+    // A tile's DMA is split: instructions 0..kDB-1 are issued in the B phase
+    // of one iteration, the rest in the A phase of the next.
+    constexpr int kDB = C / 2;
     dma_set();
-    for (int t = 0; t < kRing - 1; ++t) {
+    for (int t = 0; t < 3; ++t) {
 #pragma unroll
       for (int i = 0; i < C; ++i) dma_tile(i);
       dma_advance();
     }
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) dma_tile(i);
 
     f32x16 acc[2][MB];
 #pragma unroll
@@ -594,33 +599,60 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[h][mb] = 0.0f;
     const float cs = a.c;
-    // S^T and dP^T - D of both blocks for two tiles: set X = the tile whose
-    // dS is being formed, set Y = the next tile, whose products run meanwhile
+    // S^T and dP^T - D of both blocks (turned into P and dS in place) for
+    // two tiles, register sets by tile parity; packed dS^T likewise
     f32x16 s[2][2], dp[2][2];
-    constexpr int kPD = 6;  // LDS fragments run kPD k-steps ahead of the products
+    u32x4 db[2][2][PK];
+    constexpr int kPD = SPARSE ? 4 : 5;  // LDS fragments run kPD products ahead (registers permitting)
+    constexpr int kP = kPD < KS ? kPD : KS;   // row fragments in flight before a sweep
+    constexpr int kPT = kPD < NF ? kPD : NF;  // K^T fragments in flight before phase B
+    u32x4 fr[kPD + 1];  // K or V row fragments (ring)
+    u32x4 kq[kPD + 1];  // K^T fragments (ring)
+    auto rows_k = [&](int so) { return lds_opaque(lds_ptr(smem) + so + krow); };
+    auto rows_v = [&](int so) { return lds_opaque(lds_ptr(smem) + so + vrow); };
+    auto cols_k = [&](int so) { return lds_opaque(lds_ptr(smem) + so + ktr); };
+    auto rd_k = [&](const lchar* r, int ks) { return ld_row(r + KL::row_off(0, ks)); };
+    auto rd_v = [&](const lchar* r, int ks) { return ld_row(r + VL::row_off(0, ks)); };
+    auto rd_kt = [&](const lchar* kt, int f) {
+      return ld_tr(kt + KL::tr_off(0, f / MB, 0, f % MB), kt + KL::tr_off(0, f / MB, 1, f % MB));
+    };
+    auto prefetch_k = [&](int so) {
+      const lchar* r = rows_k(so);
+#pragma unroll
+      for (int ks = 0; ks < kP; ++ks) fr[ks] = rd_k(r, ks);
+    };
+    // The dP sweep's first V fragments are read into the K ring during the
+    // S sweep: fragment i goes to entry i once the last K fragment held
+    // there (index kf(i)) has fed its products, i.e. after slot 2 kf(i) + 1.
+    auto kf = [](int i) {
+      int k = i;
+      while (k + kPD + 1 < KS) k += kPD + 1;
+      return k;
+    };
+    // V fragment reads after the product of slot u (u = 2 KS: after the sweep)
+    auto prefetch_v_at = [&](const lchar* vr, int u) {
+#pragma unroll
+      for (int i = 0; i < kP; ++i)
+        if (2 * kf(i) + 2 == u) fr[i] = rd_v(vr, i);
+    };
 
-    // One product of both blocks for the tile in slot `so` into set Y: S^T =
-    // K Q^T (P = false, K rows) or dP^T - D = V dO^T (P = true, V rows).
-    // Each fragment feeds both blocks; vec(ks) is vector work interleaved per
-    // k-step.  S^T and dP^T run as two sweeps so that set Y's dP^T registers
-    // are only needed once half of set X has been consumed.
-    auto prod = [&](auto y_c, auto p_c, int so, bool on, auto&& vec) {
+    // One sweep of both blocks' products for the tile in slot `so` into set
+    // Y, its first kP fragments already in flight: S^T = K Q^T (P = false)
+    // or dP^T - D = V dO^T (P = true).  Every fragment feeds both blocks;
+    // vec(u) is the vector work after product u = 2 ks + h.  (No VALU
+    // instruction writes the operands: fragments come from LDS, Q^T and dO^T
+    // from memory, -D is set once per block.)
+    auto sweep = [&](auto y_c, auto p_c, int so, bool on, auto&& vec) {
       constexpr int Y = decltype(y_c)::value;
       constexpr bool P = decltype(p_c)::value;
-      const lchar* rows = lds_opaque(lds_ptr(smem) + so + (P ? vrow : krow));
-      u32x4 fr[kPD + 1];
-      auto rd = [&](int ks) { return P ? ld_row(rows + VL::row_off(0, ks)) : ld_row(rows + KL::row_off(0, ks)); };
-      if (on) {
-#pragma unroll
-        for (int ks = 0; ks < kPD && ks < KS; ++ks) fr[ks] = rd(ks);
-      }
+      const lchar* rows = P ? rows_v(so) : rows_k(so);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (on) {
-          if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = rd(ks + kPD);
-          const u32x4 f = fr[ks % (kPD + 1)];
+        if (ks + kPD < KS) fr[(ks + kPD) % (kPD + 1)] = P ? rd_v(rows, ks + kPD) : rd_k(rows, ks + kPD);
+        const u32x4 f = fr[ks % (kPD + 1)];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 2; ++h) {
+          if (on) {
             f32x16& d = P ? dp[Y][h] : s[Y][h];
             const u32x4 b = P ? oreg[h][ks] : qreg[h][ks];
             if (ks == 0) {
@@ -629,165 +661,177 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
             } else {
               mfma32_vd<Tag, false, true>(d, f, b);
             }
-            // each product is followed by its share of vector work, so the
-            // next product issues as the matrix core frees up
-            vec(2 * ks + h);
-            __builtin_amdgcn_sched_barrier(0);
           }
-        } else {
-          vec(2 * ks);
-          vec(2 * ks + 1);
+          vec(2 * ks + h);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     };
-    auto sdp = [&](auto y_c, int so, bool on) {
-      prod(y_c, std::false_type{}, so, on, [](int) {});
-      prod(y_c, std::true_type{}, so, on, [](int) {});
-    };
 
-    // the first tile's products, then the pipelined sweep
-    vm_wait<2 * C>();
-    __syncthreads();
+    // the first tile's products; its dS predecessor is zero
+    vm_wait<C + kDB>();  // tiles 0 and 1 have landed (for this wave's share) ...
+    __syncthreads();     // ... for every wave
     int j = j_first;
     int so = 0;  // slot of tile j
-    sdp(std::integral_constant<int, 0>{}, so, !SPARSE || live(j));
+    int sp = 0;  // slot of the tile whose dQ products run next (none yet: any landed slot)
+    {
+      const bool on = !SPARSE || live(j);
+      const lchar* vr = rows_v(so);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dp[0][h] = 0.0f;  // finite even where no product runs (dS = 0 * dP)
+      prefetch_k(so);
+      sweep(std::integral_constant<int, 0>{}, std::false_type{}, so, on, [&](int u) { prefetch_v_at(vr, u + 1); });
+      prefetch_v_at(vr, 2 * KS);
+      sweep(std::integral_constant<int, 0>{}, std::true_type{}, so, on, [](int) {});
+    }
     vgpr_drain(s[0]);
     vgpr_drain(dp[0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dp[1][h] = 0.0f;
+    int jn = next_tile(j);
+    int sn = slot_next(so);
+    prefetch_k(sn);
 
-    // Iteration over tile j (set X) with the next tile jn (set Y = 1 - X):
-    //   part A: S^T, dP^T of (jn, both blocks)  | dS of (j, both blocks), DMA
-    //   part B: dQ^T += K^T dS^T of (j, both blocks), DMA
+    // Iteration i (tile j = set X, its successor jn = set Y, its
+    // predecessor jp in slot sp):
+    //   A: S^T, dP^T of jn (VGPR products)
+    //      | pack dS of jp; t = S^T c - L (+ mask) of j; DMA
+    //   barrier (the tile after jn has landed; every wave is past A)
+    //   B: dQ^T += K^T dS^T of jp (AGPR products)
+    //      | P = exp2(t), dS = P (dP^T - D) of j; DMA
+    // The exponentials share issue slots with AGPR-destination products
+    // only: next to products that write VGPRs they issue markedly slower.
     // The body is unrolled for X = 0 and X = 1.  The tile count is the
-    // workgroup's, so every wave runs every iteration (barrier per iteration):
-    // keys past a query's diagonal or the sequence end get dS = 0.
+    // workgroup's, so every wave runs every iteration: keys past a query's
+    // diagonal or the sequence end get t = -inf, hence P = dS = 0.
     auto step = [&](auto x_c, auto mask_c) {
       constexpr int X = decltype(x_c)::value;
       constexpr int Y = 1 - X;
       constexpr bool MASK = decltype(mask_c)::value;
-      const int jn = next_tile(j);
-      const int son = slot_next(so);
-      vm_wait<C>();      // tile jn has landed (for this wave's share) ...
-      wg_barrier();      // ... for every wave; the slot refilled below is free
-      // dense sweeps compute every tile, the dummy one included: its keys lie
-      // past the sequence end, so the mask gives dS = 0, and its slot holds a
-      // valid reload; branches here would cost fetch bubbles a lone wave
-      // cannot hide
-      const bool live_j = SPARSE ? live(j) : true;
-      const bool live_n = SPARSE ? live(jn) : true;
-      const int k0 = j * BC;
-      // element v of block h holds key k0 + 4g + 8(v/4) + v%4; it is allowed
-      // while that offset is at most lim[h]
+      // element v of block h of tile j holds key j*BC + 4g + 8(v/4) + v%4;
+      // it is allowed while 8(v/4) + v%4 is at most lim[h]
       int lim[2];
+      if constexpr (MASK) {
+        const bool lv = SPARSE ? live(j) : true;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int last = n - 1;
-        if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
-        lim[h] = last - k0 - 4 * g;
-      }
-      constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
-      // ---- part A
-      u32x4 db[2][PK];
-      // dS^T of block h, elements v0..v1-1, then packed once the block is done
-      // dS^T of element e (block e/16, row e%16) in three stages, software-
-      // pipelined so the vector work after each product is independent
-      // operations (one element's chain alone would stall on its latencies
-      // while the matrix core idles): t = S^T c - L, P = exp2(t),
-      // dS = P (dP^T - D) (+ mask).  The asm pins each finished element here,
-      // between the products; a block's dS^T is packed once complete.
-      auto st1 = [&](int e) { s[X][e >> 4][e & 15] = fmaf(s[X][e >> 4][e & 15], cs, -Lq[e >> 4]); };
-      auto st2 = [&](int e) { s[X][e >> 4][e & 15] = fast_exp2(s[X][e >> 4][e & 15]); };
-      auto st3 = [&](int e) {
-        const int h = e >> 4, v = e & 15;
-        float x = s[X][h][v] * dp[X][h][v];
-        if constexpr (MASK) x = (8 * (v >> 2) + (v & 3) > lim[h]) ? 0.0f : x;
-        dp[X][h][v] = x;
-        asm volatile("" : "+v"(dp[X][h][v]));
-        if (v == 15) {
-#pragma unroll
-          for (int kk = 0; kk < PK; ++kk) db[h][kk] = pack8<Tag>(dp[X][h], 8 * kk);
+        for (int h = 0; h < 2; ++h) {
+          int last = n - 1;
+          if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+          lim[h] = lv ? last - j * BC - 4 * g : -1;
         }
-      };
-      // (runs whether or not the tile is live: a skipped tile's registers hold
-      // stale finite values and its dS^T is replaced by zeros below, which
-      // keeps branches out of the product sequence)
-      auto staged = [&](int t) {  // element t enters, t-2 leaves
-        if (t < 32) st1(t);
-        if (t >= 1 && t - 1 < 32) st2(t - 1);
-        if (t >= 2 && t - 2 < 32) st3(t - 2);
-      };
-      // slot u = 0 .. 2KS-1 of a sweep: the product of k-step u/2, block u%2
-      auto dma_a = [&](int u, int half) {
-#pragma unroll
-        for (int q = 0; q < kDmaA; ++q)
-          if (half * 2 * KS + u == (2 * q + 1) * 2 * KS / kDmaA) dma_tile(q);
-      };
-      constexpr int R = 32 / (4 * KS);  // elements entering per product
-      prod(std::integral_constant<int, Y>{}, std::false_type{}, son, live_n, [&](int u) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) staged(u * R + r);
-        dma_a(u, 0);
-      });
-      prod(std::integral_constant<int, Y>{}, std::true_type{}, son, live_n, [&](int u) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) staged((2 * KS + u) * R + r);
-        dma_a(u, 1);
-      });
-      staged(32);
-      staged(33);
-      if (!live_j) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int kk = 0; kk < PK; ++kk) db[h][kk] = u32x4{0u, 0u, 0u, 0u};
       }
-      valu_to_mfma(db[0]);
-      valu_to_mfma(db[1]);
-      // ---- part B
-      const lchar* kt = lds_opaque(lds_ptr(smem) + so + ktr);
-      u32x4 kq[kPD + 1];
+      const bool live_n = SPARSE ? live(jn) : true;
+      // ---- A
+      constexpr int NA = 4 * KS;        // product slots of phase A
+      constexpr int RA = 32 / NA;       // elements of tile j per slot
+      constexpr int RP = 8 * PK / (2 * KS);  // dS pairs of tile jp packed per slot of the S sweep
+      auto va = [&](int u) {
 #pragma unroll
-      for (int f = 0; f < kPD && f < NF; ++f)
-        kq[f] = ld_tr(kt + KL::tr_off(0, f / MB, 0, f % MB), kt + KL::tr_off(0, f / MB, 1, f % MB));
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (f + kPD < NF) {
-          const int fn = f + kPD;
-          kq[fn % (kPD + 1)] = ld_tr(kt + KL::tr_off(0, fn / MB, 0, fn % MB), kt + KL::tr_off(0, fn / MB, 1, fn % MB));
+        for (int r = 0; r < RA; ++r) {
+          const int e = u * RA + r, h = e >> 4, v = e & 15;
+          float t = fmaf(s[X][h][v], cs, -Lq[h]);
+          if constexpr (MASK) t = (8 * (v >> 2) + (v & 3) > lim[h]) ? -INFINITY : t;
+          s[X][h][v] = t;
         }
-        mfma32_acc<Tag>(acc[0][f % MB], kq[f % (kPD + 1)], db[0][f / MB]);
-        mfma32_acc<Tag>(acc[1][f % MB], kq[f % (kPD + 1)], db[1][f / MB]);
+        if (u < 2 * KS) {
 #pragma unroll
-        for (int q = kDmaA; q < C; ++q)
-          if (f == (2 * (q - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(q);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+          for (int r = 0; r < RP; ++r) {
+            const int q = u * RP + r, h = q / (4 * PK), kk = (q / 4) % PK, i = q & 3;
+            db[Y][h][kk][i] = pack2<Tag>(dp[Y][h][8 * kk + 2 * i], dp[Y][h][8 * kk + 2 * i + 1]);
+          }
+        }
+#pragma unroll
+        for (int q = kDB; q < C; ++q)
+          if (u == 1 + (q - kDB) * (NA - 2) / (C - kDB)) dma_tile(q);
+      };
+      const lchar* vrn = rows_v(sn);
+      const lchar* ktp = cols_k(sp);
+      sweep(std::integral_constant<int, Y>{}, std::false_type{}, sn, live_n, [&](int u) {
+        va(u);
+        prefetch_v_at(vrn, u + 1);
+      });
+      prefetch_v_at(vrn, 2 * KS);
+      sweep(std::integral_constant<int, Y>{}, std::true_type{}, sn, live_n, [&](int u) {
+        va(2 * KS + u);
+        if (u >= 2 * KS - kPT) kq[u - (2 * KS - kPT)] = rd_kt(ktp, u - (2 * KS - kPT));
+      });
       dma_advance();
+      // ---- B, first products (independent of the barrier)
+      auto dqp = [&](int f, int h) { mfma32_acc<Tag>(acc[h][f % MB], kq[f % (kPD + 1)], db[Y][h][f / MB]); };
+      if (kPT < NF) kq[kPT % (kPD + 1)] = rd_kt(ktp, kPT);
+      dqp(0, 0);
+      dqp(0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int jnn = next_tile(jn);
+      const int snn = slot_next(sn);
+      vm_wait<C>();      // tile jnn has landed (for this wave's share) ...
+      wg_barrier();      // ... for every wave; the slot refilled below is free
+      // ---- B, the rest: element e (block e/16, row e%16) of tile j in two
+      // stages one slot apart, P = exp2(t) then dS = P (dP^T - D).  Slot u
+      // (2 .. 2NF-1) takes elements E(u-2) .. E(u-1)-1.
+      auto stx = [&](int e) {
+        const int h = e >> 4, v = e & 15;
+        s[X][h][v] = fast_exp2(s[X][h][v]);
+        asm volatile("" : "+v"(s[X][h][v]));
+      };
+      auto sty = [&](int e) {
+        const int h = e >> 4, v = e & 15;
+        dp[X][h][v] = s[X][h][v] * dp[X][h][v];
+        asm volatile("" : "+v"(dp[X][h][v]));
+      };
+      constexpr int NS = 2 * NF - 2;
+      auto E = [](int k) { return 32 * k / NS; };
+      auto slot_work = [&](int u) {
+        const int k = u - 2;
+        if (k < NS)
+          for (int e = E(k); e < E(k + 1); ++e) stx(e);
+        if (k >= 1)
+          for (int e = E(k - 1); e < E(k); ++e) sty(e);
+      };
+#pragma unroll
+      for (int f = 1; f < NF; ++f) {
+        if (f + kPT < NF) kq[(f + kPT) % (kPD + 1)] = rd_kt(ktp, f + kPT);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          dqp(f, h);
+          slot_work(2 * f + h);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < kDB; ++q)
+          if (f == 1 + (2 * q + 1) * (NF - 1) / (2 * kDB)) dma_tile(q);
+      }
+      slot_work(2 * NF);
+      prefetch_k(snn);
+      sp = so;
+      so = sn;
+      sn = snn;
       j = jn;
-      so = son;
+      jn = jnn;
     };
-    // Two iterations per trip: with an odd tile count the last iteration runs
-    // on no tile (dS = 0, its slot holds a valid reload), so the register sets
-    // X/Y keep fixed roles and the accumulators never sit in a branch (which
-    // would make the register allocator copy them every iteration).
-    // Dense sweeps start with the tiles no key of which is masked for this
-    // wave (keys below its diagonal and inside the sequence), an even number
-    // of them, without any per-element test; the rest, padded to an even
-    // count, run with the mask.  The total is the same for every wave.
+    // Two iterations per trip keep the register sets in fixed roles.  The
+    // sweep runs until the dQ products of the last tile are done; iterations
+    // past it see no tile (all keys masked, slots holding valid reloads).
+    // Dense sweeps start with the iterations whose tile j has no masked key
+    // for this wave (keys below its diagonal and inside the sequence), an
+    // even number of them, without any per-element test; the rest run with
+    // the mask.  The total is the same for every wave.
     int n_plain = 0;
     if constexpr (!SPARSE) {
-      int jm = n / BC;                       // first tile reaching past the sequence end
-      if constexpr (CAUSAL) jm = min(jm, qw0 / BC);  // first tile crossing the diagonal
+      int jm = n / BC;                                  // first tile reaching past the sequence end
+      if constexpr (CAUSAL) jm = min(jm, qw0 / BC);    // first tile crossing the diagonal
       n_plain = max(jm - j_first, 0) & ~1;
     }
     for (int t = 0; t < n_plain; t += 2) {
       step(std::integral_constant<int, 0>{}, std::false_type{});
       step(std::integral_constant<int, 1>{}, std::false_type{});
     }
-    while (j < j_end) {
+    // The iteration of tile j_end (the first past the last) runs the dQ
+    // products of the last tile; the trip containing it is the last.
+    do {
       step(std::integral_constant<int, 0>{}, std::true_type{});
       step(std::integral_constant<int, 1>{}, std::true_type{});
-    }
+    } while (j <= j_end);
 
     agpr_drain(acc[0]);
     agpr_drain(acc[1]);
