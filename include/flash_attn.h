@@ -19,6 +19,9 @@
  *   [WALK] FlashAttention walkthrough (bluuewhale.github.io/posts/
  *          flash-attention-en): "How Attention Is Computed" (scaled scores),
  *          "Block-Sparse FlashAttention" (mask M in {0,1}^{Tr x Tc}).
+ *   [V1]   Flash Attention v1 notes (languisher.top/posts/flash-attention):
+ *          merging the softmax statistics of two vectors (max, normaliser,
+ *          rescaled numerators).
  *
  * Common conventions
  * ------------------
@@ -63,7 +66,7 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, negative size, bad scale/flag */
   FA_ERR_UNSUPPORTED = 2,        /* valid but outside the supported domain (d, dtype, mask block) */
-  FA_ERR_WORKSPACE_TOO_SMALL = 3,/* backward workspace smaller than flash_attn_bwd_workspace_size() */
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace smaller than the matching *_workspace_size() */
   FA_ERR_HIP = 4                 /* a HIP launch failed; see flash_attn_last_error() */
 } fa_status;
 
@@ -84,6 +87,31 @@ fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype,
                          const void* q, const void* k, const void* v,
                          float scale, int causal,
                          void* o, float* lse, hipStream_t stream);
+
+/*
+ * Split-KV forward [V1 merging of softmax statistics, applied to num_splits
+ * parts]: the result of flash_attn_fwd (same arguments and outputs, up to
+ * float32 rounding order), computed by cutting every row block's key tiles
+ * into num_splits contiguous ranges processed by separate workgroups, then
+ * merging.  Meant for problems with too few query blocks to fill the GPU
+ * (small B*H or short N).  Range s of row i yields its own output O_s
+ * (normalised by its own sum) and log-sum-exp L_s (-inf if the range has no
+ * allowed key); the merge writes LSE_i = ln sum_s e^{L_s} and
+ * O_i = sum_s e^{L_s - LSE_i} O_s.
+ *   num_splits  1 .. 64 (FA_ERR_INVALID_ARGUMENT outside).
+ *   workspace   scratch, >= flash_attn_fwd_splitkv_workspace_size() bytes:
+ *               num_splits float32 partial outputs [B][H][N][d] followed by
+ *               num_splits float32 partial log-sum-exps [B][H][N].
+ *               Contents on entry are ignored and left undefined.
+ * dtype FA_F16 or FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED).
+ */
+size_t flash_attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, fa_dtype dtype,
+                                             int num_splits);
+fa_status flash_attn_fwd_splitkv(int B, int H, int N, int d, fa_dtype dtype,
+                                 const void* q, const void* k, const void* v,
+                                 float scale, int causal, int num_splits,
+                                 void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Device workspace bytes flash_attn_bwd / flash_attn_blocksparse_bwd need:
@@ -148,8 +176,8 @@ fa_status flash_attn_blocksparse_bwd(int B, int H, int N, int d, fa_dtype dtype,
  * events, writes for each kernel class k < n the summed milliseconds and
  * launch count since the previous collect, and forgets them.  Kernel
  * classes: 0 forward (16-bit), 1 forward (float32), 2 backward D pre-pass,
- * 3 backward dK/dV pass, 4 backward dQ pass; flash_attn_kernel_name(k)
- * names them.  Events are created on first use and reused; no device
+ * 3 backward dK/dV pass, 4 backward dQ pass, 5 split-KV forward ranges,
+ * 6 split-KV merge; flash_attn_kernel_name(k) names them.  Events are created on first use and reused; no device
  * memory is allocated.  Process-wide, guarded by a mutex.
  */
 fa_status flash_attn_timing_enable(int enable);

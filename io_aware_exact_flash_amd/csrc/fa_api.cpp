@@ -168,6 +168,55 @@ fa_status run_bwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, co
   return hip_status(fn, e);
 }
 
+// Split-KV workspace: num_splits float32 [B*H][N][d] partial outputs, then
+// num_splits float32 [B*H][N] partial log-sum-exps (256-byte aligned).
+size_t splitkv_po_bytes(long long bh, long long n, int d, int splits) {
+  const size_t b = (size_t)splits * (size_t)bh * (size_t)n * (size_t)d * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+size_t splitkv_workspace_bytes(long long bh, long long n, int d, int splits) {
+  if (bh <= 0 || n <= 0 || splits <= 0) return 0;
+  return splitkv_po_bytes(bh, n, d, splits) + (size_t)splits * (size_t)bh * (size_t)n * sizeof(float);
+}
+constexpr int kMaxSplits = 64;
+
+fa_status run_fwd_split(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                        const void* k, const void* v, float scale, int causal, int splits, void* o,
+                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Problem p;
+  fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, false, &p);
+  if (s != FA_OK) return s;
+  if (splits < 1 || splits > kMaxSplits)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: num_splits %d outside 1..%d", fn, splits, kMaxSplits);
+  if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "%s: float32 split-KV forward is not supported", fn);
+  if ((long long)p.bh * ((N + 255LL) / 256) * splits >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "%s: problem too large for %d splits", fn, splits);
+  if (p.empty) return FA_OK;
+  const void* ptrs[] = {q, k, v, o, lse, ws};
+  const char* names[] = {"q", "k", "v", "o", "lse", "workspace"};
+  if ((s = check_ptrs(fn, ptrs, names, 6)) != FA_OK) return s;
+  const size_t need = splitkv_workspace_bytes(p.bh, N, d, splits);
+  if (ws_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.mask = nullptr;
+  a.mask_t = 0;
+  a.n = N;
+  a.c = scale * 1.4426950408889634f;
+  a.nsplit = splits;
+  a.po = static_cast<float*>(ws);
+  a.plse = reinterpret_cast<float*>(static_cast<char*>(ws) + splitkv_po_bytes(p.bh, N, d, splits));
+  hipError_t e = fa::launch_fwd_split(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, p.bh, a,
+                                      stream);
+  return hip_status(fn, e);
+}
+
 // ---------------------------------------------------------------- timing
 struct Mark {
   int kernel;
@@ -191,7 +240,8 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* kKernelNames[fa::kNumKernels] = {"fwd", "fwd_f32", "bwd_pre", "bwd_dkdv", "bwd_dq"};
+const char* kKernelNames[fa::kNumKernels] = {"fwd", "fwd_f32", "bwd_pre", "bwd_dkdv", "bwd_dq",
+                                            "fwd_split", "fwd_merge"};
 
 }  // namespace
 
@@ -258,6 +308,21 @@ FA_EXPORT fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype, c
                                    float* lse, hipStream_t stream) {
   return run_fwd("flash_attn_fwd", B, H, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o,
                  lse, stream);
+}
+
+FA_EXPORT size_t flash_attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, fa_dtype dtype,
+                                                       int num_splits) {
+  (void)dtype;
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  return splitkv_workspace_bytes((long long)B * H, N, d, num_splits);
+}
+
+FA_EXPORT fa_status flash_attn_fwd_splitkv(int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                                           const void* k, const void* v, float scale, int causal,
+                                           int num_splits, void* o, float* lse, void* workspace,
+                                           size_t workspace_bytes_, hipStream_t stream) {
+  return run_fwd_split("flash_attn_fwd_splitkv", B, H, N, d, dtype, q, k, v, scale, causal, num_splits, o,
+                       lse, workspace, workspace_bytes_, stream);
 }
 
 FA_EXPORT size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, fa_dtype dtype) {

@@ -50,7 +50,11 @@ constexpr int kWQ = 64;        // query rows per wave
 constexpr int kBR = 4 * kWQ;   // query rows per workgroup
 constexpr float kLazy = 8.0f;
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+// SPLIT: split-KV mode.  Workgroup (row block, range rng) covers only the
+// rng-th of a.nsplit contiguous chunks of the row block's key tiles and
+// writes its partial output (normalised by its own row sums) and partial
+// log-sum-exp to a.po / a.plse; fwd_merge_kernel combines the ranges.
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
 __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = 32;              // keys per tile
   constexpr int KS = D / 16;          // k-steps of the S^T products
@@ -77,10 +81,12 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   // Causal: workgroup p of a head runs the query blocks nqb-1-p and p one
   // after the other, so every workgroup has the same number of key tiles
   // (no long workgroup left running alone at the end of the grid).
-  const int per = CAUSAL ? (a.nqb + 1) / 2 : a.nqb;
+  const int per = (CAUSAL && !SPLIT) ? (a.nqb + 1) / 2 : a.nqb;
+  const int nsp = SPLIT ? a.nsplit : 1;
   const int lb = xcd_remap(blockIdx.x, a.nblk);
-  const int bh = lb / per;
-  const int pb_ = lb % per;
+  const int rng = lb % nsp;  // key range (split-KV)
+  const int bh = (lb / nsp) / per;
+  const int pb_ = (lb / nsp) % per;
   const size_t hoff = (size_t)bh * n * D;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
@@ -101,6 +107,12 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     const int n_tiles = (n + BC - 1) / BC;
     int j_end = n_tiles;
     if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + kBR, n) - 1) / BC + 1);
+    int j_lo = 0;
+    if constexpr (SPLIT) {  // this workgroup's chunk of the key tiles
+      const int chunk = (j_end + nsp - 1) / nsp;
+      j_lo = min(rng * chunk, j_end);
+      j_end = min(j_lo + chunk, j_end);
+    }
     // block-sparse: the workgroup spans two 128-query mask rows, each wave one
     const uint8_t* mrow0 = nullptr;
     const uint8_t* mrow1 = nullptr;
@@ -133,6 +145,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       for (int h = 0; h < 2; ++h) {
         int last = n - 1;
         if constexpr (CAUSAL) last = min(last, qw0 + 32 * h + c32);
+        if constexpr (SPLIT) last = min(last, j_end * BC - 1);
         lim[h] = lv ? last - jt * BC - 4 * g : -1;
       }
     };
@@ -147,15 +160,21 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
 
     vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
 
-    const int j_first = SPARSE ? next_tile(-1) : 0;
+    const int j_first = SPARSE ? next_tile(j_lo - 1) : j_lo;
     if (j_first >= j_end) {  // no key tile at all: O = 0, L = -inf
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int my_q = qw0 + 32 * h + c32;
         if (my_q < n) {
-          uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
-          for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(op + c) = u32x4{0u, 0u, 0u, 0u};
-          if (g == 0) a.lse[(size_t)bh * n + my_q] = -INFINITY;
+          if constexpr (SPLIT) {
+            const size_t row = ((size_t)rng * a.nbh + bh) * n + my_q;
+            for (int c = 4 * g; c < D; c += 8) *reinterpret_cast<f32x4*>(a.po + row * D + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (g == 0) a.plse[row] = -INFINITY;
+          } else {
+            uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
+            for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(op + c) = u32x4{0u, 0u, 0u, 0u};
+            if (g == 0) a.lse[(size_t)bh * n + my_q] = -INFINITY;
+          }
         }
       }
       return;
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     // the mask.  The total is the same for every wave.
     int n_plain = 0;
     if constexpr (!SPARSE) {
-      int jm = n / BC;                                   // first tile reaching past the sequence end
+      int jm = SPLIT ? min(n / BC, j_end) : n / BC;      // first tile reaching past the sequence (or range) end
       if constexpr (CAUSAL) jm = min(jm, qw0 / BC);     // first tile crossing the diagonal
       n_plain = max(jm - j_first, 0) & ~1;
     }
@@ -451,7 +470,19 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       const float l = half_sum(l_part[h][0] + l_part[h][1]);
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       const int my_q = qw0 + 32 * h + c32;
-      if (my_q < n) {
+      if (my_q < n && SPLIT) {
+        const size_t row = ((size_t)rng * a.nbh + bh) * n + my_q;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            f32x4 x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = acc[h][mb][4 * r + i] * inv;
+            *reinterpret_cast<f32x4*>(a.po + row * D + 32 * mb + 8 * r + 4 * g) = x;
+          }
+        if (g == 0) a.plse[row] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
+      } else if (my_q < n) {
         uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -467,7 +498,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     }
   };
   const int qa = a.nqb - 1 - pb_;  // the longer block first
-  const int nrun = (CAUSAL && pb_ != qa) ? 2 : 1;
+  const int nrun = (CAUSAL && !SPLIT && pb_ != qa) ? 2 : 1;
 #pragma clang loop unroll(disable)
   for (int r = 0; r < nrun; ++r) {
     if (r) {
@@ -476,6 +507,58 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     }
     run(r ? pb_ : qa);
   }
+}
+
+// Merge of the split-KV partials of one row (v1-notes, "merging two
+// vectors' softmax statistics", applied to nsplit parts): with the partial
+// log-sum-exps L_s and outputs O_s (each normalised by its own sum),
+// L = log sum_s e^{L_s} and O = sum_s e^{L_s - L} O_s.  D/4 threads per row,
+// four columns each.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kNT) void fwd_merge_kernel(FwdArgs a, long rows) {
+  constexpr int TPR = D / 4;  // threads per row
+  const long row = (long)blockIdx.x * (kNT / TPR) + threadIdx.x / TPR;
+  if (row >= rows) return;
+  const int c = 4 * (threadIdx.x % TPR);
+  const int S = a.nsplit;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.plse[(size_t)s * rows + row]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float wsum = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float wgt = expf(a.plse[(size_t)s * rows + row] - mx);
+      wsum += wgt;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(a.po + ((size_t)s * rows + row) * D + c);
+      o += wgt * x;
+    }
+    o *= 1.0f / wsum;
+    lse = mx + logf(wsum);
+  }
+  u32x2 pk;
+  pk[0] = pack2<Tag>(o[0], o[1]);
+  pk[1] = pack2<Tag>(o[2], o[3]);
+  *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + (size_t)row * D + c) = pk;
+  if (c == 0) a.lse[row] = lse;
+}
+
+template <typename Tag, int D>
+hipError_t launch_split_d(bool causal, const FwdArgs& a, hipStream_t st) {
+  timing_begin(kFwdSplit, st);
+  if (causal) hipLaunchKernelGGL((fwd_kernel<Tag, D, true, false, true>), dim3(a.nblk), dim3(kNT), 0, st, a);
+  else hipLaunchKernelGGL((fwd_kernel<Tag, D, false, false, true>), dim3(a.nblk), dim3(kNT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  timing_end(kFwdSplit, st);
+  if (e != hipSuccess) return e;
+  const long rows = (long)a.nbh * a.n;
+  constexpr int kRowsPerBlock = kNT / (D / 4);
+  timing_begin(kFwdMerge, st);
+  hipLaunchKernelGGL((fwd_merge_kernel<Tag, D>), dim3((rows + kRowsPerBlock - 1) / kRowsPerBlock), dim3(kNT), 0,
+                     st, a, rows);
+  e = hipGetLastError();
+  timing_end(kFwdMerge, st);
+  return e;
 }
 
 template <typename Tag, int D>
@@ -500,6 +583,15 @@ hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a,
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)
                  : launch_d<f16_tag, 128>(causal, sparse, bh, a, st);
+}
+
+hipError_t launch_fwd_split(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
+  a.nqb = (a.n + kBR - 1) / kBR;
+  a.nbh = bh;
+  a.nblk = a.nqb * bh * a.nsplit;
+  if (dt == Dt::BF16) return d == 64 ? launch_split_d<bf16_tag, 64>(causal, a, st)
+                                     : launch_split_d<bf16_tag, 128>(causal, a, st);
+  return d == 64 ? launch_split_d<f16_tag, 64>(causal, a, st) : launch_split_d<f16_tag, 128>(causal, a, st);
 }
 
 }  // namespace fa

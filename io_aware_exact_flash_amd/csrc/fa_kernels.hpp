@@ -23,6 +23,11 @@ struct FwdArgs {
   int nqb;               // query blocks per head
   int nblk;              // total workgroups
   float c;               // scale * log2(e)
+  // split-KV forward only
+  int nsplit;            // key ranges per query row
+  int nbh;               // B*H
+  float* po;             // [nsplit][B*H][N][d] partial outputs, each normalised by its own l
+  float* plse;           // [nsplit][B*H][N] partial log-sum-exp (-inf: no key in the range)
 };
 
 struct BwdArgs {
@@ -49,7 +54,9 @@ struct BwdArgs {
 };
 
 // Kernel classes for the optional per-kernel timing hooks.
-enum KernelId : int { kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kNumKernels = 5 };
+enum KernelId : int {
+  kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kFwdSplit = 5, kFwdMerge = 6, kNumKernels = 7
+};
 
 // Bracket one launch with events on its stream when timing is enabled
 // (no-ops otherwise).  Defined in fa_api.cpp.
@@ -59,6 +66,9 @@ void timing_end(int kernel, hipStream_t st);
 // Launchers return hipGetLastError() after the launch.
 hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st);
 hipError_t launch_fwd_f32(int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st);
+// Split-KV forward (a.nsplit key ranges per row, partials in a.po / a.plse)
+// followed by the merge into a.o / a.lse.
+hipError_t launch_fwd_split(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st);
 
 }  // namespace fa

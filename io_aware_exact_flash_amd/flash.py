@@ -34,13 +34,15 @@ SIGNATURES = {
     "flash_attn_blocksparse_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _U8P, _I, _P, _P, _P]),
     "flash_attn_blocksparse_bwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _U8P, _I,
                                         _P, _P, _P, _P, _Z, _P]),
+    "flash_attn_fwd_splitkv_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "flash_attn_fwd_splitkv": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _I, _P, _P, _P, _Z, _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
     "flash_attn_timing_collect": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), _I]),
     "flash_attn_kernel_name": (ctypes.c_char_p, [_I]),
 }
-KERNELS = 5  # timing classes: fwd, fwd_f32, bwd_pre, bwd_dkdv, bwd_dq
+KERNELS = 7  # timing classes: fwd, fwd_f32, bwd_pre, bwd_dkdv, bwd_dq, fwd_split, fwd_merge
 
 _lib = None
 _lock = threading.Lock()
@@ -135,6 +137,24 @@ def fwd(q, k, v, scale=None, causal=False):
     _check(lib().flash_attn_fwd(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 _scale(scale, d), int(bool(causal)), o.data_ptr(), lse.data_ptr(),
                                 _stream(q)))
+    return o, lse
+
+
+def fwd_splitkv_workspace_size(B, H, N, d, num_splits, dtype=torch.bfloat16) -> int:
+    return int(lib().flash_attn_fwd_splitkv_workspace_size(B, H, N, d, _DT[dtype], int(num_splits)))
+
+
+def fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, workspace=None):
+    """(O, LSE) = flash_attn_fwd_splitkv(q, k, v, scale, causal, num_splits)."""
+    B, H, N, d, dt = _shape(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = fwd_splitkv_workspace_size(B, H, N, d, num_splits, q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().flash_attn_fwd_splitkv(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        _scale(scale, d), int(bool(causal)), int(num_splits), o.data_ptr(),
+                                        lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
     return o, lse
 
 

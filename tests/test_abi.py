@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_blocksparse_fwd",
-                     "flash_attn_blocksparse_bwd", "flash_attn_bwd_workspace_size"):
+                     "flash_attn_blocksparse_bwd", "flash_attn_bwd_workspace_size",
+                     "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_size"):
         assert required in names
 
 
@@ -127,6 +128,47 @@ def test_blocksparse_validation():
                                           None) == flash.FA_ERR_UNSUPPORTED
     assert lib.flash_attn_blocksparse_bwd(*bargs, None, 128, FAKE, FAKE, FAKE, FAKE, 1 << 20,
                                           None) == flash.FA_ERR_INVALID_ARGUMENT
+
+
+def _split(ws_bytes=None, **kw):
+    a = dict(B=1, H=2, N=300, d=128, dt=flash.FA_BF16, scale=0.1, causal=1, splits=3)
+    a.update(kw)
+    need = flash.lib().flash_attn_fwd_splitkv_workspace_size(a["B"], a["H"], a["N"], a["d"], a["dt"],
+                                                             a["splits"])
+    ptr = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE)
+    ptr.update({k: v for k, v in kw.items() if k in ptr})
+    return flash.lib().flash_attn_fwd_splitkv(a["B"], a["H"], a["N"], a["d"], a["dt"], ptr["q"], ptr["k"],
+                                              ptr["v"], a["scale"], a["causal"], a["splits"], ptr["o"],
+                                              ptr["lse"], ptr["ws"], need if ws_bytes is None else ws_bytes,
+                                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=0, ws_bytes=1 << 20), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(splits=65, ws_bytes=1 << 30), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=flash.FA_F32), flash.FA_ERR_UNSUPPORTED),
+    (dict(d=80, ws_bytes=1 << 20), flash.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=FAKE_MISALIGNED), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), flash.FA_ERR_INVALID_ARGUMENT),
+])
+def test_splitkv_validation(kw, code):
+    assert _split(**kw) == code
+    assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_fwd_splitkv:")
+
+
+def test_splitkv_workspace_size_and_too_small():
+    lib = flash.lib()
+    # 3 float32 partial outputs [B*H][N][d] (rounded to 256 bytes), then 3 partial LSE [B*H][N]
+    po = 3 * 2 * 300 * 128 * 4
+    assert lib.flash_attn_fwd_splitkv_workspace_size(1, 2, 300, 128, flash.FA_BF16, 3) == \
+        ((po + 255) // 256) * 256 + 3 * 2 * 300 * 4
+    assert lib.flash_attn_fwd_splitkv_workspace_size(1, 2, 0, 128, flash.FA_BF16, 3) == 0
+    assert lib.flash_attn_fwd_splitkv_workspace_size(1, 2, 300, 128, flash.FA_BF16, 0) == 0
+    need = lib.flash_attn_fwd_splitkv_workspace_size(1, 2, 300, 128, flash.FA_BF16, 3)
+    assert _split(ws_bytes=need - 1) == flash.FA_ERR_WORKSPACE_TOO_SMALL
+    # empty problems succeed without a launch
+    assert _split(N=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == flash.FA_OK
 
 
 def test_python_binding_refuses_cpu_tensors():
