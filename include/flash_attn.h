@@ -12,7 +12,7 @@
  *          (forward), Algorithm 2 (backward), eqs. (5)-(7) online softmax,
  *          eqs. (10)-(16) deferred normalisation and log-sum-exp, eq. (17)
  *          and eqs. (27)-(30) softmax Jacobian, "Causal mask optimisation",
- *          "Reproducibility notes" (FLOP convention).
+ *          "MQA and GQA support", "Reproducibility notes" (FLOP convention).
  *   [FA1]  FlashAttention paper summary (zhaifeiyue.github.io/papers/
  *          2205.14135): Technique 1 (tiling), Technique 2 (recomputation,
  *          D_i = do_i . o_i), Block-Sparse FlashAttention.
@@ -168,6 +168,35 @@ fa_status flash_attn_blocksparse_bwd(int B, int H, int N, int d, fa_dtype dtype,
                                      void* dq, void* dk, void* dv,
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * Grouped K/V heads [FA2 "MQA and GQA support"]: flash_attn_fwd and
+ * flash_attn_bwd with Hkv K/V heads shared by H query heads (Hkv = 1 is
+ * multi-query attention, Hkv = H the plain calls).  H must be a multiple of
+ * Hkv (H = 0 requires Hkv = 0; FA_ERR_INVALID_ARGUMENT otherwise).  Query
+ * head i of a batch reads K/V head floor(i / (H / Hkv)): each run of H / Hkv
+ * consecutive query heads forms one group, whose K/V head the kernels index
+ * in place (K and V are never copied or broadcast).
+ *   q, o, dout, dq   [B][H][N][d]   dtype
+ *   lse              [B][H][N]      float32
+ *   k, v, dk, dv     [B][Hkv][N][d] dtype
+ * dK and dV of a K/V head are sums over the query heads of its group; the
+ * dK/dV pass forms them by sweeping the group's heads into the same
+ * accumulators (no extra buffer or launch).  The backward workspace is
+ * flash_attn_bwd_workspace_size(B, H, N, d, dtype) (one entry per query
+ * row).  Other arguments, dtypes and errors as flash_attn_fwd and
+ * flash_attn_bwd.
+ */
+fa_status flash_attn_fwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype,
+                             const void* q, const void* k, const void* v,
+                             float scale, int causal,
+                             void* o, float* lse, hipStream_t stream);
+fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype,
+                             const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             float scale, int causal,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Per-kernel timing (diagnostics; not part of the method).  While enabled,

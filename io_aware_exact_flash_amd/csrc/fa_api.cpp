@@ -77,6 +77,15 @@ fa_status check_ptrs(const char* fn, const void* const* ptrs, const char* const*
   return FA_OK;
 }
 
+// Grouped K/V heads: Hkv K/V heads serve H query heads, H / Hkv each.
+fa_status check_heads(const char* fn, int H, int Hkv) {
+  if (Hkv < 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s: negative Hkv (%d)", fn, Hkv);
+  if (H == 0 ? Hkv != 0 : (Hkv == 0 || H % Hkv != 0))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: H = %d query heads cannot share Hkv = %d K/V heads evenly", fn, H,
+                Hkv);
+  return FA_OK;
+}
+
 fa_status check_mask(const char* fn, const uint8_t* mask, int mask_block) {
   if (!mask) return fail(FA_ERR_INVALID_ARGUMENT, "%s: block_mask is null", fn);
   if (mask_block != fa::kMaskBlockTokens)
@@ -101,12 +110,13 @@ size_t workspace_bytes(long long bh, long long n) {
   return 2 * ws_array_bytes(bh, n);
 }
 
-fa_status run_fwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q,
+fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
                   const void* k, const void* v, float scale, int causal, const uint8_t* mask,
                   int mask_block, bool sparse, void* o, float* lse, hipStream_t stream) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, false, &p);
   if (s != FA_OK) return s;
+  if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
   if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
   if (p.empty) return FA_OK;
   const void* ptrs[] = {q, k, v, o, lse};
@@ -123,6 +133,8 @@ fa_status run_fwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, co
   a.mask_t = (N + fa::kMaskBlockTokens - 1) / fa::kMaskBlockTokens;
   a.n = N;
   a.c = scale * 1.4426950408889634f;
+  a.hq = H;
+  a.grp = H / Hkv;
   hipError_t e = (dtype == FA_F32)
                      ? fa::launch_fwd_f32(d, causal != 0, sparse, p.bh, a, stream)
                      : fa::launch_fwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0,
@@ -130,13 +142,14 @@ fa_status run_fwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, co
   return hip_status(fn, e);
 }
 
-fa_status run_bwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q,
+fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
                   const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   float scale, int causal, const uint8_t* mask, int mask_block, bool sparse,
                   void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, true, &p);
   if (s != FA_OK) return s;
+  if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
   if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
   if (p.empty) return FA_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
@@ -163,6 +176,8 @@ fa_status run_bwd(const char* fn, int B, int H, int N, int d, fa_dtype dtype, co
   a.n = N;
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
+  a.hq = H;
+  a.grp = H / Hkv;
   hipError_t e = fa::launch_bwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, sparse,
                                 p.bh, a, stream);
   return hip_status(fn, e);
@@ -209,6 +224,8 @@ fa_status run_fwd_split(const char* fn, int B, int H, int N, int d, fa_dtype dty
   a.mask_t = 0;
   a.n = N;
   a.c = scale * 1.4426950408889634f;
+  a.hq = H;
+  a.grp = 1;
   a.nsplit = splits;
   a.po = static_cast<float*>(ws);
   a.plse = reinterpret_cast<float*>(static_cast<char*>(ws) + splitkv_po_bytes(p.bh, N, d, splits));
@@ -306,7 +323,7 @@ FA_EXPORT int flash_attn_abi_version(void) { return 1; }
 FA_EXPORT fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype, const void* q,
                                    const void* k, const void* v, float scale, int causal, void* o,
                                    float* lse, hipStream_t stream) {
-  return run_fwd("flash_attn_fwd", B, H, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o,
+  return run_fwd("flash_attn_fwd", B, H, H, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o,
                  lse, stream);
 }
 
@@ -337,7 +354,7 @@ FA_EXPORT fa_status flash_attn_bwd(int B, int H, int N, int d, fa_dtype dtype, c
                                    const float* lse, float scale, int causal, void* dq, void* dk,
                                    void* dv, void* workspace, size_t workspace_bytes_,
                                    hipStream_t stream) {
-  return run_bwd("flash_attn_bwd", B, H, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr,
+  return run_bwd("flash_attn_bwd", B, H, H, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr,
                  0, false, dq, dk, dv, workspace, workspace_bytes_, stream);
 }
 
@@ -346,7 +363,7 @@ FA_EXPORT fa_status flash_attn_blocksparse_fwd(int B, int H, int N, int d, fa_dt
                                                float scale, int causal, const uint8_t* block_mask,
                                                int mask_block, void* o, float* lse,
                                                hipStream_t stream) {
-  return run_fwd("flash_attn_blocksparse_fwd", B, H, N, d, dtype, q, k, v, scale, causal, block_mask,
+  return run_fwd("flash_attn_blocksparse_fwd", B, H, H, N, d, dtype, q, k, v, scale, causal, block_mask,
                  mask_block, true, o, lse, stream);
 }
 
@@ -357,9 +374,24 @@ FA_EXPORT fa_status flash_attn_blocksparse_bwd(int B, int H, int N, int d, fa_dt
                                                int mask_block, void* dq, void* dk, void* dv,
                                                void* workspace, size_t workspace_bytes_,
                                                hipStream_t stream) {
-  return run_bwd("flash_attn_blocksparse_bwd", B, H, N, d, dtype, q, k, v, o, dout, lse, scale,
+  return run_bwd("flash_attn_blocksparse_bwd", B, H, H, N, d, dtype, q, k, v, o, dout, lse, scale,
                  causal, block_mask, mask_block, true, dq, dk, dv, workspace, workspace_bytes_,
                  stream);
+}
+
+FA_EXPORT fa_status flash_attn_fwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
+                                       const void* k, const void* v, float scale, int causal, void* o,
+                                       float* lse, hipStream_t stream) {
+  return run_fwd("flash_attn_fwd_gqa", B, H, Hkv, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o,
+                 lse, stream);
+}
+
+FA_EXPORT fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
+                                       const void* k, const void* v, const void* o, const void* dout,
+                                       const float* lse, float scale, int causal, void* dq, void* dk, void* dv,
+                                       void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  return run_bwd("flash_attn_bwd_gqa", B, H, Hkv, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0,
+                 false, dq, dk, dv, workspace, workspace_bytes_, stream);
 }
 
 FA_EXPORT const char* flash_attn_status_string(fa_status status) {

@@ -106,15 +106,27 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // tiles (low key blocks see the most queries).
   const int per = CAUSAL ? (a.nkb + 1) / 2 : a.nkb;
   const int lb = xcd_remap(blockIdx.x, a.nblk_kv);
-  const int bh = lb / per;
+  const int bh = lb / per;  // K/V head, an index over B x Hkv
   const int pk_ = lb % per;
   const size_t hoff = (size_t)bh * n * D;
-  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
-  const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
-  const float* __restrict__ Ltg = a.lt + (size_t)bh * n;
-  const float* __restrict__ Dg = a.dvec + (size_t)bh * n;
+  // Grouped heads: the grp consecutive query heads that read this K/V head
+  // each contribute to dK and dV; the workgroup sweeps them one after the
+  // other into the same accumulators.
+  const int hkv = a.hq / a.grp;
+  const int qbh0 = a.grp == 1 ? bh : (bh / hkv) * a.hq + (bh % hkv) * a.grp;
+  const uint16_t* Qg = nullptr;
+  const uint16_t* dOg = nullptr;
+  const float* Ltg = nullptr;
+  const float* Dg = nullptr;
+  auto set_head = [&](int hg) {
+    const size_t qh = (size_t)(qbh0 + hg);
+    Qg = reinterpret_cast<const uint16_t*>(a.q) + qh * n * D;
+    dOg = reinterpret_cast<const uint16_t*>(a.dout) + qh * n * D;
+    Ltg = a.lt + qh * n;
+    Dg = a.dvec + qh * n;
+  };
 
   auto run = [&](const int kb) {
     const int k0 = kb * BKV;
@@ -168,9 +180,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // (The addressing of the tile being loaded is set once per tile, in
     // dma_set() below.)
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
-    const uint16_t* d_q = Qg;
-    const uint16_t* d_o = dOg;
-    const float* d_ld = Ltg;  // this lane's L or D source (lanes 0-15)
+    const uint16_t* d_q = nullptr;
+    const uint16_t* d_o = nullptr;
+    const float* d_ld = nullptr;  // this lane's L or D source (lanes 0-15)
     int d_last = 0;
     uint32_t d_lds = 0, d_slot = 0;
     const int rrow = TL::row_base(c32, g);
@@ -201,12 +213,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       sq = slot_next(sq);
       dma_set();
     };
-    dma_set();
-    for (int t = 0; t < kRing - 1; ++t) {
-#pragma unroll
-      for (int u = 0; u < C; ++u) dma_tile(u);
-      dma_advance();
-    }
 
     f32x16 dkacc[NB], dvacc[NB];
 #pragma unroll
@@ -251,14 +257,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    // the first tile's products, then the pipelined sweep
-    vm_wait<2 * C>();
-    __syncthreads();
-    int i = i_first;
-    int so = 0;  // slot of tile i
-    prod(std::integral_constant<int, 0>{}, so, [](int) {});
-    vgpr_drain(s);
-    vgpr_drain(dp);
+    int i = i_first;  // the tile in set X
+    int so = 0;       // its slot
 
     // Iteration over tile i (set X) with the next tile in (set Y = 1 - X):
     //   part A: S, dP of in                   | P, dS of i, DMA
@@ -375,17 +375,41 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       if constexpr (CAUSAL) n_pre = min((w + 2) & ~1, (T + 1) & ~1);
       n_plain = max(n / BQ - (i_first + n_pre), 0) & ~1;
     }
-    for (int t = 0; t < n_pre; t += 2) {
-      step(std::integral_constant<int, 0>{}, std::true_type{});
-      step(std::integral_constant<int, 1>{}, std::true_type{});
-    }
-    for (int t = 0; t < n_plain; t += 2) {
-      step(std::integral_constant<int, 0>{}, std::false_type{});
-      step(std::integral_constant<int, 1>{}, std::false_type{});
-    }
-    while (i < n_tiles) {
-      step(std::integral_constant<int, 0>{}, std::true_type{});
-      step(std::integral_constant<int, 1>{}, std::true_type{});
+#pragma clang loop unroll(disable)
+    for (int hg = 0; hg < a.grp; ++hg) {
+      if (hg) {
+        vm_wait<0>();     // the previous head's DMA has landed ...
+        __syncthreads();  // ... and every wave is out of its LDS tiles
+      }
+      set_head(hg);
+      iq = i_first;
+      sq = 0;
+      dma_set();
+      for (int t = 0; t < kRing - 1; ++t) {
+#pragma unroll
+        for (int u = 0; u < C; ++u) dma_tile(u);
+        dma_advance();
+      }
+      // the first tile's products, then the pipelined sweep
+      vm_wait<2 * C>();
+      __syncthreads();
+      i = i_first;
+      so = 0;
+      prod(std::integral_constant<int, 0>{}, so, [](int) {});
+      vgpr_drain(s);
+      vgpr_drain(dp);
+      for (int t = 0; t < n_pre; t += 2) {
+        step(std::integral_constant<int, 0>{}, std::true_type{});
+        step(std::integral_constant<int, 1>{}, std::true_type{});
+      }
+      for (int t = 0; t < n_plain; t += 2) {
+        step(std::integral_constant<int, 0>{}, std::false_type{});
+        step(std::integral_constant<int, 1>{}, std::false_type{});
+      }
+      while (i < n_tiles) {
+        step(std::integral_constant<int, 0>{}, std::true_type{});
+        step(std::integral_constant<int, 1>{}, std::true_type{});
+      }
     }
 
     agpr_drain(dkacc);
@@ -473,9 +497,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   const int bh = lb / per;
   const int pq_ = lb % per;
   const size_t hoff = (size_t)bh * n * D;
+  const size_t kvoff = (size_t)kv_head(bh, a.hq, a.grp) * n * D;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
-  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
-  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
   const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
 
   auto run = [&](const int qb) {
@@ -902,7 +927,7 @@ hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a,
   a.nqb = (a.n + kDqRows - 1) / kDqRows;
   a.nblk_q = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   a.nkb = (a.n + 127) / 128;
-  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * bh;
+  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.grp);  // per K/V head
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)

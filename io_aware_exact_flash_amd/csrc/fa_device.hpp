@@ -379,4 +379,11 @@ __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
 }
 
+// K/V head read by query head bh (an index over B x H) when grp consecutive
+// query heads share one K/V head: batch bh / hq, head bh % hq reads K/V head
+// (bh % hq) / grp of the hq / grp heads of that batch.
+__device__ __forceinline__ int kv_head(int bh, int hq, int grp) {
+  return grp == 1 ? bh : (bh / hq) * (hq / grp) + (bh % hq) / grp;
+}
+
 }  // namespace fa

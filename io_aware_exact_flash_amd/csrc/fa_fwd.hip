@@ -88,9 +88,10 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   const int bh = (lb / nsp) / per;
   const int pb_ = (lb / nsp) % per;
   const size_t hoff = (size_t)bh * n * D;
+  const size_t kvoff = (size_t)kv_head(bh, a.hq, a.grp) * n * D;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
-  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
-  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
 
   auto run = [&](const int qb) {
     const int q0 = qb * kBR;

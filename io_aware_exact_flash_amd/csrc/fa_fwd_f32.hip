@@ -34,8 +34,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   const int qb = a.nqb - 1 - (lb % a.nqb);
   const size_t hoff = (size_t)bh * n * D;
   const float* __restrict__ Q = reinterpret_cast<const float*>(a.q) + hoff;
-  const float* __restrict__ K = reinterpret_cast<const float*>(a.k) + hoff;
-  const float* __restrict__ V = reinterpret_cast<const float*>(a.v) + hoff;
+  const size_t kvoff = (size_t)kv_head(bh, a.hq, a.grp) * n * D;
+  const float* __restrict__ K = reinterpret_cast<const float*>(a.k) + kvoff;
+  const float* __restrict__ V = reinterpret_cast<const float*>(a.v) + kvoff;
   const int q0 = qb * 32;
   const int my_q = q0 + c32;
 

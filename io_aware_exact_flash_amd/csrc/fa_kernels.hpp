@@ -23,6 +23,9 @@ struct FwdArgs {
   int nqb;               // query blocks per head
   int nblk;              // total workgroups
   float c;               // scale * log2(e)
+  // grouped K/V heads: query head i of a batch reads K/V head i / grp
+  int hq;                // query heads per batch (H)
+  int grp;               // query heads per K/V head (H / Hkv; 1 = one K/V head per query head)
   // split-KV forward only
   int nsplit;            // key ranges per query row
   int nbh;               // B*H
@@ -51,6 +54,10 @@ struct BwdArgs {
   int nkb;               // key blocks per head (dK/dV pass)
   float scale;
   float c;               // scale * log2(e)
+  // grouped K/V heads (as in FwdArgs): the dK/dV pass runs per K/V head and
+  // sums over the grp query heads that share it
+  int hq;
+  int grp;
 };
 
 // Kernel classes for the optional per-kernel timing hooks.

@@ -36,6 +36,9 @@ SIGNATURES = {
                                         _P, _P, _P, _P, _Z, _P]),
     "flash_attn_fwd_splitkv_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "flash_attn_fwd_splitkv": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _I, _P, _P, _P, _Z, _P]),
+    "flash_attn_fwd_gqa": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _P, _P, _P]),
+    "flash_attn_bwd_gqa": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _P, _Z,
+                                _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
@@ -98,6 +101,15 @@ def _shape(q: torch.Tensor, *others: torch.Tensor):
             raise ValueError("tensors must be contiguous [B, H, N, d]")
     B, H, N, d = q.shape
     return B, H, N, d, _DT[q.dtype]
+
+
+def _shape_gqa(q, k, v, *per_query):
+    """q (and o, dout) [B, H, N, d]; k, v [B, Hkv, N, d] with Hkv dividing H."""
+    B, H, N, d, dt = _shape(q, *per_query)
+    B2, Hkv, N2, d2, _ = _shape(k, v)
+    if (B2, N2, d2) != (B, N, d) or k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k, v must be [B, Hkv, N, d] with the batch, length, head size, dtype and device of q")
+    return B, H, Hkv, N, d, dt
 
 
 def _scale(scale, d):
@@ -205,4 +217,28 @@ def blocksparse_bwd(q, k, v, o, dout, lse, block_mask, scale=None, causal=False,
                                             _scale(scale, d), int(bool(causal)), block_mask.data_ptr(),
                                             MASK_BLOCK, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                             ws.data_ptr(), nbytes, _stream(q)))
+    return dq, dk, dv
+
+
+def fwd_gqa(q, k, v, scale=None, causal=False):
+    """(O, LSE) = flash_attn_fwd_gqa(q [B,H,N,d], k, v [B,Hkv,N,d], scale, causal)."""
+    B, H, Hkv, N, d, dt = _shape_gqa(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib().flash_attn_fwd_gqa(B, H, Hkv, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    _scale(scale, d), int(bool(causal)), o.data_ptr(), lse.data_ptr(),
+                                    _stream(q)))
+    return o, lse
+
+
+def bwd_gqa(q, k, v, o, dout, lse, scale=None, causal=False, workspace=None):
+    """(dQ, dK, dV) = flash_attn_bwd_gqa(...); dK, dV have the shape of k, v."""
+    B, H, Hkv, N, d, dt = _shape_gqa(q, k, v, o, dout)
+    _lse_ok(lse, q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws, nbytes = _workspace(q) if workspace is None else (workspace, workspace.numel())
+    _check(lib().flash_attn_bwd_gqa(B, H, Hkv, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    o.data_ptr(), dout.data_ptr(), lse.data_ptr(), _scale(scale, d),
+                                    int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    ws.data_ptr(), nbytes, _stream(q)))
     return dq, dk, dv

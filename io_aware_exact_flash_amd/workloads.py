@@ -10,6 +10,9 @@ Recipe (one generator per purpose, CPU ``torch.Generator``):
   iid N(0, 1) float32 ``[B, H, N, d]``, multiplies by ``gain`` and rounds to
   ``dtype``.  The bench workloads use seed = workload number and gain 0.5
   only for the 8192-token causal workload.
+* ``qkvdo_grouped(B, H, Hkv, N, d, dtype, seed, gain)`` draws the same way
+  Q ``[B, H, N, d]``, K and V ``[B, Hkv, N, d]``, dO ``[B, H, N, d]``, in
+  that order (grouped K/V heads).
 * ``block_mask(T, density, seed)`` keeps every diagonal block and each
   off-diagonal block with probability p = (density T^2 - T) / (T^2 - T), so
   the expected kept fraction is ``density``; drawn as ``rand(T, T) < p``.
@@ -48,6 +51,18 @@ def qkvdo(B, H, N, d, dtype="bf16", seed=0, gain=1.0):
     out = []
     for _ in range(4):
         x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+        if gain != 1.0:
+            x = x * gain
+        out.append(x.to(_DTYPES[dtype]))
+    return tuple(out)
+
+
+def qkvdo_grouped(B, H, Hkv, N, d, dtype="bf16", seed=0, gain=1.0):
+    """Q, K, V, dO as CPU tensors of ``dtype``; K and V have Hkv heads."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = []
+    for heads in (H, Hkv, Hkv, H):
+        x = torch.randn((B, heads, N, d), generator=g, dtype=torch.float32)
         if gain != 1.0:
             x = x * gain
         out.append(x.to(_DTYPES[dtype]))

@@ -158,3 +158,50 @@ def grad_q_rows(q, k, v, do, scale, causal=False, block_mask=None, mask_block=MA
     rowdot = (P * dP).sum(axis=1)
     dS = P * (dP - rowdot[:, None])
     return scale * (dS @ k)
+
+
+# ---------------------------------------------------------------- grouped K/V heads
+# FlashAttention-2 notes, "MQA and GQA support": query heads are split into
+# groups that each read one shared K/V head (one group: multi-query
+# attention; one head per group: ordinary multi-head attention).  The notes
+# give the group of query head i as a floor division of i by the group
+# parameter; read with H / Hkv query heads per group, head i belongs to group
+# i // (H / Hkv), i.e. runs of consecutive heads share a K/V head.
+
+def kv_head_of(h: int, H: int, Hkv: int) -> int:
+    """K/V head read by query head h when Hkv K/V heads serve H query heads."""
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"H={H} query heads cannot share Hkv={Hkv} K/V heads evenly")
+    return h // (H // Hkv)
+
+
+def forward_gqa(q, k, v, scale, causal=False, heads=None):
+    """q [B, H, N, d], k, v [B, Hkv, N, d] -> {(b, h): (O, LSE)}: each query
+    head attends over its group's K/V head."""
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    return {(b, h): forward_head(q[b, h], k[b, kv_head_of(h, H, Hkv)], v[b, kv_head_of(h, H, Hkv)],
+                                 scale, causal)
+            for (b, h) in _heads(B, H, heads)}
+
+
+def backward_gqa(q, k, v, do, scale, causal=False):
+    """Gradients of sum(O o dO) with grouped K/V heads.
+
+    Returns (dq {(b, h)}, dk {(b, hk)}, dv {(b, hk)}).  A shared K/V head
+    enters the loss once per query head of its group, so its gradient is the
+    sum of those heads' per-head gradients (the notes' backward reduction over
+    the group)."""
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    dq = {}
+    dk = {(b, g): np.zeros(k.shape[2:], dtype=np.float64) for b in range(B) for g in range(Hkv)}
+    dv = {(b, g): np.zeros(v.shape[2:], dtype=np.float64) for b in range(B) for g in range(Hkv)}
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            gq, gk, gv = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dq[(b, h)] = gq
+            dk[(b, g)] += gk
+            dv[(b, g)] += gv
+    return dq, dk, dv

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_blocksparse_fwd",
                      "flash_attn_blocksparse_bwd", "flash_attn_bwd_workspace_size",
-                     "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_size"):
+                     "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_size",
+                     "flash_attn_fwd_gqa", "flash_attn_bwd_gqa"):
         assert required in names
 
 
@@ -169,6 +170,42 @@ def test_splitkv_workspace_size_and_too_small():
     assert _split(ws_bytes=need - 1) == flash.FA_ERR_WORKSPACE_TOO_SMALL
     # empty problems succeed without a launch
     assert _split(N=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == flash.FA_OK
+
+
+def _gqa_fwd(H, Hkv, **kw):
+    a = dict(B=1, N=256, d=64, dt=flash.FA_BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE)
+    a.update(kw)
+    return flash.lib().flash_attn_fwd_gqa(a["B"], H, Hkv, a["N"], a["d"], a["dt"], a["q"], a["k"], a["v"],
+                                          0.125, 1, a["o"], a["lse"], None)
+
+
+def _gqa_bwd(H, Hkv, **kw):
+    a = dict(B=1, N=256, d=128, dt=flash.FA_BF16)
+    a.update(kw)
+    need = flash.lib().flash_attn_bwd_workspace_size(a["B"], H, a["N"], a["d"], a["dt"])
+    p = [FAKE] * 9
+    if kw.get("null_dk"):
+        p[7] = None
+    return flash.lib().flash_attn_bwd_gqa(a["B"], H, Hkv, a["N"], a["d"], a["dt"], *p[:6], 0.125, 0,
+                                          *p[6:], FAKE, need, None)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 3), (4, 0), (4, -1), (4, 8), (0, 1)])
+def test_gqa_head_validation(H, Hkv):
+    # Hkv must divide H (and be 0 exactly when H is): checked before any launch
+    assert _gqa_fwd(H, Hkv) == flash.FA_ERR_INVALID_ARGUMENT
+    assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_fwd_gqa:")
+    assert _gqa_bwd(H, Hkv) == flash.FA_ERR_INVALID_ARGUMENT
+    assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_bwd_gqa:")
+
+
+def test_gqa_other_checks_and_empty_problems():
+    assert _gqa_fwd(4, 2, d=96) == flash.FA_ERR_UNSUPPORTED
+    assert _gqa_bwd(4, 2, dt=flash.FA_F32) == flash.FA_ERR_UNSUPPORTED
+    assert _gqa_bwd(4, 1, null_dk=True) == flash.FA_ERR_INVALID_ARGUMENT
+    assert _gqa_fwd(4, 2, v=FAKE_MISALIGNED) == flash.FA_ERR_INVALID_ARGUMENT
+    assert _gqa_fwd(0, 0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
+    assert _gqa_fwd(4, 2, N=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -416,3 +416,71 @@ def test_row_restricted_dq_by_finite_differences(causal):
             fm = _loss(q, k, v, do, 0.6, causal, None, 128)
             q[i, t] = old
             assert abs((fp - fm) / (2 * h) - g[a, t]) <= 1e-6 * max(1.0, np.abs(g).max())
+
+
+# ------------------------------------------------------- P9 grouped K/V heads
+def test_gqa_group_map():
+    """FA2 notes, "MQA and GQA support": a single K/V head serves every query
+    head (MQA); one K/V head per query head is plain multi-head attention;
+    otherwise runs of H / Hkv consecutive query heads share one K/V head."""
+    assert [A.kv_head_of(h, 8, 1) for h in range(8)] == [0] * 8
+    assert [A.kv_head_of(h, 8, 8) for h in range(8)] == list(range(8))
+    assert [A.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [A.kv_head_of(h, 6, 3) for h in range(6)] == [0, 0, 1, 1, 2, 2]
+    for H, Hkv in ((6, 4), (4, 0), (3, -1)):
+        with pytest.raises(ValueError):
+            A.kv_head_of(0, H, Hkv)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_forward_against_broadcast_bruteforce(H, Hkv, causal):
+    """Grouped forward equals pure-Python attention over K/V heads broadcast
+    to every query head (the copy the notes say the kernels avoid)."""
+    r = _rng(100 + 10 * H + Hkv + causal)
+    B, n, d = 2, 5, 3
+    q = r.standard_normal((B, H, n, d))
+    k = r.standard_normal((B, Hkv, n, d))
+    v = r.standard_normal((B, Hkv, n, d))
+    krep = np.repeat(k, H // Hkv, axis=1)  # [B, H, n, d]
+    vrep = np.repeat(v, H // Hkv, axis=1)
+    got = A.forward_gqa(q, k, v, 0.6, causal)
+    ok = (lambda i, j: j <= i) if causal else (lambda i, j: True)
+    for b in range(B):
+        for h in range(H):
+            O, L = brute_attention(q[b, h].tolist(), krep[b, h].tolist(), vrep[b, h].tolist(), 0.6, ok)
+            np.testing.assert_allclose(got[(b, h)][0], O, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(got[(b, h)][1], L, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("H,Hkv,causal", [(4, 2, False), (3, 1, True), (2, 2, True)])
+def test_gqa_gradients_by_central_differences(H, Hkv, causal):
+    """dK, dV of a shared head sum over its group: checked against central
+    differences of the total loss sum_h sum(O_h o dO_h)."""
+    r = _rng(7 * H + Hkv)
+    B, n, d, s = 1, 4, 2, 0.8
+    q = r.standard_normal((B, H, n, d))
+    k = r.standard_normal((B, Hkv, n, d))
+    v = r.standard_normal((B, Hkv, n, d))
+    do = r.standard_normal((B, H, n, d))
+
+    def loss():
+        out = A.forward_gqa(q, k, v, s, causal)
+        return float(sum((out[(0, h)][0] * do[0, h]).sum() for h in range(H)))
+
+    dq, dk, dv = A.backward_gqa(q, k, v, do, s, causal)
+    G = {"q": np.stack([dq[(0, h)] for h in range(H)])[None],
+         "k": np.stack([dk[(0, g)] for g in range(Hkv)])[None],
+         "v": np.stack([dv[(0, g)] for g in range(Hkv)])[None]}
+    eps = 1e-6
+    for name, X in (("q", q), ("k", k), ("v", v)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            old = X[idx]
+            X[idx] = old + eps
+            fp = loss()
+            X[idx] = old - eps
+            fm = loss()
+            X[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        assert np.abs(num - G[name]).max() <= 1e-6 * max(1.0, np.abs(G[name]).max()), name

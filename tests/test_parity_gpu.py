@@ -249,3 +249,94 @@ def test_splitkv_forward(dtype, d, causal, shape, splits):
     tol = TOL[dtype]
     compare("O", o, O, tol["o"], REL_RMS[dtype])
     compare_lse("LSE", lse, L, tol["lse"])
+
+
+def _oracle_gqa(f64, s, causal):
+    q, k, v, do = f64
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    fw = A.forward_gqa(q, k, v, s, causal)
+    dQ, dK, dV = A.backward_gqa(q, k, v, do, s, causal)
+    O = np.stack([np.stack([fw[(b, h)][0] for h in range(H)]) for b in range(B)])
+    L = np.stack([np.stack([fw[(b, h)][1] for h in range(H)]) for b in range(B)])
+    gQ = np.stack([np.stack([dQ[(b, h)] for h in range(H)]) for b in range(B)])
+    gK = np.stack([np.stack([dK[(b, g)] for g in range(Hkv)]) for b in range(B)])
+    gV = np.stack([np.stack([dV[(b, g)] for g in range(Hkv)]) for b in range(B)])
+    return O, L, gQ, gK, gV
+
+
+GQA_SHAPES = [(1, 4, 1, 200), (2, 6, 2, 333), (1, 4, 4, 130), (1, 3, 1, 1), (2, 4, 2, 519),
+              (1, 16, 1, 300)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", GQA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gqa_forward_backward(dtype, d, causal, shape):
+    """Grouped K/V heads: each query head reads its group's K/V head in place;
+    dK and dV of a K/V head sum over the group.  A sum of G per-head
+    gradients with independent roundings has ~sqrt(G) times the error of one,
+    so the absolute gradient bound scales by sqrt(G)."""
+    B, H, Hkv, N = shape
+    G = H // Hkv
+    cpu = workloads.qkvdo_grouped(B, H, Hkv, N, d, dtype, seed=500 + N + d + H + Hkv)
+    q, k, v, do = (t.cuda() for t in cpu)
+    f64 = tuple(t.to(torch.float64).numpy() for t in cpu)
+    s = fp32_scale(d)
+    o, lse = flash.fwd_gqa(q, k, v, scale=s, causal=causal)
+    dq, dk, dv = flash.bwd_gqa(q, k, v, o, do, lse, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    assert dk.shape == k.shape and dv.shape == v.shape and dq.shape == q.shape
+    O, L, gQ, gK, gV = _oracle_gqa(f64, s, causal)
+    tol = TOL[dtype]
+    compare("O", o, O, tol["o"], REL_RMS[dtype])
+    compare_lse("LSE", lse, L, tol["lse"])
+    compare("dQ", dq, gQ, tol["grad"], REL_RMS[dtype])
+    compare("dK", dk, gK, tol["grad"] * max(1.0, G ** 0.5), REL_RMS[dtype])
+    compare("dV", dv, gV, tol["grad"] * max(1.0, G ** 0.5), REL_RMS[dtype])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_float32_forward(causal):
+    B, H, Hkv, N, d = 2, 6, 3, 150, 64
+    cpu = workloads.qkvdo_grouped(B, H, Hkv, N, d, "f32", seed=77)
+    q, k, v, _ = (t.cuda() for t in cpu)
+    f64 = tuple(t.to(torch.float64).numpy() for t in cpu)
+    s = fp32_scale(d)
+    o, lse = flash.fwd_gqa(q, k, v, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    O, L, *_ = _oracle_gqa(f64, s, causal)
+    compare("O", o, O, TOL["f32"]["o"], REL_RMS["f32"])
+    compare_lse("LSE", lse, L, TOL["f32"]["lse"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_matches_broadcast_heads_bitwise(causal):
+    """Reading the group's K/V head in place gives the same bits as the plain
+    calls on K/V copied out to every query head (forward and dQ), and one
+    K/V head per query head is the plain call."""
+    B, H, Hkv, N, d = 2, 8, 2, 700, 128
+    q, k, v, do = (t.cuda() for t in workloads.qkvdo_grouped(B, H, Hkv, N, d, "bf16", seed=91))
+    krep = k.repeat_interleave(H // Hkv, dim=1).contiguous()
+    vrep = v.repeat_interleave(H // Hkv, dim=1).contiguous()
+    o, lse = flash.fwd_gqa(q, k, v, causal=causal)
+    dq, dk, dv = flash.bwd_gqa(q, k, v, o, do, lse, causal=causal)
+    o2, lse2 = flash.fwd(q, krep, vrep, causal=causal)
+    dq2, _, _ = flash.bwd(q, krep, vrep, o2, do, lse2, causal=causal)
+    o3, lse3 = flash.fwd_gqa(q, krep, vrep, causal=causal)
+    dq3, dk3, dv3 = flash.bwd_gqa(q, krep, vrep, o3, do, lse3, causal=causal)
+    dq4, dk4, dv4 = flash.bwd(q, krep, vrep, o3, do, lse3, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(dq, dq2)
+    assert torch.equal(o3, o2) and torch.equal(dq3, dq4) and torch.equal(dk3, dk4) and torch.equal(dv3, dv4)
+
+
+def test_gqa_empty_inputs():
+    for B, H, Hkv, N in ((0, 4, 2, 64), (1, 0, 0, 64), (1, 4, 1, 0)):
+        q = torch.zeros((B, H, N, 64), dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros((B, Hkv, N, 64), dtype=torch.bfloat16, device="cuda")
+        o, lse = flash.fwd_gqa(q, k, k)
+        dq, dk, dv = flash.bwd_gqa(q, k, k, o, q, lse)
+        torch.cuda.synchronize()
+        assert o.shape == q.shape and dk.shape == k.shape
