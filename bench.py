@@ -226,6 +226,86 @@ def run_workload(num, steps, warmup, quiet=False):
     return w, res
 
 
+# Shapes for the variants that widen the path (timed with --variants; stderr
+# lines plus a "variants" object in the JSON line).  FLOPs as for the main
+# workloads (causal halved).
+VARIANTS = {
+    "splitkv": dict(name="split-KV forward, few heads", B=1, H=8, N=8192, d=128, dtype="bf16", causal=True,
+                    splits=(2, 4), seed=11),
+    "gqa": dict(name="grouped K/V heads (4 query heads per K/V head)", B=4, H=32, Hkv=8, N=4096, d=128,
+                dtype="bf16", causal=True, seed=12),
+    "mqa": dict(name="multi-query (one K/V head)", B=4, H=32, Hkv=1, N=4096, d=128,
+                dtype="bf16", causal=True, seed=13),
+}
+
+
+def time_ms(fn, steps, warmup):
+    """Average milliseconds of fn() over `steps` calls, bracketed by events on
+    torch's current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def run_variants(steps, warmup):
+    import torch
+    from io_aware_exact_flash_amd import flash, workloads
+
+    out = {}
+    v = VARIANTS["splitkv"]
+    q, k, vv, _ = (t.cuda() for t in workloads.qkvdo(v["B"], v["H"], v["N"], v["d"], v["dtype"], seed=v["seed"]))
+    f = 4.0 * v["B"] * v["H"] * v["N"] ** 2 * v["d"] * (0.5 if v["causal"] else 1.0)
+    res = {"plain": time_ms(lambda: flash.fwd(q, k, vv, causal=v["causal"]), steps, warmup)}
+    for sp in v["splits"]:
+        nb = flash.fwd_splitkv_workspace_size(v["B"], v["H"], v["N"], v["d"], sp, q.dtype)
+        ws = torch.empty(nb, dtype=torch.uint8, device=q.device)
+        res[f"splits_{sp}"] = time_ms(lambda: flash.fwd_splitkv(q, k, vv, sp, causal=v["causal"], workspace=ws),
+                                      steps, warmup)
+    out["splitkv"] = {"workload": f"{v['name']}: B={v['B']} H={v['H']} N={v['N']} d={v['d']} {v['dtype']} causal",
+                      "fwd_ms": {n: round(t, 4) for n, t in res.items()},
+                      "fwd_tflops": {n: round(f / (t * 1e-3) / 1e12, 1) for n, t in res.items()}}
+    log(f"variant splitkv: {out['splitkv']}")
+    del q, k, vv
+
+    for key in ("gqa", "mqa"):
+        v = VARIANTS[key]
+        q, k, vv, do = (t.cuda() for t in workloads.qkvdo_grouped(v["B"], v["H"], v["Hkv"], v["N"], v["d"],
+                                                                   v["dtype"], seed=v["seed"]))
+        krep = k.repeat_interleave(v["H"] // v["Hkv"], dim=1).contiguous()
+        vrep = vv.repeat_interleave(v["H"] // v["Hkv"], dim=1).contiguous()
+        ws = torch.empty(flash.bwd_workspace_size(v["B"], v["H"], v["N"], v["d"], q.dtype), dtype=torch.uint8,
+                         device=q.device)
+        wsg = torch.empty(flash.bwd_gqa_workspace_size(v["B"], v["H"], v["Hkv"], v["N"], v["d"], q.dtype),
+                          dtype=torch.uint8, device=q.device)
+        f = 4.0 * v["B"] * v["H"] * v["N"] ** 2 * v["d"] * (0.5 if v["causal"] else 1.0)
+        o, lse = flash.fwd_gqa(q, k, vv, causal=v["causal"])
+        c = v["causal"]
+        res = {
+            "broadcast_fwd": (time_ms(lambda: flash.fwd(q, krep, vrep, causal=c), steps, warmup), f),
+            "grouped_fwd": (time_ms(lambda: flash.fwd_gqa(q, k, vv, causal=c), steps, warmup), f),
+            "broadcast_bwd": (time_ms(lambda: flash.bwd(q, krep, vrep, o, do, lse, causal=c, workspace=ws),
+                                      steps, warmup), 2.5 * f),
+            "grouped_bwd": (time_ms(lambda: flash.bwd_gqa(q, k, vv, o, do, lse, causal=c, workspace=wsg),
+                                    steps, warmup), 2.5 * f),
+        }
+        out[key] = {"workload": f"{v['name']}: B={v['B']} H={v['H']} Hkv={v['Hkv']} N={v['N']} d={v['d']} "
+                                f"{v['dtype']} causal; broadcast_* = the plain calls on K/V copied to every head",
+                    "ms": {n: round(t, 4) for n, (t, _) in res.items()},
+                    "tflops": {n: round(fl / (t * 1e-3) / 1e12, 1) for n, (t, fl) in res.items()}}
+        log(f"variant {key}: {out[key]}")
+        del q, k, vv, do, krep, vrep, ws, wsg, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +316,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time every other workload (stderr lines)")
     ap.add_argument("--cpu-heads", type=int, default=10, help="(batch, head) pairs the oracle baseline runs (about 1 s each at N=8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the split-KV forward and grouped K/V heads (adds a 'variants' object)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy a device buffer of this many bytes 3 times "
                          "(calibrates the HBM byte counters of a profiling run)")
@@ -270,6 +352,7 @@ def main():
         log(f"copied {args.copy_bytes} bytes 3 times")
         del src, dst
 
+    variants = run_variants(args.steps, args.warmup) if args.variants else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_heads)
     line = {
         "metric": METRIC,
@@ -298,6 +381,8 @@ def main():
         "roofline": r["roofline"],
         "cpu_baseline": cpu,
     }
+    if variants is not None:
+        line["variants"] = variants
     print(json.dumps(line), flush=True)
 
 

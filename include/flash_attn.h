@@ -182,15 +182,21 @@ fa_status flash_attn_blocksparse_bwd(int B, int H, int N, int d, fa_dtype dtype,
  *   k, v, dk, dv     [B][Hkv][N][d] dtype
  * dK and dV of a K/V head are sums over the query heads of its group; the
  * dK/dV pass forms them by sweeping the group's heads into the same
- * accumulators (no extra buffer or launch).  The backward workspace is
- * flash_attn_bwd_workspace_size(B, H, N, d, dtype) (one entry per query
- * row).  Other arguments, dtypes and errors as flash_attn_fwd and
- * flash_attn_bwd.
+ * accumulators.  When B*Hkv*ceil(N/128) is too small to fill the GPU, each
+ * group is cut into up to H/Hkv ranges of heads swept by separate
+ * workgroups, whose float32 partial sums a reduction pass adds up (fixed
+ * order, so results are deterministic).  The backward workspace is
+ * flash_attn_bwd_gqa_workspace_size() bytes: the flash_attn_bwd workspace
+ * of the H query heads followed, when ranges are used, by the float32
+ * partial dK and dV; it depends on the shape only and returns 0 for
+ * empty or invalid shapes.  Other arguments, dtypes and errors as
+ * flash_attn_fwd and flash_attn_bwd.
  */
 fa_status flash_attn_fwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype,
                              const void* q, const void* k, const void* v,
                              float scale, int causal,
                              void* o, float* lse, hipStream_t stream);
+size_t flash_attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype dtype);
 fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype,
                              const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse,
@@ -206,8 +212,10 @@ fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype
  * launch count since the previous collect, and forgets them.  Kernel
  * classes: 0 forward (16-bit), 1 forward (float32), 2 backward D pre-pass,
  * 3 backward dK/dV pass, 4 backward dQ pass, 5 split-KV forward ranges,
- * 6 split-KV merge; flash_attn_kernel_name(k) names them.  Events are created on first use and reused; no device
- * memory is allocated.  Process-wide, guarded by a mutex.
+ * 6 split-KV merge, 7 dK/dV range sum (grouped heads);
+ * flash_attn_kernel_name(k) names them.  Events are created on first use
+ * and reused; no device memory is allocated.  Process-wide, guarded by a
+ * mutex.
  */
 fa_status flash_attn_timing_enable(int enable);
 fa_status flash_attn_timing_collect(double* total_ms, int* launches, int n);

@@ -109,6 +109,18 @@ size_t workspace_bytes(long long bh, long long n) {
   if (bh <= 0 || n <= 0) return 0;
   return 2 * ws_array_bytes(bh, n);
 }
+// Grouped K/V heads: when the dK/dV pass cuts each group of query heads into
+// several ranges, the float32 partial dK and dV of every range follow
+// ([hsplit][B*Hkv][N][d] each, 256-byte aligned).
+size_t partial_bytes(long long bhkv, long long n, int d, int hsplit) {
+  if (hsplit <= 1) return 0;
+  const size_t b = (size_t)hsplit * (size_t)bhkv * (size_t)n * (size_t)d * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+size_t gqa_workspace_bytes(long long bh, long long bhkv, long long n, int d, int grp) {
+  if (bh <= 0 || n <= 0) return 0;
+  return workspace_bytes(bh, n) + 2 * partial_bytes(bhkv, n, d, fa::dkdv_head_splits(bhkv, n, grp));
+}
 
 fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
                   const void* k, const void* v, float scale, int causal, const uint8_t* mask,
@@ -155,7 +167,10 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace"};
   if ((s = check_ptrs(fn, ptrs, names, 10)) != FA_OK) return s;
-  const size_t need = workspace_bytes(p.bh, N);
+  const int grp = H / Hkv;
+  const long long bhkv = (long long)B * Hkv;
+  const int hsplit = fa::dkdv_head_splits(bhkv, N, grp);
+  const size_t need = gqa_workspace_bytes(p.bh, bhkv, N, d, grp);
   if (ws_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
 
@@ -177,7 +192,14 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
   a.hq = H;
-  a.grp = H / Hkv;
+  a.grp = grp;
+  a.hsplit = hsplit;
+  a.nbhkv = (int)bhkv;
+  if (hsplit > 1) {
+    char* part = static_cast<char*>(ws) + workspace_bytes(p.bh, N);
+    a.pdk = reinterpret_cast<float*>(part);
+    a.pdv = reinterpret_cast<float*>(part + partial_bytes(bhkv, N, d, hsplit));
+  }
   hipError_t e = fa::launch_bwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, sparse,
                                 p.bh, a, stream);
   return hip_status(fn, e);
@@ -257,8 +279,8 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* kKernelNames[fa::kNumKernels] = {"fwd", "fwd_f32", "bwd_pre", "bwd_dkdv", "bwd_dq",
-                                            "fwd_split", "fwd_merge"};
+const char* kKernelNames[fa::kNumKernels] = {"fwd",       "fwd_f32",   "bwd_pre",        "bwd_dkdv",
+                                            "bwd_dq",    "fwd_split", "fwd_merge",      "bwd_dkdv_reduce"};
 
 }  // namespace
 
@@ -384,6 +406,12 @@ FA_EXPORT fa_status flash_attn_fwd_gqa(int B, int H, int Hkv, int N, int d, fa_d
                                        float* lse, hipStream_t stream) {
   return run_fwd("flash_attn_fwd_gqa", B, H, Hkv, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o,
                  lse, stream);
+}
+
+FA_EXPORT size_t flash_attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype dtype) {
+  (void)dtype;
+  if (B <= 0 || H <= 0 || N <= 0 || Hkv <= 0 || H % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  return gqa_workspace_bytes((long long)B * H, (long long)B * Hkv, N, d, H / Hkv);
 }
 
 FA_EXPORT fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,

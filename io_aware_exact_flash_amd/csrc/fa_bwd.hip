@@ -106,16 +106,24 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // tiles (low key blocks see the most queries).
   const int per = CAUSAL ? (a.nkb + 1) / 2 : a.nkb;
   const int lb = xcd_remap(blockIdx.x, a.nblk_kv);
-  const int bh = lb / per;  // K/V head, an index over B x Hkv
+  const int unit = lb / per;
   const int pk_ = lb % per;
+  const int bh = unit / a.hsplit;   // K/V head, an index over B x Hkv
+  const int rng = unit % a.hsplit;  // range of the group's query heads
   const size_t hoff = (size_t)bh * n * D;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
   const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
   // Grouped heads: the grp consecutive query heads that read this K/V head
-  // each contribute to dK and dV; the workgroup sweeps them one after the
-  // other into the same accumulators.
+  // each contribute to dK and dV; the workgroup sweeps those of its range
+  // one after the other into the same accumulators.  With several ranges
+  // (a.hsplit > 1) it writes float32 partial sums that a reduction pass
+  // adds up.
   const int hkv = a.hq / a.grp;
   const int qbh0 = a.grp == 1 ? bh : (bh / hkv) * a.hq + (bh % hkv) * a.grp;
+  const int h_lo = rng * a.grp / a.hsplit;
+  const int h_hi = (rng + 1) * a.grp / a.hsplit;
+  const bool partial = a.hsplit > 1;
+  const size_t poff = (size_t)rng * a.nbhkv * n * D + hoff;  // this range's partial dK, dV
   const uint16_t* Qg = nullptr;
   const uint16_t* dOg = nullptr;
   const float* Ltg = nullptr;
@@ -158,7 +166,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     int i_first = CAUSAL ? k0 / BQ : 0;
     if (!tile_live(i_first)) i_first = next_tile(i_first);
     if (i_first >= n_tiles) {  // no query sees these keys: dK = dV = 0
-      if (my_k < n) {
+      if (my_k < n && partial) {
+        float* dkp = a.pdk + poff + (size_t)my_k * D;
+        float* dvp = a.pdv + poff + (size_t)my_k * D;
+        for (int c = 4 * g; c < D; c += 8) {
+          *reinterpret_cast<f32x4*>(dkp + c) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          *reinterpret_cast<f32x4*>(dvp + c) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      } else if (my_k < n) {
         uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
         uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
         for (int c = 8 * g; c < D; c += 16) {
@@ -376,8 +391,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       n_plain = max(n / BQ - (i_first + n_pre), 0) & ~1;
     }
 #pragma clang loop unroll(disable)
-    for (int hg = 0; hg < a.grp; ++hg) {
-      if (hg) {
+    for (int hg = h_lo; hg < h_hi; ++hg) {
+      if (hg != h_lo) {
         vm_wait<0>();     // the previous head's DMA has landed ...
         __syncthreads();  // ... and every wave is out of its LDS tiles
       }
@@ -414,7 +429,24 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
     agpr_drain(dkacc);
     agpr_drain(dvacc);
-    if (my_k < n) {
+    if (my_k < n && partial) {
+      float* dkp = a.pdk + poff + (size_t)my_k * D;
+      float* dvp = a.pdv + poff + (size_t)my_k * D;
+      const float sc = a.scale;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f32x4 pk, pv;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            pk[t] = dkacc[nb][4 * r + t] * sc;
+            pv[t] = dvacc[nb][4 * r + t];
+          }
+          *reinterpret_cast<f32x4*>(dkp + 32 * nb + 8 * r + 4 * g) = pk;
+          *reinterpret_cast<f32x4*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
+        }
+    } else if (my_k < n) {
       uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
       uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
       const float sc = a.scale;
@@ -442,6 +474,30 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     run(r ? kb2 : pk_);
   }
+}
+
+// ------------------------------------------------------------ dK/dV range sum
+// dK = sum over ranges of the float32 partials (already scaled), rounded to
+// the input type once; dV likewise.  Thread i handles four consecutive
+// elements of dK (i < n4) or dV.  Memory bound: reads hsplit partials,
+// writes one 16-bit result.
+template <typename Tag>
+__global__ __launch_bounds__(kNT) void bwd_dkdv_reduce_kernel(const float* __restrict__ pdk,
+                                                              const float* __restrict__ pdv,
+                                                              uint16_t* __restrict__ dk,
+                                                              uint16_t* __restrict__ dv, long n4,
+                                                              int hsplit) {
+  const long i = (long)blockIdx.x * kNT + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const bool is_v = i >= n4;
+  const long j = is_v ? i - n4 : i;
+  const float* p = (is_v ? pdv : pdk) + 4 * j;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(p);
+  for (int s = 1; s < hsplit; ++s) acc += *reinterpret_cast<const f32x4*>(p + (size_t)s * 4 * n4);
+  u32x2 out;
+  out[0] = pack2<Tag>(acc[0], acc[1]);
+  out[1] = pack2<Tag>(acc[2], acc[3]);
+  *reinterpret_cast<u32x2*>((is_v ? dv : dk) + 4 * j) = out;
 }
 
 // ------------------------------------------------------------ dQ pass
@@ -906,6 +962,16 @@ hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
   e = hipGetLastError();
   timing_end(kBwdDkDv, st);
   if (e != hipSuccess) return e;
+  if (a.hsplit > 1) {
+    const long n4 = (long)a.nbhkv * a.n * (D / 4);
+    timing_begin(kBwdDkDvReduce, st);
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<Tag>), dim3((2 * n4 + kNT - 1) / kNT), dim3(kNT), 0, st,
+                       a.pdk, a.pdv, reinterpret_cast<uint16_t*>(a.dk), reinterpret_cast<uint16_t*>(a.dv), n4,
+                       a.hsplit);
+    e = hipGetLastError();
+    timing_end(kBwdDkDvReduce, st);
+    if (e != hipSuccess) return e;
+  }
   timing_begin(kBwdDq, st);
   hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3(a.nblk_q), dim3(kNT), 0, st, a);
   e = hipGetLastError();
@@ -927,7 +993,7 @@ hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a,
   a.nqb = (a.n + kDqRows - 1) / kDqRows;
   a.nblk_q = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   a.nkb = (a.n + 127) / 128;
-  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.grp);  // per K/V head
+  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.grp) * a.hsplit;  // per K/V head and range
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)

@@ -58,11 +58,36 @@ struct BwdArgs {
   // sums over the grp query heads that share it
   int hq;
   int grp;
+  // hsplit > 1: the group's query heads are cut into hsplit ranges swept by
+  // separate workgroups, each writing scaled float32 partial dK, dV; a
+  // reduction pass sums them into dk, dv
+  int hsplit;
+  int nbhkv;             // B*Hkv
+  float* pdk;            // [hsplit][B*Hkv][N][d]
+  float* pdv;            // [hsplit][B*Hkv][N][d]
 };
+
+// (K/V head, key block) units the dK/dV pass aims for before it cuts groups
+// of query heads into ranges: four per compute unit of a 256-CU MI355X (a
+// causal launch pairs two units per workgroup, so two workgroups per unit).
+constexpr int kDkDvTargetUnits = 1024;
+constexpr int kDkDvKeys = 128;  // keys per dK/dV unit
+
+// Ranges the group of grp query heads is cut into (1 = no partials): enough
+// units to fill the GPU, never more ranges than heads.  Depends on the shape
+// only, so the workspace size can be computed before the call.
+inline int dkdv_head_splits(long long bhkv, long long n, int grp) {
+  if (grp <= 1 || bhkv <= 0 || n <= 0) return 1;
+  const long long units = (n + kDkDvKeys - 1) / kDkDvKeys * bhkv;
+  long long s = (kDkDvTargetUnits + units - 1) / units;
+  if (s > grp) s = grp;
+  return s < 1 ? 1 : (int)s;
+}
 
 // Kernel classes for the optional per-kernel timing hooks.
 enum KernelId : int {
-  kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kFwdSplit = 5, kFwdMerge = 6, kNumKernels = 7
+  kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kFwdSplit = 5, kFwdMerge = 6,
+  kBwdDkDvReduce = 7, kNumKernels = 8
 };
 
 // Bracket one launch with events on its stream when timing is enabled

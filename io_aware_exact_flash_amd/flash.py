@@ -37,6 +37,7 @@ SIGNATURES = {
     "flash_attn_fwd_splitkv_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "flash_attn_fwd_splitkv": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _I, _P, _P, _P, _Z, _P]),
     "flash_attn_fwd_gqa": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _P, _P, _P]),
+    "flash_attn_bwd_gqa_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "flash_attn_bwd_gqa": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _P, _Z,
                                 _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
@@ -45,7 +46,7 @@ SIGNATURES = {
     "flash_attn_timing_collect": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), _I]),
     "flash_attn_kernel_name": (ctypes.c_char_p, [_I]),
 }
-KERNELS = 7  # timing classes: fwd, fwd_f32, bwd_pre, bwd_dkdv, bwd_dq, fwd_split, fwd_merge
+KERNELS = 8  # timing classes: fwd, fwd_f32, bwd_pre, bwd_dkdv, bwd_dq, fwd_split, fwd_merge, bwd_dkdv_reduce
 
 _lib = None
 _lock = threading.Lock()
@@ -231,12 +232,20 @@ def fwd_gqa(q, k, v, scale=None, causal=False):
     return o, lse
 
 
+def bwd_gqa_workspace_size(B, H, Hkv, N, d, dtype=torch.bfloat16) -> int:
+    return int(lib().flash_attn_bwd_gqa_workspace_size(B, H, Hkv, N, d, _DT[dtype]))
+
+
 def bwd_gqa(q, k, v, o, dout, lse, scale=None, causal=False, workspace=None):
     """(dQ, dK, dV) = flash_attn_bwd_gqa(...); dK, dV have the shape of k, v."""
     B, H, Hkv, N, d, dt = _shape_gqa(q, k, v, o, dout)
     _lse_ok(lse, q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws, nbytes = _workspace(q) if workspace is None else (workspace, workspace.numel())
+    if workspace is None:
+        nbytes = bwd_gqa_workspace_size(B, H, Hkv, N, d, q.dtype)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        ws, nbytes = workspace, workspace.numel()
     _check(lib().flash_attn_bwd_gqa(B, H, Hkv, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                     o.data_ptr(), dout.data_ptr(), lse.data_ptr(), _scale(scale, d),
                                     int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),

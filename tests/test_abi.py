@@ -182,7 +182,7 @@ def _gqa_fwd(H, Hkv, **kw):
 def _gqa_bwd(H, Hkv, **kw):
     a = dict(B=1, N=256, d=128, dt=flash.FA_BF16)
     a.update(kw)
-    need = flash.lib().flash_attn_bwd_workspace_size(a["B"], H, a["N"], a["d"], a["dt"])
+    need = flash.lib().flash_attn_bwd_gqa_workspace_size(a["B"], H, max(Hkv, 1), a["N"], a["d"], a["dt"])
     p = [FAKE] * 9
     if kw.get("null_dk"):
         p[7] = None
@@ -199,10 +199,32 @@ def test_gqa_head_validation(H, Hkv):
     assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_bwd_gqa:")
 
 
+def test_gqa_workspace_size():
+    lib = flash.lib()
+    base = lambda B, H, N: lib.flash_attn_bwd_workspace_size(B, H, N, 128, flash.FA_BF16)
+    r256 = lambda b: (b + 255) // 256 * 256
+    # one K/V head per query head, or enough (K/V head, 128-key block) units: no partials
+    assert lib.flash_attn_bwd_gqa_workspace_size(2, 8, 8, 1000, 128, flash.FA_BF16) == base(2, 8, 1000)
+    assert lib.flash_attn_bwd_gqa_workspace_size(8, 128, 64, 200, 128, flash.FA_BF16) == base(8, 128, 200)
+    # 2 units, group of 4 heads: 4 ranges, float32 partial dK and dV [4][B*Hkv][N][d] each
+    assert lib.flash_attn_bwd_gqa_workspace_size(1, 4, 1, 200, 128, flash.FA_BF16) == \
+        base(1, 4, 200) + 2 * r256(4 * 1 * 200 * 128 * 4)
+    # 256 units, group of 8: ceil(1024 / 256) = 4 ranges of two heads
+    assert lib.flash_attn_bwd_gqa_workspace_size(8, 256, 32, 128, 64, flash.FA_BF16) == \
+        lib.flash_attn_bwd_workspace_size(8, 256, 128, 64, flash.FA_BF16) + 2 * r256(4 * 256 * 128 * 64 * 4)
+    for args in ((1, 4, 3, 200, 128), (1, 4, 0, 200, 128), (0, 4, 2, 200, 128), (1, 4, 2, 0, 128),
+                 (1, 4, 2, 200, 96)):
+        assert lib.flash_attn_bwd_gqa_workspace_size(*args, flash.FA_BF16) == 0
+
+
 def test_gqa_other_checks_and_empty_problems():
     assert _gqa_fwd(4, 2, d=96) == flash.FA_ERR_UNSUPPORTED
     assert _gqa_bwd(4, 2, dt=flash.FA_F32) == flash.FA_ERR_UNSUPPORTED
     assert _gqa_bwd(4, 1, null_dk=True) == flash.FA_ERR_INVALID_ARGUMENT
+    # the plain backward workspace is too small once partial sums are needed
+    small = flash.lib().flash_attn_bwd_workspace_size(1, 4, 256, 128, flash.FA_BF16)
+    assert flash.lib().flash_attn_bwd_gqa(1, 4, 1, 256, 128, flash.FA_BF16, *[FAKE] * 6, 0.125, 0,
+                                          *[FAKE] * 4, small, None) == flash.FA_ERR_WORKSPACE_TOO_SMALL
     assert _gqa_fwd(4, 2, v=FAKE_MISALIGNED) == flash.FA_ERR_INVALID_ARGUMENT
     assert _gqa_fwd(0, 0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
     assert _gqa_fwd(4, 2, N=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK

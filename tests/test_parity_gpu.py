@@ -265,8 +265,13 @@ def _oracle_gqa(f64, s, causal):
     return O, L, gQ, gK, gV
 
 
+# The dK/dV pass cuts a group of G = H/Hkv query heads into s = min(G,
+# ceil(1024 / units)) ranges, units = B*Hkv*ceil(N/128): the small shapes run
+# one head per range (float32 partials + range sum); (8, 256, 32, 128) runs
+# ranges of two heads; (8, 128, 64, 200) one range per group (no partials).
 GQA_SHAPES = [(1, 4, 1, 200), (2, 6, 2, 333), (1, 4, 4, 130), (1, 3, 1, 1), (2, 4, 2, 519),
               (1, 16, 1, 300)]
+GQA_SHAPES_MANY_HEADS = [(8, 256, 32, 128), (8, 128, 64, 200)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -274,6 +279,17 @@ GQA_SHAPES = [(1, 4, 1, 200), (2, 6, 2, 333), (1, 4, 4, 130), (1, 3, 1, 1), (2, 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", GQA_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_gqa_forward_backward(dtype, d, causal, shape):
+    _check_gqa(dtype, d, causal, shape)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", GQA_SHAPES_MANY_HEADS, ids=lambda s: "x".join(map(str, s)))
+def test_gqa_forward_backward_many_heads(d, causal, shape):
+    _check_gqa("bf16", d, causal, shape)
+
+
+def _check_gqa(dtype, d, causal, shape):
     """Grouped K/V heads: each query head reads its group's K/V head in place;
     dK and dV of a K/V head sum over the group.  A sum of G per-head
     gradients with independent roundings has ~sqrt(G) times the error of one,
