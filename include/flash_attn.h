@@ -205,6 +205,48 @@ fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Variable-length batches: B sequences of different lengths packed along
+ * one token axis, each attended on its own (the per-head problem of
+ * [FA2 Algorithm 1, Algorithm 2] for every sequence; grouped K/V heads as
+ * in flash_attn_fwd_gqa).  Sequence b holds rows cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1; no attention crosses sequences, and the causal rule
+ * (key j visible to query i iff j <= i) counts positions from the start
+ * of each sequence.
+ *   cu_seqlens      in  device int32 [B+1], 4-byte aligned: 0 = cu[0] <=
+ *                       cu[1] <= ... <= cu[B] = total, every length <=
+ *                       max_seqlen.  Not read on the host; the kernels
+ *                       clamp each sequence into [0, total] and to
+ *                       max_seqlen rows, so inconsistent offsets give
+ *                       unspecified results but no access outside the
+ *                       tensors.
+ *   q, o, dout, dq  [total][H][d]   dtype (token-major: row stride H*d)
+ *   k, v, dk, dv    [total][Hkv][d] dtype
+ *   lse             [H][total]      float32
+ * A batch of B sequences of equal length N in the [B][N][H][d] layout is
+ * the packed batch with cu_seqlens = 0, N, 2N, ..., BN.  Domain as the
+ * dense calls with N = max_seqlen, plus H*d < 2^23 (FA_ERR_UNSUPPORTED
+ * otherwise); FA_F32 in the forward only.  Work is launched for
+ * max_seqlen rows per sequence; shorter sequences leave workgroups idle.
+ * The backward workspace is flash_attn_varlen_bwd_workspace_size() bytes
+ * (the per-row arrays of H*total rows, then the grouped-head partial sums
+ * when used); it returns 0 for empty or invalid shapes.
+ */
+fa_status flash_attn_varlen_fwd(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                fa_dtype dtype, const int* cu_seqlens,
+                                const void* q, const void* k, const void* v,
+                                float scale, int causal,
+                                void* o, float* lse, hipStream_t stream);
+size_t flash_attn_varlen_bwd_workspace_size(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                            fa_dtype dtype);
+fa_status flash_attn_varlen_bwd(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                fa_dtype dtype, const int* cu_seqlens,
+                                const void* q, const void* k, const void* v,
+                                const void* o, const void* dout, const float* lse,
+                                float scale, int causal,
+                                void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-kernel timing (diagnostics; not part of the method).  While enabled,
  * every kernel the library launches is bracketed by two HIP events recorded
  * on its launch stream.  flash_attn_timing_collect waits for the recorded

@@ -98,16 +98,17 @@ fa_status hip_status(const char* fn, hipError_t e) {
   return fail(FA_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
 }
 
-// Two float32 arrays of B*H*N (D and the base-2 LSE), each followed by
-// 256 spare bytes (16-byte loads of a ragged last tile may reach past the
-// end) and 256-byte aligned.
-size_t ws_array_bytes(long long bh, long long n) {
-  size_t b = (size_t)bh * (size_t)n * sizeof(float);
+// Two float32 arrays with one entry per query row (D and the base-2 LSE;
+// rows = B*H*N, or H*total for a packed batch), each followed by 256 spare
+// bytes (16-byte loads of a ragged last tile may reach past the end) and
+// 256-byte aligned.
+size_t ws_array_bytes(long long rows) {
+  size_t b = (size_t)rows * sizeof(float);
   return ((b + 255) & ~(size_t)255) + 256;
 }
-size_t workspace_bytes(long long bh, long long n) {
-  if (bh <= 0 || n <= 0) return 0;
-  return 2 * ws_array_bytes(bh, n);
+size_t workspace_bytes(long long rows) {
+  if (rows <= 0) return 0;
+  return 2 * ws_array_bytes(rows);
 }
 // Grouped K/V heads: when the dK/dV pass cuts each group of query heads into
 // several ranges, the float32 partial dK and dV of every range follow
@@ -117,20 +118,24 @@ size_t partial_bytes(long long bhkv, long long n, int d, int hsplit) {
   const size_t b = (size_t)hsplit * (size_t)bhkv * (size_t)n * (size_t)d * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
-size_t gqa_workspace_bytes(long long bh, long long bhkv, long long n, int d, int grp) {
-  if (bh <= 0 || n <= 0) return 0;
-  return workspace_bytes(bh, n) + 2 * partial_bytes(bhkv, n, d, fa::dkdv_head_splits(bhkv, n, grp));
+// rows: per-row entries; n: the longest sequence (sizes the partials)
+size_t gqa_workspace_bytes(long long rows, long long bhkv, long long n, int d, int grp) {
+  if (rows <= 0 || n <= 0) return 0;
+  return workspace_bytes(rows) + 2 * partial_bytes(bhkv, n, d, fa::dkdv_head_splits(bhkv, n, grp));
 }
 
+// `seqs` null: dense [B][H][N][d] tensors with Hkv K/V heads; otherwise the
+// (already validated) layout of a packed batch whose longest sequence is N.
 fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
                   const void* k, const void* v, float scale, int causal, const uint8_t* mask,
-                  int mask_block, bool sparse, void* o, float* lse, hipStream_t stream) {
+                  int mask_block, bool sparse, void* o, float* lse, hipStream_t stream,
+                  const fa::Seqs* seqs = nullptr) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, false, &p);
   if (s != FA_OK) return s;
   if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
   if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
-  if (p.empty) return FA_OK;
+  if (p.empty || (seqs && seqs->total == 0)) return FA_OK;
   const void* ptrs[] = {q, k, v, o, lse};
   const char* names[] = {"q", "k", "v", "o", "lse"};
   if ((s = check_ptrs(fn, ptrs, names, 5)) != FA_OK) return s;
@@ -145,8 +150,7 @@ fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   a.mask_t = (N + fa::kMaskBlockTokens - 1) / fa::kMaskBlockTokens;
   a.n = N;
   a.c = scale * 1.4426950408889634f;
-  a.hq = H;
-  a.grp = H / Hkv;
+  a.sq = seqs ? *seqs : fa::dense_seqs(H, Hkv, N, d);
   hipError_t e = (dtype == FA_F32)
                      ? fa::launch_fwd_f32(d, causal != 0, sparse, p.bh, a, stream)
                      : fa::launch_fwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0,
@@ -157,20 +161,23 @@ fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
 fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
                   const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   float scale, int causal, const uint8_t* mask, int mask_block, bool sparse,
-                  void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream,
+                  const fa::Seqs* seqs = nullptr) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, true, &p);
   if (s != FA_OK) return s;
   if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
   if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
-  if (p.empty) return FA_OK;
+  if (p.empty || (seqs && seqs->total == 0)) return FA_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace"};
   if ((s = check_ptrs(fn, ptrs, names, 10)) != FA_OK) return s;
   const int grp = H / Hkv;
   const long long bhkv = (long long)B * Hkv;
   const int hsplit = fa::dkdv_head_splits(bhkv, N, grp);
-  const size_t need = gqa_workspace_bytes(p.bh, bhkv, N, d, grp);
+  // per-row arrays: one per query row of every head (dense B*H*N, packed H*total)
+  const long long lrows = seqs ? (long long)H * seqs->total : p.bh * (long long)N;
+  const size_t need = gqa_workspace_bytes(lrows, bhkv, N, d, grp);
   if (ws_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
 
@@ -182,7 +189,7 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   a.dout = dout;
   a.lse = lse;
   a.dvec = static_cast<float*>(ws);
-  a.lt = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_array_bytes(p.bh, N));
+  a.lt = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_array_bytes(lrows));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -191,18 +198,47 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   a.n = N;
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
-  a.hq = H;
-  a.grp = grp;
+  a.sq = seqs ? *seqs : fa::dense_seqs(H, Hkv, N, d);
   a.hsplit = hsplit;
   a.nbhkv = (int)bhkv;
+  a.hkv = Hkv;
   if (hsplit > 1) {
-    char* part = static_cast<char*>(ws) + workspace_bytes(p.bh, N);
+    char* part = static_cast<char*>(ws) + workspace_bytes(lrows);
     a.pdk = reinterpret_cast<float*>(part);
     a.pdv = reinterpret_cast<float*>(part + partial_bytes(bhkv, N, d, hsplit));
   }
   hipError_t e = fa::launch_bwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, sparse,
                                 p.bh, a, stream);
   return hip_status(fn, e);
+}
+
+// Packed variable-length batches: q, o, dout, dq [total][H][d]; k, v, dk, dv
+// [total][Hkv][d]; lse and the per-row workspace arrays [H][total].
+fa_status check_varlen(const char* fn, int B, int H, int Hkv, int total, int max_seqlen, int d,
+                       const int* cu, fa::Seqs* out) {
+  if (total < 0 || max_seqlen < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: negative size (total=%d max_seqlen=%d)", fn, total, max_seqlen);
+  fa_status s = check_heads(fn, H, Hkv);
+  if (s != FA_OK) return s;
+  if (B > 0 && !cu) return fail(FA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is null", fn);
+  if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is not 4-byte aligned", fn);
+  // the kernels form row offsets in bytes with 24-bit multiplies
+  if ((long long)H * d * 2 >= (1LL << 24))
+    return fail(FA_ERR_UNSUPPORTED, "%s: row stride H*d = %lld elements too large", fn, (long long)H * d);
+  fa::Seqs q{};
+  q.cu = cu;
+  q.qsh = d;
+  q.qsr = H * d;
+  q.ksh = d;
+  q.ksr = Hkv * d;
+  q.lb = 0;
+  q.lh = total;
+  q.hq = H;
+  q.grp = Hkv > 0 ? H / Hkv : 1;
+  q.total = total;
+  *out = q;
+  return FA_OK;
 }
 
 // Split-KV workspace: num_splits float32 [B*H][N][d] partial outputs, then
@@ -246,8 +282,7 @@ fa_status run_fwd_split(const char* fn, int B, int H, int N, int d, fa_dtype dty
   a.mask_t = 0;
   a.n = N;
   a.c = scale * 1.4426950408889634f;
-  a.hq = H;
-  a.grp = 1;
+  a.sq = fa::dense_seqs(H, H, N, d);
   a.nsplit = splits;
   a.po = static_cast<float*>(ws);
   a.plse = reinterpret_cast<float*>(static_cast<char*>(ws) + splitkv_po_bytes(p.bh, N, d, splits));
@@ -368,7 +403,7 @@ FA_EXPORT size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, fa_dt
   (void)d;
   (void)dtype;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return workspace_bytes((long long)B * H, N);
+  return workspace_bytes((long long)B * H * N);
 }
 
 FA_EXPORT fa_status flash_attn_bwd(int B, int H, int N, int d, fa_dtype dtype, const void* q,
@@ -411,7 +446,7 @@ FA_EXPORT fa_status flash_attn_fwd_gqa(int B, int H, int Hkv, int N, int d, fa_d
 FA_EXPORT size_t flash_attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype dtype) {
   (void)dtype;
   if (B <= 0 || H <= 0 || N <= 0 || Hkv <= 0 || H % Hkv != 0 || (d != 64 && d != 128)) return 0;
-  return gqa_workspace_bytes((long long)B * H, (long long)B * Hkv, N, d, H / Hkv);
+  return gqa_workspace_bytes((long long)B * H * N, (long long)B * Hkv, N, d, H / Hkv);
 }
 
 FA_EXPORT fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
@@ -420,6 +455,39 @@ FA_EXPORT fa_status flash_attn_bwd_gqa(int B, int H, int Hkv, int N, int d, fa_d
                                        void* workspace, size_t workspace_bytes_, hipStream_t stream) {
   return run_bwd("flash_attn_bwd_gqa", B, H, Hkv, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0,
                  false, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+FA_EXPORT fa_status flash_attn_varlen_fwd(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                          fa_dtype dtype, const int* cu_seqlens, const void* q, const void* k,
+                                          const void* v, float scale, int causal, void* o, float* lse,
+                                          hipStream_t stream) {
+  const char* fn = "flash_attn_varlen_fwd";
+  fa::Seqs sq;
+  fa_status s = check_varlen(fn, B, H, Hkv, total, max_seqlen, d, cu_seqlens, &sq);
+  if (s != FA_OK) return s;
+  return run_fwd(fn, B, H, Hkv, max_seqlen, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o, lse, stream,
+                 &sq);
+}
+
+FA_EXPORT size_t flash_attn_varlen_bwd_workspace_size(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                                      fa_dtype dtype) {
+  (void)dtype;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || total <= 0 || max_seqlen <= 0 || (d != 64 && d != 128))
+    return 0;
+  return gqa_workspace_bytes((long long)H * total, (long long)B * Hkv, max_seqlen, d, H / Hkv);
+}
+
+FA_EXPORT fa_status flash_attn_varlen_bwd(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                          fa_dtype dtype, const int* cu_seqlens, const void* q, const void* k,
+                                          const void* v, const void* o, const void* dout, const float* lse,
+                                          float scale, int causal, void* dq, void* dk, void* dv, void* workspace,
+                                          size_t workspace_bytes_, hipStream_t stream) {
+  const char* fn = "flash_attn_varlen_bwd";
+  fa::Seqs sq;
+  fa_status s = check_varlen(fn, B, H, Hkv, total, max_seqlen, d, cu_seqlens, &sq);
+  if (s != FA_OK) return s;
+  return run_bwd(fn, B, H, Hkv, max_seqlen, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0, false, dq,
+                 dk, dv, workspace, workspace_bytes_, stream, &sq);
 }
 
 FA_EXPORT const char* flash_attn_status_string(fa_status status) {

@@ -36,19 +36,22 @@ constexpr int kDqRows = 256;  // queries per dQ workgroup
 // ------------------------------------------------------------ D pre-pass
 // Also writes the base-2 log-sum-exp L log2(e) the dK/dV pass subtracts,
 // +inf for rows without any allowed key (so that P = exp2(S c - Lt) = 0).
+// Workgroup x covers rows of query head x / blocks_per_head.
 template <typename Tag, int D>
-__global__ __launch_bounds__(kNT) void bwd_pre_kernel(const uint16_t* __restrict__ o,
-                                                      const uint16_t* __restrict__ dout,
-                                                      const float* __restrict__ lse,
-                                                      float* __restrict__ dvec,
-                                                      float* __restrict__ lt, long rows) {
+__global__ __launch_bounds__(kNT) void bwd_pre_kernel(BwdArgs args, int blocks_per_head) {
   constexpr int TPR = D / 8;  // threads per row, 16 bytes each
-  const long row = (long)blockIdx.x * (kNT / TPR) + threadIdx.x / TPR;
+  constexpr int RPB = kNT / TPR;
+  const int bh = blockIdx.x / blocks_per_head;
+  const int row = (blockIdx.x % blocks_per_head) * RPB + threadIdx.x / TPR;
+  const HeadAt at = head_at(args.sq, bh / args.sq.hq, bh % args.sq.hq, args.n);
   const int c = threadIdx.x % TPR;
+  const uint16_t* __restrict__ o = reinterpret_cast<const uint16_t*>(args.o) + at.q;
+  const uint16_t* __restrict__ dout = reinterpret_cast<const uint16_t*>(args.dout) + at.q;
+  const size_t ro = (size_t)min(row, max(at.n - 1, 0)) * args.sq.qsr + 8 * c;
   float acc = 0.0f;
-  if (row < rows) {
-    u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
-    u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+  if (row < at.n) {
+    u32x4 a = *reinterpret_cast<const u32x4*>(o + ro);
+    u32x4 b = *reinterpret_cast<const u32x4*>(dout + ro);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       acc = fmaf(to_f32<Tag>(a[t] & 0xffff), to_f32<Tag>(b[t] & 0xffff), acc);
@@ -57,10 +60,10 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) {
-    dvec[row] = acc;
-    const float l = lse[row];
-    lt[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  if (row < at.n && c == 0) {
+    args.dvec[at.l + row] = acc;
+    const float l = args.lse[at.l + row];
+    args.lt[at.l + row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
 }
 
@@ -100,40 +103,43 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
-  const int n = a.n;
   // Causal: workgroup p of a head runs the key blocks p and nkb-1-p one
   // after the other, so every workgroup sees the same number of query
-  // tiles (low key blocks see the most queries).
+  // tiles (low key blocks see the most queries).  The grid covers the
+  // longest sequence; a shorter one leaves workgroups idle.
   const int per = CAUSAL ? (a.nkb + 1) / 2 : a.nkb;
   const int lb = xcd_remap(blockIdx.x, a.nblk_kv);
   const int unit = lb / per;
   const int pk_ = lb % per;
   const int bh = unit / a.hsplit;   // K/V head, an index over B x Hkv
   const int rng = unit % a.hsplit;  // range of the group's query heads
-  const size_t hoff = (size_t)bh * n * D;
-  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + hoff;
-  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + hoff;
+  // the group's first query head locates the K/V head and the sequence
+  const HeadAt at = head_at(a.sq, bh / a.hkv, (bh % a.hkv) * a.sq.grp, a.n);
+  const int n = at.n;  // this sequence's length
+  const int qsr = a.sq.qsr, ksr = a.sq.ksr;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + at.kv;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + at.kv;
   // Grouped heads: the grp consecutive query heads that read this K/V head
   // each contribute to dK and dV; the workgroup sweeps those of its range
   // one after the other into the same accumulators.  With several ranges
   // (a.hsplit > 1) it writes float32 partial sums that a reduction pass
   // adds up.
-  const int hkv = a.hq / a.grp;
-  const int qbh0 = a.grp == 1 ? bh : (bh / hkv) * a.hq + (bh % hkv) * a.grp;
-  const int h_lo = rng * a.grp / a.hsplit;
-  const int h_hi = (rng + 1) * a.grp / a.hsplit;
+  const int grp = a.sq.grp;
+  const int h_lo = rng * grp / a.hsplit;
+  const int h_hi = (rng + 1) * grp / a.hsplit;
   const bool partial = a.hsplit > 1;
-  const size_t poff = (size_t)rng * a.nbhkv * n * D + hoff;  // this range's partial dK, dV
+  const size_t poff = ((size_t)rng * a.nbhkv + bh) * a.n * D;  // this range's partial dK, dV
   const uint16_t* Qg = nullptr;
   const uint16_t* dOg = nullptr;
   const float* Ltg = nullptr;
   const float* Dg = nullptr;
-  auto set_head = [&](int hg) {
-    const size_t qh = (size_t)(qbh0 + hg);
-    Qg = reinterpret_cast<const uint16_t*>(a.q) + qh * n * D;
-    dOg = reinterpret_cast<const uint16_t*>(a.dout) + qh * n * D;
-    Ltg = a.lt + qh * n;
-    Dg = a.dvec + qh * n;
+  auto set_head = [&](int hg) {  // query head hg of the group
+    const long long qo = at.q + hg * a.sq.qsh;
+    const long long lo = at.l + hg * a.sq.lh;
+    Qg = reinterpret_cast<const uint16_t*>(a.q) + qo;
+    dOg = reinterpret_cast<const uint16_t*>(a.dout) + qo;
+    Ltg = a.lt + lo;
+    Dg = a.dvec + lo;
   };
 
   auto run = [&](const int kb) {
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
     u32x4 kreg[KS], vreg[KS];  // K^T, V^T fragments (B operands), in AGPRs
     {
-      const size_t r = (size_t)min(my_k, n - 1) * D + 8 * g;
+      const size_t r = (size_t)min(my_k, n - 1) * ksr + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         gload_agpr(kreg[ks], Kg + r + 16 * ks);
@@ -174,8 +180,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
           *reinterpret_cast<f32x4*>(dvp + c) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
       } else if (my_k < n) {
-        uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
-        uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
+        uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + at.kv + (size_t)my_k * ksr;
+        uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + at.kv + (size_t)my_k * ksr;
         for (int c = 8 * g; c < D; c += 16) {
           *reinterpret_cast<u32x4*>(dkp + c) = u32x4{0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(dvp + c) = u32x4{0u, 0u, 0u, 0u};
@@ -211,16 +217,16 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     int sq = 0;        // its slot
     auto dma_set = [&]() {
       const int it = iq < n_tiles ? iq : i_first;
-      d_q = Qg + (size_t)it * BQ * D;
-      d_o = dOg + (size_t)it * BQ * D;
+      d_q = Qg + (size_t)it * BQ * qsr;
+      d_o = dOg + (size_t)it * BQ * qsr;
       d_last = n - 1 - it * BQ;
       d_slot = lds_base + sq;
       d_lds = d_slot + 1024 * w;
       d_ld = (lane < 8 ? Ltg : Dg) + min(it * BQ + 4 * (lane & 7), n - 1);
     };
     auto dma_tile = [&](int t) {
-      if (t < QD::kPer) qd.issue_at(t, d_q, d_last, d_lds);
-      else if (t < 2 * QD::kPer) qd.issue_at(t - QD::kPer, d_o, d_last, d_lds + LDO);
+      if (t < QD::kPer) qd.issue_at(t, d_q, d_last, 2 * qsr, d_lds);
+      else if (t < 2 * QD::kPer) qd.issue_at(t - QD::kPer, d_o, d_last, 2 * qsr, d_lds + LDO);
       else if (lane < 16) dma16(d_ld, d_slot + LLD);
     };
     auto dma_advance = [&]() {
@@ -447,8 +453,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
           *reinterpret_cast<f32x4*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
         }
     } else if (my_k < n) {
-      uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + hoff + (size_t)my_k * D;
-      uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + hoff + (size_t)my_k * D;
+      uint16_t* dkp = reinterpret_cast<uint16_t*>(a.dk) + at.kv + (size_t)my_k * ksr;
+      uint16_t* dvp = reinterpret_cast<uint16_t*>(a.dv) + at.kv + (size_t)my_k * ksr;
       const float sc = a.scale;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -464,8 +470,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
   };
-  const int kb2 = a.nkb - 1 - pk_;
-  const int nrun = (CAUSAL && pk_ != kb2) ? 2 : 1;
+  const int nkb = (n + BKV - 1) / BKV;  // this sequence's key blocks
+  const int kb2 = nkb - 1 - pk_;
+  // blocks pk_ and kb2 (paired causal), or pk_ alone; none past the end of
+  // a shorter sequence
+  const int nrun = CAUSAL ? (pk_ < kb2 ? 2 : pk_ == kb2 ? 1 : 0) : (pk_ < nkb ? 1 : 0);
 #pragma clang loop unroll(disable)
   for (int r = 0; r < nrun; ++r) {
     if (r) {
@@ -479,25 +488,29 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // ------------------------------------------------------------ dK/dV range sum
 // dK = sum over ranges of the float32 partials (already scaled), rounded to
 // the input type once; dV likewise.  Thread i handles four consecutive
-// elements of dK (i < n4) or dV.  Memory bound: reads hsplit partials,
+// elements of dK (i < n4) or dV; the partials are [range][B*Hkv][N][d]
+// with N the longest sequence.  Memory bound: reads hsplit partials,
 // writes one 16-bit result.
-template <typename Tag>
-__global__ __launch_bounds__(kNT) void bwd_dkdv_reduce_kernel(const float* __restrict__ pdk,
-                                                              const float* __restrict__ pdv,
-                                                              uint16_t* __restrict__ dk,
-                                                              uint16_t* __restrict__ dv, long n4,
-                                                              int hsplit) {
+template <typename Tag, int D>
+__global__ __launch_bounds__(kNT) void bwd_dkdv_reduce_kernel(BwdArgs a, long n4) {
   const long i = (long)blockIdx.x * kNT + threadIdx.x;
   if (i >= 2 * n4) return;
   const bool is_v = i >= n4;
   const long j = is_v ? i - n4 : i;
-  const float* p = (is_v ? pdv : pdk) + 4 * j;
+  const long row = j / (D / 4);
+  const int c = 4 * (int)(j % (D / 4));
+  const int bhkv = (int)(row / a.n);
+  const int t = (int)(row % a.n);
+  const HeadAt at = head_at(a.sq, bhkv / a.hkv, (bhkv % a.hkv) * a.sq.grp, a.n);
+  if (t >= at.n) return;  // past a shorter sequence
+  const float* p = (is_v ? a.pdv : a.pdk) + row * D + c;
   f32x4 acc = *reinterpret_cast<const f32x4*>(p);
-  for (int s = 1; s < hsplit; ++s) acc += *reinterpret_cast<const f32x4*>(p + (size_t)s * 4 * n4);
+  for (int s = 1; s < a.hsplit; ++s) acc += *reinterpret_cast<const f32x4*>(p + (size_t)s * 4 * n4);
   u32x2 out;
   out[0] = pack2<Tag>(acc[0], acc[1]);
   out[1] = pack2<Tag>(acc[2], acc[3]);
-  *reinterpret_cast<u32x2*>((is_v ? dv : dk) + 4 * j) = out;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(is_v ? a.dv : a.dk) + at.kv + (size_t)t * a.sq.ksr + c;
+  *reinterpret_cast<u32x2*>(dst) = out;
 }
 
 // ------------------------------------------------------------ dQ pass
@@ -545,19 +558,19 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
-  const int n = a.n;
   // Causal: workgroup p of a head runs the query blocks nqb-1-p and p one
   // after the other (equal work for every workgroup).
   const int per = CAUSAL ? (a.nqb + 1) / 2 : a.nqb;
   const int lb = xcd_remap(blockIdx.x, a.nblk_q);
   const int bh = lb / per;
   const int pq_ = lb % per;
-  const size_t hoff = (size_t)bh * n * D;
-  const size_t kvoff = (size_t)kv_head(bh, a.hq, a.grp) * n * D;
-  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
-  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
-  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
-  const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + hoff;
+  const HeadAt at = head_at(a.sq, bh / a.sq.hq, bh % a.sq.hq, a.n);
+  const int n = at.n;  // this head's length
+  const int qsr = a.sq.qsr, ksr = a.sq.ksr;
+  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + at.q;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + at.kv;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + at.kv;
+  const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + at.q;
 
   auto run = [&](const int qb) {
     const int q0 = qb * BR;
@@ -569,15 +582,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int h = 0; h < 2; ++h) {
       const int my_q = qw0 + 32 * h + c32;
       const int qr = min(my_q, n - 1);
-      const size_t r = (size_t)qr * D + 8 * g;
+      const size_t r = (size_t)qr * qsr + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
         gload_agpr(oreg[h][ks], dOg + r + 16 * ks);
       }
-      const float l = a.lse[(size_t)bh * n + qr];
+      const float l = a.lse[at.l + qr];
       Lq[h] = (l == -INFINITY || my_q >= n) ? INFINITY : l * kLog2e;
-      Dq[h] = a.dvec[(size_t)bh * n + qr];
+      Dq[h] = a.dvec[at.l + qr];
     }
 
     f32x16 negD[2];  // -D of each block's query, the dP^T accumulators' starting value
@@ -627,7 +640,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int h = 0; h < 2; ++h) {
         const int my_q = qw0 + 32 * h + c32;
         if (my_q < n) {
-          uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
+          uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + at.q + (size_t)my_q * qsr;
           for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(dqp + c) = u32x4{0u, 0u, 0u, 0u};
         }
       }
@@ -647,15 +660,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     uint32_t d_lds = 0;
     auto dma_set = [&]() {
       const int jt = jq < j_end ? jq : j_first;
-      dk = Kg + (size_t)jt * BC * D;
-      dv = Vg + (size_t)jt * BC * D;
+      dk = Kg + (size_t)jt * BC * ksr;
+      dv = Vg + (size_t)jt * BC * ksr;
       d_last = n - 1 - jt * BC;
       d_lds = lds_base + sq + 1024 * w;
     };
     // DMA instruction i (of C) of the tile
     auto dma_tile = [&](int i) {
-      if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
-      else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
+      if (i < KD::kPer) kd.issue_at(i, dk, d_last, 2 * ksr, d_lds);
+      else vd.issue_at(i - KD::kPer, dv, d_last, 2 * ksr, d_lds + KD::kSlot);
     };
     auto dma_advance = [&]() {
       if (jq < j_end) jq = next_tile(jq);
@@ -921,7 +934,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int h = 0; h < 2; ++h) {
       const int my_q = qw0 + 32 * h + c32;
       if (my_q < n) {
-        uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + hoff + (size_t)my_q * D;
+        uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + at.q + (size_t)my_q * qsr;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -934,8 +947,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
-  const int qa = a.nqb - 1 - pq_;  // the longer block first
-  const int nrun = (CAUSAL && pq_ != qa) ? 2 : 1;
+  const int nqb = (n + BR - 1) / BR;  // this head's query blocks
+  const int qa = nqb - 1 - pq_;      // the longer block first
+  const int nrun = CAUSAL ? (pq_ < qa ? 2 : pq_ == qa ? 1 : 0) : (qa >= 0 ? 1 : 0);
 #pragma clang loop unroll(disable)
   for (int r = 0; r < nrun; ++r) {
     if (r) {
@@ -948,12 +962,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
 
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
-  const long rows = (long)bh * a.n;
   constexpr int rows_per_blk = kNT / (D / 8);
+  const int blocks_per_head = (a.n + rows_per_blk - 1) / rows_per_blk;
   timing_begin(kBwdPre, st);
-  hipLaunchKernelGGL((bwd_pre_kernel<Tag, D>), dim3((rows + rows_per_blk - 1) / rows_per_blk), dim3(kNT),
-                     0, st, reinterpret_cast<const uint16_t*>(a.o),
-                     reinterpret_cast<const uint16_t*>(a.dout), a.lse, a.dvec, a.lt, rows);
+  hipLaunchKernelGGL((bwd_pre_kernel<Tag, D>), dim3((long)bh * blocks_per_head), dim3(kNT), 0, st, a,
+                     blocks_per_head);
   hipError_t e = hipGetLastError();
   timing_end(kBwdPre, st);
   if (e != hipSuccess) return e;
@@ -965,9 +978,8 @@ hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
   if (a.hsplit > 1) {
     const long n4 = (long)a.nbhkv * a.n * (D / 4);
     timing_begin(kBwdDkDvReduce, st);
-    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<Tag>), dim3((2 * n4 + kNT - 1) / kNT), dim3(kNT), 0, st,
-                       a.pdk, a.pdv, reinterpret_cast<uint16_t*>(a.dk), reinterpret_cast<uint16_t*>(a.dv), n4,
-                       a.hsplit);
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<Tag, D>), dim3((2 * n4 + kNT - 1) / kNT), dim3(kNT), 0, st, a,
+                       n4);
     e = hipGetLastError();
     timing_end(kBwdDkDvReduce, st);
     if (e != hipSuccess) return e;
@@ -993,7 +1005,7 @@ hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a,
   a.nqb = (a.n + kDqRows - 1) / kDqRows;
   a.nblk_q = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   a.nkb = (a.n + 127) / 128;
-  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.grp) * a.hsplit;  // per K/V head and range
+  a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.sq.grp) * a.hsplit;  // per K/V head and range
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)

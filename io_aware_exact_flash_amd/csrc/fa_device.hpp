@@ -338,11 +338,12 @@ struct Dma {
   }
   // Instruction k of wave w's share of a tile, with the tile's addressing
   // hoisted by the caller (once per tile): t0 its first row, last its last
-  // valid row (rows past it re-read it), lds_w the LDS byte address of the
-  // tile plus 1024 * w.
-  __device__ __forceinline__ void issue_at(int k, const uint16_t* __restrict__ t0, int last, uint32_t lds_w) const {
+  // valid row (rows past it re-read it), rsb the source row stride in bytes
+  // (below 2^24), lds_w the LDS byte address of the tile plus 1024 * w.
+  __device__ __forceinline__ void issue_at(int k, const uint16_t* __restrict__ t0, int last, uint32_t rsb,
+                                           uint32_t lds_w) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t off = (uint32_t)min(row[k], last) * (2 * D) + colb[k];
+    const uint32_t off = __umul24((uint32_t)min(row[k], last), rsb) + colb[k];
     dma16_s(t0, off, lds_w + NW * k * 1024);
 #endif
   }
@@ -377,13 +378,6 @@ __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   int q = nblk / kX, r = nblk % kX;
   int x = b % kX, local = b / kX;
   return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
-}
-
-// K/V head read by query head bh (an index over B x H) when grp consecutive
-// query heads share one K/V head: batch bh / hq, head bh % hq reads K/V head
-// (bh % hq) / grp of the hq / grp heads of that batch.
-__device__ __forceinline__ int kv_head(int bh, int hq, int grp) {
-  return grp == 1 ? bh : (bh / hq) * (hq / grp) + (bh % hq) / grp;
 }
 
 }  // namespace fa

@@ -77,21 +77,25 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so loop control stays scalar
   const int c32 = lane & 31, g = lane >> 5;
-  const int n = a.n;
   // Causal: workgroup p of a head runs the query blocks nqb-1-p and p one
   // after the other, so every workgroup has the same number of key tiles
-  // (no long workgroup left running alone at the end of the grid).
+  // (no long workgroup left running alone at the end of the grid).  The
+  // grid covers the longest sequence; a shorter one leaves workgroups idle.
   const int per = (CAUSAL && !SPLIT) ? (a.nqb + 1) / 2 : a.nqb;
   const int nsp = SPLIT ? a.nsplit : 1;
   const int lb = xcd_remap(blockIdx.x, a.nblk);
   const int rng = lb % nsp;  // key range (split-KV)
   const int bh = (lb / nsp) / per;
   const int pb_ = (lb / nsp) % per;
-  const size_t hoff = (size_t)bh * n * D;
-  const size_t kvoff = (size_t)kv_head(bh, a.hq, a.grp) * n * D;
-  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + hoff;
-  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
-  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
+  const HeadAt at = head_at(a.sq, bh / a.sq.hq, bh % a.sq.hq, a.n);
+  const int n = at.n;           // this head's length
+  const int qsr = a.sq.qsr;     // row strides (elements)
+  const int ksr = a.sq.ksr;
+  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + at.q;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + at.kv;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + at.kv;
+  uint16_t* __restrict__ Og = reinterpret_cast<uint16_t*>(a.o) + at.q;
+  float* __restrict__ Lg = a.lse + at.l;
 
   auto run = [&](const int qb) {
     const int q0 = qb * kBR;
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     u32x4 qreg[2][KS];                  // Q^T fragments, in AGPRs
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const size_t r = (size_t)min(qw0 + 32 * h + c32, n - 1) * D + 8 * g;
+      const size_t r = (size_t)min(qw0 + 32 * h + c32, n - 1) * qsr + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) gload_agpr(qreg[h][ks], Qg + r + 16 * ks);
     }
@@ -168,13 +172,13 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
         const int my_q = qw0 + 32 * h + c32;
         if (my_q < n) {
           if constexpr (SPLIT) {
-            const size_t row = ((size_t)rng * a.nbh + bh) * n + my_q;
+            const size_t row = ((size_t)rng * a.nbh + bh) * a.n + my_q;
             for (int c = 4 * g; c < D; c += 8) *reinterpret_cast<f32x4*>(a.po + row * D + c) = f32x4{0.f, 0.f, 0.f, 0.f};
             if (g == 0) a.plse[row] = -INFINITY;
           } else {
-            uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
+            uint16_t* op = Og + (size_t)my_q * qsr;
             for (int c = 0; c < D; c += 8) *reinterpret_cast<u32x4*>(op + c) = u32x4{0u, 0u, 0u, 0u};
-            if (g == 0) a.lse[(size_t)bh * n + my_q] = -INFINITY;
+            if (g == 0) Lg[my_q] = -INFINITY;
           }
         }
       }
@@ -194,15 +198,15 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     uint32_t d_lds = 0;
     auto dma_set = [&]() {
       const int jt = jq < j_end ? jq : j_first;
-      dk = Kg + (size_t)jt * BC * D;
-      dv = Vg + (size_t)jt * BC * D;
+      dk = Kg + (size_t)jt * BC * ksr;
+      dv = Vg + (size_t)jt * BC * ksr;
       d_last = n - 1 - jt * BC;
       d_lds = lds_base + sq + 1024 * w;
     };
     // DMA instruction i (of C) of the tile
     auto dma_tile = [&](int i) {
-      if (i < KD::kPer) kd.issue_at(i, dk, d_last, d_lds);
-      else vd.issue_at(i - KD::kPer, dv, d_last, d_lds + KD::kSlot);
+      if (i < KD::kPer) kd.issue_at(i, dk, d_last, 2 * ksr, d_lds);
+      else vd.issue_at(i - KD::kPer, dv, d_last, 2 * ksr, d_lds + KD::kSlot);
     };
     auto dma_advance = [&]() {
       if (jq < j_end) jq = next_tile(jq);
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       const int my_q = qw0 + 32 * h + c32;
       if (my_q < n && SPLIT) {
-        const size_t row = ((size_t)rng * a.nbh + bh) * n + my_q;
+        const size_t row = ((size_t)rng * a.nbh + bh) * a.n + my_q;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
           }
         if (g == 0) a.plse[row] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
       } else if (my_q < n) {
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + hoff + (size_t)my_q * D;
+        uint16_t* op = Og + (size_t)my_q * qsr;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -494,12 +498,15 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
             pk[1] = pack2<Tag>(acc[h][mb][4 * r + 2] * inv, acc[h][mb][4 * r + 3] * inv);
             *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * r + 4 * g) = pk;
           }
-        if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
+        if (g == 0) Lg[my_q] = l > 0.0f ? m_run[h] * kLn2 + logf(l) : -INFINITY;
       }
     }
   };
-  const int qa = a.nqb - 1 - pb_;  // the longer block first
-  const int nrun = (CAUSAL && !SPLIT && pb_ != qa) ? 2 : 1;
+  const int nqb = (n + kBR - 1) / kBR;  // this head's query blocks
+  const int qa = nqb - 1 - pb_;         // the longer block first
+  // blocks qa and pb_ (paired causal), or qa alone; none past the end of a
+  // shorter sequence
+  const int nrun = (CAUSAL && !SPLIT) ? (pb_ < qa ? 2 : pb_ == qa ? 1 : 0) : (qa >= 0 ? 1 : 0);
 #pragma clang loop unroll(disable)
   for (int r = 0; r < nrun; ++r) {
     if (r) {

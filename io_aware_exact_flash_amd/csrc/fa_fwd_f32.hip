@@ -28,21 +28,22 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x;
   const int c32 = lane & 31, g = lane >> 5;
-  const int n = a.n;
   const int lb = xcd_remap(blockIdx.x, a.nblk);
   const int bh = lb / a.nqb;
-  const int qb = a.nqb - 1 - (lb % a.nqb);
-  const size_t hoff = (size_t)bh * n * D;
-  const float* __restrict__ Q = reinterpret_cast<const float*>(a.q) + hoff;
-  const size_t kvoff = (size_t)kv_head(bh, a.hq, a.grp) * n * D;
-  const float* __restrict__ K = reinterpret_cast<const float*>(a.k) + kvoff;
-  const float* __restrict__ V = reinterpret_cast<const float*>(a.v) + kvoff;
+  const HeadAt at = head_at(a.sq, bh / a.sq.hq, bh % a.sq.hq, a.n);
+  const int n = at.n;
+  const int qb = (n + 31) / 32 - 1 - (lb % a.nqb);  // the longest blocks first
+  if (qb < 0) return;                                // past a shorter sequence
+  const int qsr = a.sq.qsr, ksr = a.sq.ksr;
+  const float* __restrict__ Q = reinterpret_cast<const float*>(a.q) + at.q;
+  const float* __restrict__ K = reinterpret_cast<const float*>(a.k) + at.kv;
+  const float* __restrict__ V = reinterpret_cast<const float*>(a.v) + at.kv;
   const int q0 = qb * 32;
   const int my_q = q0 + c32;
 
   float qv[D / 2];
   {
-    const float* qp = Q + (size_t)min(my_q, n - 1) * D;
+    const float* qp = Q + (size_t)min(my_q, n - 1) * qsr;
 #pragma unroll
     for (int t = 0; t < D / 2; ++t) qv[t] = qp[2 * t + g];
   }
@@ -65,8 +66,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
     for (int e = lane; e < kBC * D; e += 64) {
       int r = e / D, col = e % D;
       int row = min(k0 + r, n - 1);
-      ks_[r * LD + col] = K[(size_t)row * D + col];
-      vs_[r * LD + col] = V[(size_t)row * D + col];
+      ks_[r * LD + col] = K[(size_t)row * ksr + col];
+      vs_[r * LD + col] = V[(size_t)row * ksr + col];
     }
     __syncthreads();
     f32x16 s = 0.0f;
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   const float l = half_sum(l_part);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (my_q < n) {
-    float* op = reinterpret_cast<float*>(a.o) + hoff + (size_t)my_q * D;
+    float* op = reinterpret_cast<float*>(a.o) + at.q + (size_t)my_q * qsr;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
         for (int t = 0; t < 4; ++t) o4[t] = oacc[mb][4 * r + t] * inv;
         *reinterpret_cast<f32x4*>(op + 32 * mb + 8 * r + 4 * g) = o4;
       }
-    if (g == 0) a.lse[(size_t)bh * n + my_q] = l > 0.0f ? m_run * kLn2 + logf(l) : -INFINITY;
+    if (g == 0) a.lse[at.l + my_q] = l > 0.0f ? m_run * kLn2 + logf(l) : -INFINITY;
   }
 }
 

@@ -10,7 +10,69 @@ enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
 
 constexpr int kMaskBlockTokens = 128;  // tokens per block-mask entry
 
-// Forward: one head is N x d, heads [B*H] contiguous.
+// Where the rows of one (batch, head) live.  Row t of head h of batch b of
+// a per-token tensor starts at element
+//     b * sb + h * sh + t * sr            (batched layouts), or
+//     (cu[b] + t) * sr + h * sh           (packed variable-length batches);
+// the per-row float arrays (LSE, D and the base-2 LSE) at
+//     b * lb + h * lh + t   or   cu[b] + h * lh + t.
+// Query-side tensors (q, o, dout, dq) and key-side tensors (k, v, dk, dv)
+// each have their own strides; a K/V head serves grp consecutive query heads.
+struct Seqs {
+  const int* cu;         // [B+1] sequence starts of a packed batch (device), or nullptr
+  long long qsb, qsh;    // query side: batch and head strides (elements)
+  long long ksb, ksh;    // key side
+  int qsr, ksr;          // row strides (elements, multiples of 8)
+  long long lb, lh;      // per-row arrays: batch and head strides
+  int hq;                // query heads per batch (H)
+  int grp;               // query heads per K/V head (H / Hkv)
+  int total;             // packed batches: rows in all (sequence bounds are clamped to it)
+};
+
+// Dense [B][H][N][d] tensors with Hkv K/V heads; LSE [B][H][N].
+inline Seqs dense_seqs(int H, int Hkv, int N, int d) {
+  Seqs s{};
+  s.cu = nullptr;
+  s.qsh = (long long)N * d;
+  s.qsb = s.qsh * H;
+  s.ksh = (long long)N * d;
+  s.ksb = s.ksh * Hkv;
+  s.qsr = d;
+  s.ksr = d;
+  s.lh = N;
+  s.lb = (long long)N * H;
+  s.hq = H;
+  s.grp = Hkv > 0 ? H / Hkv : 1;
+  return s;
+}
+
+// One query head (batch b, head h): element offsets of its rows, of its
+// K/V head's rows and of its per-row arrays, and its length (n_max unless
+// the batch is packed).
+struct HeadAt {
+  long long q, kv, l;
+  int n;
+};
+__device__ __forceinline__ HeadAt head_at(const Seqs& s, int b, int h, int n_max) {
+  HeadAt r;
+  const int hk = s.grp == 1 ? h : h / s.grp;
+  if (s.cu) {
+    // clamped, so that inconsistent offsets cannot reach outside the tensors
+    const int t0 = min(max(s.cu[b], 0), s.total);
+    r.n = min(max(s.cu[b + 1] - t0, 0), min(n_max, s.total - t0));
+    r.q = (long long)t0 * s.qsr + h * s.qsh;
+    r.kv = (long long)t0 * s.ksr + hk * s.ksh;
+    r.l = t0 + h * s.lh;
+  } else {
+    r.n = n_max;
+    r.q = b * s.qsb + h * s.qsh;
+    r.kv = b * s.ksb + hk * s.ksh;
+    r.l = b * s.lb + h * s.lh;
+  }
+  return r;
+}
+
+// Forward: heads of up to N rows (N = the longest sequence when packed).
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -23,10 +85,8 @@ struct FwdArgs {
   int nqb;               // query blocks per head
   int nblk;              // total workgroups
   float c;               // scale * log2(e)
-  // grouped K/V heads: query head i of a batch reads K/V head i / grp
-  int hq;                // query heads per batch (H)
-  int grp;               // query heads per K/V head (H / Hkv; 1 = one K/V head per query head)
-  // split-KV forward only
+  Seqs sq;               // layout of the tensors and of lse
+  // split-KV forward only (dense layout)
   int nsplit;            // key ranges per query row
   int nbh;               // B*H
   float* po;             // [nsplit][B*H][N][d] partial outputs, each normalised by its own l
@@ -54,17 +114,18 @@ struct BwdArgs {
   int nkb;               // key blocks per head (dK/dV pass)
   float scale;
   float c;               // scale * log2(e)
-  // grouped K/V heads (as in FwdArgs): the dK/dV pass runs per K/V head and
-  // sums over the grp query heads that share it
-  int hq;
-  int grp;
+  // layout of the tensors, of lse and of the workspace arrays dvec and lt;
+  // the dK/dV pass runs per K/V head and sums over the grp query heads that
+  // share it
+  Seqs sq;
   // hsplit > 1: the group's query heads are cut into hsplit ranges swept by
   // separate workgroups, each writing scaled float32 partial dK, dV; a
   // reduction pass sums them into dk, dv
   int hsplit;
   int nbhkv;             // B*Hkv
-  float* pdk;            // [hsplit][B*Hkv][N][d]
+  float* pdk;            // [hsplit][B*Hkv][N][d] (N = the longest sequence)
   float* pdv;            // [hsplit][B*Hkv][N][d]
+  int hkv;               // K/V heads per batch
 };
 
 // (K/V head, key block) units the dK/dV pass aims for before it cuts groups

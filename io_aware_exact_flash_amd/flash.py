@@ -40,6 +40,10 @@ SIGNATURES = {
     "flash_attn_bwd_gqa_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "flash_attn_bwd_gqa": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _P, _Z,
                                 _P]),
+    "flash_attn_varlen_fwd": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _I, _P, _P, _P]),
+    "flash_attn_varlen_bwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "flash_attn_varlen_bwd": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P,
+                                   _P, _Z, _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
@@ -250,4 +254,59 @@ def bwd_gqa(q, k, v, o, dout, lse, scale=None, causal=False, workspace=None):
                                     o.data_ptr(), dout.data_ptr(), lse.data_ptr(), _scale(scale, d),
                                     int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                     ws.data_ptr(), nbytes, _stream(q)))
+    return dq, dk, dv
+
+
+def _varlen(q, k, v, cu_seqlens, *per_query):
+    """Packed batch: q (and o, dout) [total, H, d], k, v [total, Hkv, d], cu_seqlens int32 [B + 1]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed tensors must be [total, heads, d]")
+    if q.dtype not in _DT or not q.is_cuda:
+        raise ValueError("packed tensors must be float32/float16/bfloat16 on a HIP device (no CPU path exists)")
+    total, H, d = q.shape
+    for t in per_query:
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("o and dout must match q")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    Hkv = k.shape[1]
+    for t in (k, v):
+        if t.shape != (total, Hkv, d) or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("k, v must be contiguous [total, Hkv, d] with q's length, head size, dtype, device")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor on the inputs' device")
+    return cu_seqlens.numel() - 1, H, Hkv, total, d, _DT[q.dtype]
+
+
+def varlen_fwd(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False):
+    """(O [total, H, d], LSE [H, total]) = flash_attn_varlen_fwd(...)."""
+    B, H, Hkv, total, d, dt = _varlen(q, k, v, cu_seqlens)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    _check(lib().flash_attn_varlen_fwd(B, H, Hkv, total, int(max_seqlen), d, dt, cu_seqlens.data_ptr(),
+                                       q.data_ptr(), k.data_ptr(), v.data_ptr(), _scale(scale, d),
+                                       int(bool(causal)), o.data_ptr(), lse.data_ptr(), _stream(q)))
+    return o, lse
+
+
+def varlen_bwd_workspace_size(B, H, Hkv, total, max_seqlen, d, dtype=torch.bfloat16) -> int:
+    return int(lib().flash_attn_varlen_bwd_workspace_size(B, H, Hkv, total, max_seqlen, d, _DT[dtype]))
+
+
+def varlen_bwd(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, scale=None, causal=False, workspace=None):
+    """(dQ, dK, dV) = flash_attn_varlen_bwd(...); lse is the forward's [H, total]."""
+    B, H, Hkv, total, d, dt = _varlen(q, k, v, cu_seqlens, o, dout)
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, total] tensor on the inputs' device")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        nbytes = varlen_bwd_workspace_size(B, H, Hkv, total, int(max_seqlen), d, q.dtype)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        ws, nbytes = workspace, workspace.numel()
+    _check(lib().flash_attn_varlen_bwd(B, H, Hkv, total, int(max_seqlen), d, dt, cu_seqlens.data_ptr(),
+                                       q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                       lse.data_ptr(), _scale(scale, d), int(bool(causal)), dq.data_ptr(),
+                                       dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes, _stream(q)))
     return dq, dk, dv

@@ -13,6 +13,12 @@ Recipe (one generator per purpose, CPU ``torch.Generator``):
 * ``qkvdo_grouped(B, H, Hkv, N, d, dtype, seed, gain)`` draws the same way
   Q ``[B, H, N, d]``, K and V ``[B, Hkv, N, d]``, dO ``[B, H, N, d]``, in
   that order (grouped K/V heads).
+* ``seq_lengths(B, max_len, seed)`` draws B sequence lengths uniformly in
+  [1, max_len] and sets the first to max_len (the longest sequence of a
+  packed batch); ``packed_qkvdo(lengths, H, Hkv, d, dtype, seed, gain)``
+  draws Q ``[T, H, d]``, K, V ``[T, Hkv, d]``, dO ``[T, H, d]`` (T = the
+  sum of the lengths) in that order and returns them with the int32
+  offsets ``cu`` = 0, l0, l0 + l1, ... .
 * ``block_mask(T, density, seed)`` keeps every diagonal block and each
   off-diagonal block with probability p = (density T^2 - T) / (T^2 - T), so
   the expected kept fraction is ``density``; drawn as ``rand(T, T) < p``.
@@ -67,6 +73,31 @@ def qkvdo_grouped(B, H, Hkv, N, d, dtype="bf16", seed=0, gain=1.0):
             x = x * gain
         out.append(x.to(_DTYPES[dtype]))
     return tuple(out)
+
+
+def seq_lengths(B: int, max_len: int, seed: int):
+    """B lengths uniform in [1, max_len], the first one max_len."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    lens = torch.randint(1, max_len + 1, (B,), generator=g).tolist()
+    if B:
+        lens[0] = max_len
+    return lens
+
+
+def packed_qkvdo(lengths, H, Hkv, d, dtype="bf16", seed=0, gain=1.0):
+    """Packed batch: Q, K, V, dO as CPU tensors and int32 offsets cu [B + 1]."""
+    T = int(sum(lengths))
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = []
+    for heads in (H, Hkv, Hkv, H):
+        x = torch.randn((T, heads, d), generator=g, dtype=torch.float32)
+        if gain != 1.0:
+            x = x * gain
+        out.append(x.to(_DTYPES[dtype]))
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return (*out, cu)
 
 
 def block_mask(T: int, density: float, seed: int) -> torch.Tensor:

@@ -205,3 +205,46 @@ def backward_gqa(q, k, v, do, scale, causal=False):
             dk[(b, g)] += gk
             dv[(b, g)] += gv
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+# Several sequences of different lengths packed along one token axis: each
+# sequence is its own attention problem (its keys only; the causal rule
+# counts positions from its own start).  q [T, H, d], k, v [T, Hkv, d],
+# cu [B + 1] with sequence b on rows cu[b] .. cu[b+1]-1; LSE is [H, T].
+
+def forward_varlen(q, k, v, cu, scale, causal=False):
+    q = np.asarray(q, dtype=np.float64)
+    T, H, _ = q.shape
+    Hkv = k.shape[1]
+    O = np.zeros(q.shape)
+    L = np.full((H, T), -np.inf)
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e <= s:
+            continue
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            O[s:e, h], L[h, s:e] = forward_head(q[s:e, h], k[s:e, g], v[s:e, g], scale, causal)
+    return O, L
+
+
+def backward_varlen(q, k, v, do, cu, scale, causal=False):
+    """(dQ [T, H, d], dK, dV [T, Hkv, d]) of sum(O o dO) for a packed batch."""
+    q = np.asarray(q, dtype=np.float64)
+    T, H, _ = q.shape
+    Hkv = k.shape[1]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e <= s:
+            continue
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            gq, gk, gv = backward_head(q[s:e, h], k[s:e, g], v[s:e, g], do[s:e, h], scale, causal)
+            dq[s:e, h] = gq
+            dk[s:e, g] += gk
+            dv[s:e, g] += gv
+    return dq, dk, dv

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     for required in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_blocksparse_fwd",
                      "flash_attn_blocksparse_bwd", "flash_attn_bwd_workspace_size",
                      "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_size",
-                     "flash_attn_fwd_gqa", "flash_attn_bwd_gqa"):
+                     "flash_attn_fwd_gqa", "flash_attn_bwd_gqa", "flash_attn_varlen_fwd",
+                     "flash_attn_varlen_bwd", "flash_attn_varlen_bwd_workspace_size"):
         assert required in names
 
 
@@ -228,6 +229,52 @@ def test_gqa_other_checks_and_empty_problems():
     assert _gqa_fwd(4, 2, v=FAKE_MISALIGNED) == flash.FA_ERR_INVALID_ARGUMENT
     assert _gqa_fwd(0, 0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
     assert _gqa_fwd(4, 2, N=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
+
+
+def _vl_fwd(B=2, H=4, Hkv=2, total=500, max_seqlen=300, d=64, dt=flash.FA_BF16, cu=FAKE, **kw):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE)
+    p.update(kw)
+    return flash.lib().flash_attn_varlen_fwd(B, H, Hkv, total, max_seqlen, d, dt, cu, p["q"], p["k"], p["v"],
+                                             0.125, 1, p["o"], p["lse"], None)
+
+
+def _vl_bwd(B=2, H=4, Hkv=2, total=500, max_seqlen=300, d=64, dt=flash.FA_BF16, cu=FAKE, ws_bytes=None):
+    need = flash.lib().flash_attn_varlen_bwd_workspace_size(B, H, max(Hkv, 1), total, max_seqlen, d, dt)
+    return flash.lib().flash_attn_varlen_bwd(B, H, Hkv, total, max_seqlen, d, dt, cu, *[FAKE] * 6, 0.125, 0,
+                                             *[FAKE] * 4, need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(cu=FAKE + 2), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(total=-1), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen=-3), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hkv=3), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(H=1 << 16, Hkv=1 << 16, d=128), flash.FA_ERR_UNSUPPORTED),
+    (dict(d=80), flash.FA_ERR_UNSUPPORTED),
+])
+def test_varlen_validation(kw, code):
+    assert _vl_fwd(**kw) == code
+    assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_varlen_fwd:")
+    assert _vl_bwd(**kw) == code
+    assert flash.lib().flash_attn_last_error().decode().startswith("flash_attn_varlen_bwd:")
+
+
+def test_varlen_workspace_and_empty():
+    lib = flash.lib()
+    r256 = lambda b: (b + 255) // 256 * 256
+    # per-row arrays of H*total rows (two, each + 256 spare bytes); 2 sequences x 1 K/V head x
+    # ceil(300/128) = 6 units, group of 4: 4 ranges of float32 partials [4][B*Hkv][300][64]
+    assert lib.flash_attn_varlen_bwd_workspace_size(2, 4, 1, 500, 300, 64, flash.FA_BF16) == \
+        2 * (r256(4 * 500 * 4) + 256) + 2 * r256(4 * 2 * 300 * 64 * 4)
+    assert lib.flash_attn_varlen_bwd_workspace_size(2, 4, 4, 500, 300, 64, flash.FA_BF16) == \
+        2 * (r256(4 * 500 * 4) + 256)
+    assert lib.flash_attn_varlen_bwd_workspace_size(2, 4, 4, 0, 300, 64, flash.FA_BF16) == 0
+    assert _vl_bwd(Hkv=1, ws_bytes=2 * (r256(4 * 500 * 4) + 256)) == flash.FA_ERR_WORKSPACE_TOO_SMALL
+    assert _vl_bwd(dt=flash.FA_F32) == flash.FA_ERR_UNSUPPORTED
+    # empty batches launch nothing
+    assert _vl_fwd(total=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
+    assert _vl_fwd(B=0, cu=None, total=0, max_seqlen=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -484,3 +484,60 @@ def test_gqa_gradients_by_central_differences(H, Hkv, causal):
             X[idx] = old
             num[idx] = (fp - fm) / (2 * eps)
         assert np.abs(num - G[name]).max() <= 1e-6 * max(1.0, np.abs(G[name]).max()), name
+
+
+# ------------------------------------------------------- P10 packed variable-length batches
+def test_varlen_each_sequence_is_its_own_problem():
+    """Packed sequences against pure-Python attention on each sequence alone
+    (causal positions counted from the sequence start), with grouped heads;
+    an empty sequence contributes nothing."""
+    r = _rng(41)
+    lens, H, Hkv, d, s = [3, 0, 5, 1], 4, 2, 3, 0.7
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = r.standard_normal((T, H, d))
+    k = r.standard_normal((T, Hkv, d))
+    v = r.standard_normal((T, Hkv, d))
+    for causal in (False, True):
+        O, L = A.forward_varlen(q, k, v, cu, s, causal)
+        ok = (lambda i, j: j <= i) if causal else (lambda i, j: True)
+        for b in range(len(lens)):
+            a, e = cu[b], cu[b + 1]
+            for h in range(H):
+                g = h // (H // Hkv)
+                if e == a:
+                    continue
+                Ob, Lb = brute_attention(q[a:e, h].tolist(), k[a:e, g].tolist(), v[a:e, g].tolist(), s, ok)
+                np.testing.assert_allclose(O[a:e, h], Ob, rtol=1e-12, atol=1e-13)
+                np.testing.assert_allclose(L[h, a:e], Lb, rtol=1e-12, atol=1e-13)
+        # changing the tokens of one sequence leaves the others untouched
+        q2 = q.copy()
+        q2[cu[2]:cu[3]] += 1.0
+        O2, _ = A.forward_varlen(q2, k, v, cu, s, causal)
+        np.testing.assert_array_equal(O2[:cu[2]], O[:cu[2]])
+        np.testing.assert_array_equal(O2[cu[3]:], O[cu[3]:])
+
+
+def test_varlen_gradients_by_central_differences():
+    r = _rng(43)
+    lens, H, Hkv, d, s = [3, 2], 2, 1, 2, 0.9
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = r.standard_normal((T, H, d))
+    k = r.standard_normal((T, Hkv, d))
+    v = r.standard_normal((T, Hkv, d))
+    do = r.standard_normal((T, H, d))
+    for causal in (False, True):
+        G = dict(zip("qkv", A.backward_varlen(q, k, v, do, cu, s, causal)))
+        eps = 1e-6
+        for name, X in (("q", q), ("k", k), ("v", v)):
+            num = np.zeros_like(X)
+            for idx in np.ndindex(*X.shape):
+                old = X[idx]
+                X[idx] = old + eps
+                fp = float((A.forward_varlen(q, k, v, cu, s, causal)[0] * do).sum())
+                X[idx] = old - eps
+                fm = float((A.forward_varlen(q, k, v, cu, s, causal)[0] * do).sum())
+                X[idx] = old
+                num[idx] = (fp - fm) / (2 * eps)
+            assert np.abs(num - G[name]).max() <= 1e-6 * max(1.0, np.abs(G[name]).max()), (name, causal)

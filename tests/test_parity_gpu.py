@@ -356,3 +356,81 @@ def test_gqa_empty_inputs():
         dq, dk, dv = flash.bwd_gqa(q, k, k, o, q, lse)
         torch.cuda.synchronize()
         assert o.shape == q.shape and dk.shape == k.shape
+
+
+VARLEN_CASES = [
+    # (lengths, H, Hkv)
+    ([200, 1, 333, 0, 64, 519], 4, 2),
+    ([300, 300], 2, 2),
+    ([17], 3, 1),
+    ([1000, 129, 256, 7], 2, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(VARLEN_CASES)))
+def test_varlen_forward_backward(dtype, d, causal, case):
+    """Packed variable-length batch (token-major [total, heads, d]) against the
+    oracle run on each sequence alone; empty and one-token sequences
+    included.  dK, dV of a shared head use the grouped-head bound."""
+    lens, H, Hkv = VARLEN_CASES[case]
+    G = H // Hkv
+    q, k, v, do, cu = workloads.packed_qkvdo(lens, H, Hkv, d, dtype, seed=600 + case + d)
+    f64 = [t.to(torch.float64).numpy() for t in (q, k, v, do)]
+    gq, gk, gv, gdo, gcu = (t.cuda() for t in (q, k, v, do, cu))
+    s = fp32_scale(d)
+    o, lse = flash.varlen_fwd(gq, gk, gv, gcu, max(lens), scale=s, causal=causal)
+    dq, dk, dv = flash.varlen_bwd(gq, gk, gv, o, gdo, lse, gcu, max(lens), scale=s, causal=causal)
+    torch.cuda.synchronize()
+    O, L = A.forward_varlen(*f64[:3], cu.numpy(), s, causal)
+    gQ, gK, gV = A.backward_varlen(*f64, cu.numpy(), s, causal)
+    tol = TOL[dtype]
+    compare("O", o, O, tol["o"], REL_RMS[dtype])
+    compare_lse("LSE", lse, L, tol["lse"])
+    compare("dQ", dq, gQ, tol["grad"], REL_RMS[dtype])
+    compare("dK", dk, gK, tol["grad"] * max(1.0, G ** 0.5), REL_RMS[dtype])
+    compare("dV", dv, gV, tol["grad"] * max(1.0, G ** 0.5), REL_RMS[dtype])
+
+
+def test_varlen_float32_forward():
+    lens, H, Hkv, d = [100, 37, 256], 2, 1, 64
+    q, k, v, _, cu = workloads.packed_qkvdo(lens, H, Hkv, d, "f32", seed=71)
+    f64 = [t.to(torch.float64).numpy() for t in (q, k, v)]
+    s = fp32_scale(d)
+    o, lse = flash.varlen_fwd(q.cuda(), k.cuda(), v.cuda(), cu.cuda(), max(lens), scale=s, causal=True)
+    torch.cuda.synchronize()
+    O, L = A.forward_varlen(*f64, cu.numpy(), s, True)
+    compare("O", o, O, TOL["f32"]["o"], REL_RMS["f32"])
+    compare_lse("LSE", lse, L, TOL["f32"]["lse"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hkv", [4, 2])
+def test_bnhd_layout_matches_dense_bitwise(causal, Hkv):
+    """A [B, N, H, d] batch passed as a packed batch of equal lengths runs the
+    same arithmetic as the dense [B, H, N, d] calls: identical bits."""
+    B, H, N, d = 3, 4, 700, 128
+    q, k, v, do = (t.cuda() for t in workloads.qkvdo_grouped(B, H, Hkv, N, d, "bf16", seed=93))
+    o, lse = flash.fwd_gqa(q, k, v, causal=causal)
+    dq, dk, dv = flash.bwd_gqa(q, k, v, o, do, lse, causal=causal)
+    tok = lambda t: t.transpose(1, 2).contiguous().view(B * N, t.shape[1], d)  # [B,H,N,d] -> [B*N, H, d]
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+    o2, lse2 = flash.varlen_fwd(tok(q), tok(k), tok(v), cu, N, causal=causal)
+    dq2, dk2, dv2 = flash.varlen_bwd(tok(q), tok(k), tok(v), o2, tok(do), lse2, cu, N, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, tok(o))
+    assert torch.equal(lse2, lse.permute(1, 0, 2).reshape(H, B * N))
+    for a, b in ((dq2, dq), (dk2, dk), (dv2, dv)):
+        assert torch.equal(a, tok(b))
+
+
+def test_varlen_empty_batches():
+    for lens in ([], [0, 0]):
+        q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+        cu = torch.zeros(len(lens) + 1, dtype=torch.int32, device="cuda")
+        o, lse = flash.varlen_fwd(q, q, q, cu, max(lens, default=0))
+        dq, dk, dv = flash.varlen_bwd(q, q, q, o, q, lse, cu, max(lens, default=0))
+        torch.cuda.synchronize()
+        assert o.shape == q.shape and lse.shape == (2, 0)
