@@ -236,6 +236,8 @@ VARIANTS = {
                 dtype="bf16", causal=True, seed=12),
     "mqa": dict(name="multi-query (one K/V head)", B=4, H=32, Hkv=1, N=4096, d=128,
                 dtype="bf16", causal=True, seed=13),
+    "varlen": dict(name="packed variable-length batch", B=8, H=16, Hkv=16, max_len=4096, d=128,
+                   dtype="bf16", causal=True, seed=14),
 }
 
 
@@ -302,6 +304,36 @@ def run_variants(steps, warmup):
                     "tflops": {n: round(fl / (t * 1e-3) / 1e12, 1) for n, (t, fl) in res.items()}}
         log(f"variant {key}: {out[key]}")
         del q, k, vv, do, krep, vrep, ws, wsg, o, lse
+
+    v = VARIANTS["varlen"]
+    lens = workloads.seq_lengths(v["B"], v["max_len"], v["seed"])
+    q, k, vv, do, cu = workloads.packed_qkvdo(lens, v["H"], v["Hkv"], v["d"], v["dtype"], seed=v["seed"])
+    q, k, vv, do, cu = (t.cuda() for t in (q, k, vv, do, cu))
+    T, mx, c = sum(lens), max(lens), v["causal"]
+    f = sum(4.0 * v["H"] * n * n * v["d"] * (0.5 if c else 1.0) for n in lens)
+    wsv = torch.empty(flash.varlen_bwd_workspace_size(v["B"], v["H"], v["Hkv"], T, mx, v["d"], q.dtype),
+                      dtype=torch.uint8, device=q.device)
+    o, lse = flash.varlen_fwd(q, k, vv, cu, mx, causal=c)
+    # the same sequences padded to the longest one, through the dense calls
+    qp, kp, vp, dop = (torch.zeros((v["B"], v["H"], mx, v["d"]), dtype=q.dtype, device=q.device)
+                       for _ in range(4))
+    ws = torch.empty(flash.bwd_workspace_size(v["B"], v["H"], mx, v["d"], q.dtype), dtype=torch.uint8,
+                     device=q.device)
+    op, lsep = flash.fwd(qp, kp, vp, causal=c)
+    res = {
+        "packed_fwd": time_ms(lambda: flash.varlen_fwd(q, k, vv, cu, mx, causal=c), steps, warmup),
+        "packed_bwd": time_ms(lambda: flash.varlen_bwd(q, k, vv, o, do, lse, cu, mx, causal=c, workspace=wsv),
+                              steps, warmup),
+        "padded_fwd": time_ms(lambda: flash.fwd(qp, kp, vp, causal=c), steps, warmup),
+        "padded_bwd": time_ms(lambda: flash.bwd(qp, kp, vp, op, dop, lsep, causal=c, workspace=ws), steps, warmup),
+    }
+    out["varlen"] = {"workload": f"{v['name']}: lengths {lens} (total {T}), H={v['H']} d={v['d']} {v['dtype']} "
+                                 f"causal; padded_* = the dense calls on the batch padded to {mx}",
+                     "ms": {n: round(t, 4) for n, t in res.items()},
+                     "tflops_useful": {n: round((2.5 * f if n.endswith("bwd") else f) / (t * 1e-3) / 1e12, 1)
+                                       for n, t in res.items()}}
+    log(f"variant varlen: {out['varlen']}")
+    del q, k, vv, do, cu, o, lse, qp, kp, vp, dop, op, lsep, ws, wsv
     torch.cuda.empty_cache()
     return out
 
@@ -317,7 +349,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=10, help="(batch, head) pairs the oracle baseline runs (about 1 s each at N=8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
-                    help="also time the split-KV forward and grouped K/V heads (adds a 'variants' object)")
+                    help="also time the split-KV forward, grouped K/V heads and a packed variable-length "
+                         "batch (adds a 'variants' object)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy a device buffer of this many bytes 3 times "
                          "(calibrates the HBM byte counters of a profiling run)")

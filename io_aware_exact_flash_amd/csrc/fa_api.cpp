@@ -237,6 +237,7 @@ fa_status check_varlen(const char* fn, int B, int H, int Hkv, int total, int max
   q.hq = H;
   q.grp = Hkv > 0 ? H / Hkv : 1;
   q.total = total;
+  q.nb = B;
   *out = q;
   return FA_OK;
 }

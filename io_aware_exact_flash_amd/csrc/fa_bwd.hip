@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(BwdArgs args, int blocks_p
   constexpr int RPB = kNT / TPR;
   const int bh = blockIdx.x / blocks_per_head;
   const int row = (blockIdx.x % blocks_per_head) * RPB + threadIdx.x / TPR;
-  const HeadAt at = head_at(args.sq, bh / args.sq.hq, bh % args.sq.hq, args.n);
+  const HeadAt at = query_head(args.sq, bh, args.n);
   const int c = threadIdx.x % TPR;
   const uint16_t* __restrict__ o = reinterpret_cast<const uint16_t*>(args.o) + at.q;
   const uint16_t* __restrict__ dout = reinterpret_cast<const uint16_t*>(args.dout) + at.q;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int bh = unit / a.hsplit;   // K/V head, an index over B x Hkv
   const int rng = unit % a.hsplit;  // range of the group's query heads
   // the group's first query head locates the K/V head and the sequence
-  const HeadAt at = head_at(a.sq, bh / a.hkv, (bh % a.hkv) * a.sq.grp, a.n);
+  const HeadAt at = group_head(a.sq, bh, a.hkv, a.n);
   const int n = at.n;  // this sequence's length
   const int qsr = a.sq.qsr, ksr = a.sq.ksr;
   const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + at.kv;
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kNT) void bwd_dkdv_reduce_kernel(BwdArgs a, long n4
   const int c = 4 * (int)(j % (D / 4));
   const int bhkv = (int)(row / a.n);
   const int t = (int)(row % a.n);
-  const HeadAt at = head_at(a.sq, bhkv / a.hkv, (bhkv % a.hkv) * a.sq.grp, a.n);
+  const HeadAt at = group_head(a.sq, bhkv, a.hkv, a.n);
   if (t >= at.n) return;  // past a shorter sequence
   const float* p = (is_v ? a.pdv : a.pdk) + row * D + c;
   f32x4 acc = *reinterpret_cast<const f32x4*>(p);
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   const int lb = xcd_remap(blockIdx.x, a.nblk_q);
   const int bh = lb / per;
   const int pq_ = lb % per;
-  const HeadAt at = head_at(a.sq, bh / a.sq.hq, bh % a.sq.hq, a.n);
+  const HeadAt at = query_head(a.sq, bh, a.n);
   const int n = at.n;  // this head's length
   const int qsr = a.sq.qsr, ksr = a.sq.ksr;
   const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + at.q;

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   const int rng = lb % nsp;  // key range (split-KV)
   const int bh = (lb / nsp) / per;
   const int pb_ = (lb / nsp) % per;
-  const HeadAt at = head_at(a.sq, bh / a.sq.hq, bh % a.sq.hq, a.n);
+  const HeadAt at = query_head(a.sq, bh, a.n);
   const int n = at.n;           // this head's length
   const int qsr = a.sq.qsr;     // row strides (elements)
   const int ksr = a.sq.ksr;

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   const int c32 = lane & 31, g = lane >> 5;
   const int lb = xcd_remap(blockIdx.x, a.nblk);
   const int bh = lb / a.nqb;
-  const HeadAt at = head_at(a.sq, bh / a.sq.hq, bh % a.sq.hq, a.n);
+  const HeadAt at = query_head(a.sq, bh, a.n);
   const int n = at.n;
   const int qb = (n + 31) / 32 - 1 - (lb % a.nqb);  // the longest blocks first
   if (qb < 0) return;                                // past a shorter sequence

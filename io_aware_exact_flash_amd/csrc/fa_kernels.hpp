@@ -27,6 +27,7 @@ struct Seqs {
   int hq;                // query heads per batch (H)
   int grp;               // query heads per K/V head (H / Hkv)
   int total;             // packed batches: rows in all (sequence bounds are clamped to it)
+  int nb;                // packed batches: number of sequences
 };
 
 // Dense [B][H][N][d] tensors with Hkv K/V heads; LSE [B][H][N].
@@ -53,6 +54,34 @@ struct HeadAt {
   long long q, kv, l;
   int n;
 };
+__device__ __forceinline__ HeadAt head_at(const Seqs& s, int b, int h, int n_max);
+
+// Linear head index -> (batch, head), `heads` heads per batch.  Dense
+// batches enumerate heads batch-major.  Packed batches enumerate them
+// head-major, so that the contiguous ranges of heads the workgroup
+// remapping gives each XCD hold sequences of every length (balanced work).
+__device__ __forceinline__ void split_bh(const Seqs& s, int bh, int heads, int& b, int& h) {
+  if (s.cu) {
+    b = bh % s.nb;
+    h = bh / s.nb;
+  } else {
+    b = bh / heads;
+    h = bh % heads;
+  }
+}
+// Query head bh (over B x H).
+__device__ __forceinline__ HeadAt query_head(const Seqs& s, int bh, int n_max) {
+  int b, h;
+  split_bh(s, bh, s.hq, b, h);
+  return head_at(s, b, h, n_max);
+}
+// The first query head of K/V head bh (over B x Hkv, hkv per batch).
+__device__ __forceinline__ HeadAt group_head(const Seqs& s, int bh, int hkv, int n_max) {
+  int b, hk;
+  split_bh(s, bh, hkv, b, hk);
+  return head_at(s, b, hk * s.grp, n_max);
+}
+
 __device__ __forceinline__ HeadAt head_at(const Seqs& s, int b, int h, int n_max) {
   HeadAt r;
   const int hk = s.grp == 1 ? h : h / s.grp;
