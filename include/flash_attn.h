@@ -247,6 +247,37 @@ fa_status flash_attn_varlen_bwd(int B, int H, int Hkv, int total, int max_seqlen
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dropout on the attention probabilities, fused into the passes [FA1
+ * summary: matmul, softmax, dropout and mask fused into one kernel]:
+ *   O = (P o Z) V / (1 - p'),  LSE as without dropout,
+ * with Z in {0, 1} drawn, never stored, from the counter-based generator
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): element (query i,
+ * key j) of head h of batch b is kept iff byte j % 4 of word i % 4 of
+ *   Philox4x32-10(counter = (i / 4, j / 4, b*H + h, offset),
+ *                 key = (seed & 0xffffffff, seed >> 32))
+ * is at least t = floor(256 dropout_p + 0.5), and p' = t / 256 (the drop
+ * probability is quantised to 1/256).  The backward recomputes the same Z
+ * from (seed, offset) and returns the exact gradient of that O:
+ * dV = (P o Z)^T dO / (1 - p'), dS = P o (dP' o Z / (1 - p') - D) with
+ * dP' = dO V^T and D = rowsum(dO o O).  dropout_p in [0, 1) with t <= 255
+ * (FA_ERR_INVALID_ARGUMENT otherwise); dtype FA_F16 or FA_BF16.  Other
+ * arguments, layouts and errors as flash_attn_fwd / flash_attn_bwd (same
+ * workspace); seed, offset and dropout_p must equal the forward's.
+ */
+fa_status flash_attn_fwd_dropout(int B, int H, int N, int d, fa_dtype dtype,
+                                 const void* q, const void* k, const void* v,
+                                 float scale, int causal,
+                                 float dropout_p, uint64_t seed, uint32_t offset,
+                                 void* o, float* lse, hipStream_t stream);
+fa_status flash_attn_bwd_dropout(int B, int H, int N, int d, fa_dtype dtype,
+                                 const void* q, const void* k, const void* v,
+                                 const void* o, const void* dout, const float* lse,
+                                 float scale, int causal,
+                                 float dropout_p, uint64_t seed, uint32_t offset,
+                                 void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-kernel timing (diagnostics; not part of the method).  While enabled,
  * every kernel the library launches is bracketed by two HIP events recorded
  * on its launch stream.  flash_attn_timing_collect waits for the recorded
@@ -254,7 +285,8 @@ fa_status flash_attn_varlen_bwd(int B, int H, int Hkv, int total, int max_seqlen
  * launch count since the previous collect, and forgets them.  Kernel
  * classes: 0 forward (16-bit), 1 forward (float32), 2 backward D pre-pass,
  * 3 backward dK/dV pass, 4 backward dQ pass, 5 split-KV forward ranges,
- * 6 split-KV merge, 7 dK/dV range sum (grouped heads);
+ * 6 split-KV merge, 7 dK/dV range sum (grouped heads), 8 forward with
+ * dropout, 9 dK/dV pass with dropout, 10 dQ pass with dropout;
  * flash_attn_kernel_name(k) names them.  Events are created on first use
  * and reused; no device memory is allocated.  Process-wide, guarded by a
  * mutex.

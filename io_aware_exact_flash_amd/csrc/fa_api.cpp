@@ -86,6 +86,22 @@ fa_status check_heads(const char* fn, int H, int Hkv) {
   return FA_OK;
 }
 
+// Dropout: drop probability p in [0, 1) quantised to t / 256 with
+// t = floor(256 p + 0.5) <= 255; kept values are scaled by 256 / (256 - t).
+fa_status make_drop(const char* fn, float p, uint64_t seed, uint32_t offset, fa::Drop* d) {
+  if (!(std::isfinite(p) && p >= 0.0f && p < 1.0f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: dropout_p must lie in [0, 1) (got %g)", fn, (double)p);
+  const double t = std::floor((double)p * 256.0 + 0.5);
+  if (t > 255.0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: dropout_p %g rounds to a drop threshold of 256/256", fn, (double)p);
+  d->thr = (uint32_t)t;
+  d->k0 = (uint32_t)seed;
+  d->k1 = (uint32_t)(seed >> 32);
+  d->offset = offset;
+  d->scale = (float)(256.0 / (256.0 - t));
+  return FA_OK;
+}
+
 fa_status check_mask(const char* fn, const uint8_t* mask, int mask_block) {
   if (!mask) return fail(FA_ERR_INVALID_ARGUMENT, "%s: block_mask is null", fn);
   if (mask_block != fa::kMaskBlockTokens)
@@ -129,10 +145,11 @@ size_t gqa_workspace_bytes(long long rows, long long bhkv, long long n, int d, i
 fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype dtype, const void* q,
                   const void* k, const void* v, float scale, int causal, const uint8_t* mask,
                   int mask_block, bool sparse, void* o, float* lse, hipStream_t stream,
-                  const fa::Seqs* seqs = nullptr) {
+                  const fa::Seqs* seqs = nullptr, const fa::Drop* drop = nullptr) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, false, &p);
   if (s != FA_OK) return s;
+  if (drop && dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "%s: float32 dropout is not supported", fn);
   if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
   if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
   if (p.empty || (seqs && seqs->total == 0)) return FA_OK;
@@ -151,10 +168,15 @@ fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   a.n = N;
   a.c = scale * 1.4426950408889634f;
   a.sq = seqs ? *seqs : fa::dense_seqs(H, Hkv, N, d);
-  hipError_t e = (dtype == FA_F32)
-                     ? fa::launch_fwd_f32(d, causal != 0, sparse, p.bh, a, stream)
-                     : fa::launch_fwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0,
-                                      sparse, p.bh, a, stream);
+  const fa::Dt dt = dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16;
+  hipError_t e;
+  if (drop) {
+    a.drop = *drop;
+    e = fa::launch_fwd_dropout(dt, d, causal != 0, p.bh, a, stream);
+  } else {
+    e = (dtype == FA_F32) ? fa::launch_fwd_f32(d, causal != 0, sparse, p.bh, a, stream)
+                          : fa::launch_fwd(dt, d, causal != 0, sparse, p.bh, a, stream);
+  }
   return hip_status(fn, e);
 }
 
@@ -162,7 +184,7 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
                   const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   float scale, int causal, const uint8_t* mask, int mask_block, bool sparse,
                   void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream,
-                  const fa::Seqs* seqs = nullptr) {
+                  const fa::Seqs* seqs = nullptr, const fa::Drop* drop = nullptr) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, true, &p);
   if (s != FA_OK) return s;
@@ -207,8 +229,14 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
     a.pdk = reinterpret_cast<float*>(part);
     a.pdv = reinterpret_cast<float*>(part + partial_bytes(bhkv, N, d, hsplit));
   }
-  hipError_t e = fa::launch_bwd(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, sparse,
-                                p.bh, a, stream);
+  const fa::Dt dt = dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16;
+  hipError_t e;
+  if (drop) {
+    a.drop = *drop;
+    e = fa::launch_bwd_dropout(dt, d, causal != 0, p.bh, a, stream);
+  } else {
+    e = fa::launch_bwd(dt, d, causal != 0, sparse, p.bh, a, stream);
+  }
   return hip_status(fn, e);
 }
 
@@ -315,8 +343,9 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* kKernelNames[fa::kNumKernels] = {"fwd",       "fwd_f32",   "bwd_pre",        "bwd_dkdv",
-                                            "bwd_dq",    "fwd_split", "fwd_merge",      "bwd_dkdv_reduce"};
+const char* kKernelNames[fa::kNumKernels] = {"fwd",          "fwd_f32",   "bwd_pre",         "bwd_dkdv",
+                                            "bwd_dq",       "fwd_split", "fwd_merge",       "bwd_dkdv_reduce",
+                                            "fwd_dropout",  "bwd_dkdv_dropout", "bwd_dq_dropout"};
 
 }  // namespace
 
@@ -489,6 +518,31 @@ FA_EXPORT fa_status flash_attn_varlen_bwd(int B, int H, int Hkv, int total, int 
   if (s != FA_OK) return s;
   return run_bwd(fn, B, H, Hkv, max_seqlen, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0, false, dq,
                  dk, dv, workspace, workspace_bytes_, stream, &sq);
+}
+
+FA_EXPORT fa_status flash_attn_fwd_dropout(int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                                           const void* k, const void* v, float scale, int causal, float dropout_p,
+                                           uint64_t seed, uint32_t offset, void* o, float* lse,
+                                           hipStream_t stream) {
+  const char* fn = "flash_attn_fwd_dropout";
+  fa::Drop dr;
+  fa_status s = make_drop(fn, dropout_p, seed, offset, &dr);
+  if (s != FA_OK) return s;
+  return run_fwd(fn, B, H, H, N, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o, lse, stream, nullptr,
+                 &dr);
+}
+
+FA_EXPORT fa_status flash_attn_bwd_dropout(int B, int H, int N, int d, fa_dtype dtype, const void* q,
+                                           const void* k, const void* v, const void* o, const void* dout,
+                                           const float* lse, float scale, int causal, float dropout_p,
+                                           uint64_t seed, uint32_t offset, void* dq, void* dk, void* dv,
+                                           void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  const char* fn = "flash_attn_bwd_dropout";
+  fa::Drop dr;
+  fa_status s = make_drop(fn, dropout_p, seed, offset, &dr);
+  if (s != FA_OK) return s;
+  return run_bwd(fn, B, H, H, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0, false, dq, dk, dv,
+                 workspace, workspace_bytes_, stream, nullptr, &dr);
 }
 
 FA_EXPORT const char* flash_attn_status_string(fa_status status) {

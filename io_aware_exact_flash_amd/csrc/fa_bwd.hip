@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(BwdArgs args, int blocks_p
 // feed the dV/dK products as B operands without leaving registers.  The
 // sweep is software-pipelined by one tile: S, dP of the next tile run
 // interleaved with the vector work (P, dS) of the current one.
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool DROP = false>
 __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 128;            // keys per workgroup (4 waves x 32)
   constexpr int BQ = 32;              // queries per tile
@@ -133,7 +133,20 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const uint16_t* dOg = nullptr;
   const float* Ltg = nullptr;
   const float* Dg = nullptr;
+  int hcan = 0;  // b*H + h of the current query head (dropout counter)
+  int hcan0 = 0;
+  // dropout parameters, held in vector registers (scalar registers are
+  // the scarcer file in this kernel)
+  uint32_t d_k0 = a.drop.k0, d_k1 = a.drop.k1, d_off = a.drop.offset, d_thr = a.drop.thr;
+  float d_scale = a.drop.scale;
+  if constexpr (DROP) {
+    int b_, hk_;
+    split_bh(a.sq, bh, a.hkv, b_, hk_);
+    hcan0 = b_ * a.sq.hq + hk_ * grp;
+    asm volatile("" : "+v"(d_k0), "+v"(d_k1), "+v"(d_off), "+v"(d_thr), "+v"(d_scale), "+v"(hcan0));
+  }
   auto set_head = [&](int hg) {  // query head hg of the group
+    hcan = hcan0 + hg;
     const long long qo = at.q + hg * a.sq.qsh;
     const long long lo = at.l + hg * a.sq.lh;
     Qg = reinterpret_cast<const uint16_t*>(a.q) + qo;
@@ -293,6 +306,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       vm_wait<C>();      // tile `in` has landed (for this wave's share) ...
       wg_barrier();      // ... for every wave; the slot refilled below is free
       const int q0 = i * BQ;
+      // dropout bytes of tile i: the quad's four lanes (keys 4m .. 4m+3)
+      // draw the 4x4 blocks of queries 8a + 4g .. 8a + 4g + 3 (a = lane % 4);
+      // a byte transpose and a word exchange leave each lane its own key's
+      // 16 bytes in element order
+      u32x4 kb;
+      if constexpr (DROP) {
+        const u32x4 ctr = {(uint32_t)(q0 / 4 + g + 2 * (c32 & 3)), (uint32_t)my_k >> 2, (uint32_t)hcan, d_off};
+        kb = quad_transpose4(byte_transpose4(philox4x32_10(ctr, d_k0, d_k1)), lane);
+      }
       const lchar* base = lds_ptr(smem) + so;
       // element v holds query q0 + 4g + 8(v/4) + v%4 (and this lane's key);
       // it is allowed while that offset lies in [lo, hi)
@@ -318,7 +340,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       auto st2 = [&](int v) { s[X][v] = fast_exp2(s[X][v]); };
       auto st3 = [&](int v) {
         float pp = s[X][v];
-        float x = pp * (dp[X][v] - dv(v));
+        float x;
+        if constexpr (DROP) {  // dP = dP' Z / (1 - p) with dP' = dO V^T; dV takes P Z
+          const uint32_t km = keep_mask(kb, v, d_thr);
+          x = pp * fmaf(dp[X][v], masked(d_scale, km), -dv(v));
+          pp = masked(pp, km);
+        } else {
+          x = pp * (dp[X][v] - dv(v));
+        }
         if constexpr (MASK) {
           const int o = 8 * (v >> 2) + (v & 3);
           const bool dead = o < lo || o >= hi;
@@ -390,14 +419,18 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // with a tile past the end (every row dead).  The total is the same for
     // every wave; two iterations per trip keep the sets X/Y in fixed roles
     // and the accumulators out of any branch.
-    int n_pre = 0, n_plain = 0;
-    if constexpr (!SPARSE) {
-      const int T = n_tiles - i_first;
-      if constexpr (CAUSAL) n_pre = min((w + 2) & ~1, (T + 1) & ~1);
-      n_plain = max(n / BQ - (i_first + n_pre), 0) & ~1;
-    }
 #pragma clang loop unroll(disable)
     for (int hg = h_lo; hg < h_hi; ++hg) {
+      // (formed per head from an opaque copy of n: hoisted out of the head
+      // loop, these counts would hold scalar registers across the sweep)
+      int n_pre = 0, n_plain = 0;
+      if constexpr (!SPARSE) {
+        int n_ = n;
+        asm volatile("" : "+s"(n_));
+        const int T = (n_ + BQ - 1) / BQ - i_first;
+        if constexpr (CAUSAL) n_pre = min((w + 2) & ~1, (T + 1) & ~1);
+        n_plain = max(n_ / BQ - (i_first + n_pre), 0) & ~1;
+      }
       if (hg != h_lo) {
         vm_wait<0>();     // the previous head's DMA has landed ...
         __syncthreads();  // ... and every wave is out of its LDS tiles
@@ -439,6 +472,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       float* dkp = a.pdk + poff + (size_t)my_k * D;
       float* dvp = a.pdv + poff + (size_t)my_k * D;
       const float sc = a.scale;
+      const float sv = DROP ? d_scale : 1.0f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -447,7 +481,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             pk[t] = dkacc[nb][4 * r + t] * sc;
-            pv[t] = dvacc[nb][4 * r + t];
+            pv[t] = dvacc[nb][4 * r + t] * sv;
           }
           *reinterpret_cast<f32x4*>(dkp + 32 * nb + 8 * r + 4 * g) = pk;
           *reinterpret_cast<f32x4*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
@@ -463,8 +497,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
           u32x2 pk, pv;
           pk[0] = pack2<Tag>(dkacc[nb][4 * r] * sc, dkacc[nb][4 * r + 1] * sc);
           pk[1] = pack2<Tag>(dkacc[nb][4 * r + 2] * sc, dkacc[nb][4 * r + 3] * sc);
-          pv[0] = pack2<Tag>(dvacc[nb][4 * r], dvacc[nb][4 * r + 1]);
-          pv[1] = pack2<Tag>(dvacc[nb][4 * r + 2], dvacc[nb][4 * r + 3]);
+          if constexpr (DROP) {
+            const float sv = d_scale;
+            pv[0] = pack2<Tag>(dvacc[nb][4 * r] * sv, dvacc[nb][4 * r + 1] * sv);
+            pv[1] = pack2<Tag>(dvacc[nb][4 * r + 2] * sv, dvacc[nb][4 * r + 3] * sv);
+          } else {
+            pv[0] = pack2<Tag>(dvacc[nb][4 * r], dvacc[nb][4 * r + 1]);
+            pv[1] = pack2<Tag>(dvacc[nb][4 * r + 2], dvacc[nb][4 * r + 3]);
+          }
           *reinterpret_cast<u32x2*>(dkp + 32 * nb + 8 * r + 4 * g) = pk;
           *reinterpret_cast<u32x2*>(dvp + 32 * nb + 8 * r + 4 * g) = pv;
         }
@@ -960,7 +1000,147 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+// ------------------------------------------------------------ dQ pass with dropout
+// dS^T = P^T o (dP'^T Z / (1 - p) - D) with dP'^T = V dO^T and Z the
+// dropout decisions (drawn as in the forward: lane = query).  One wave per
+// 32 queries (four per workgroup), K/V tiles of 32 keys moved into LDS one
+// at a time; simpler than the pipelined pass above, whose registers leave
+// no room for the dropout decisions.
+constexpr int kDqDropRows = 128;
+
+template <typename Tag, int D, bool CAUSAL>
+__global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
+  constexpr int BC = 32;
+  constexpr int KS = D / 16, MB = D / 32, PK = BC / 16, NF = PK * MB;
+  using KL = Pad<D, true>;
+  using VL = Pad<D, false>;
+  using KD = Dma<BC, D, true, kNT / 64>;
+  using VD = Dma<BC, D, false, kNT / 64>;
+  __shared__ __attribute__((aligned(16))) char smem[KD::kSlot + VD::kSlot];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, g = lane >> 5;
+  const int nqb = (a.n + kDqDropRows - 1) / kDqDropRows;
+  const int lb = xcd_remap(blockIdx.x, a.nblk_q);
+  const int bh = lb / nqb;
+  const HeadAt at = query_head(a.sq, bh, a.n);
+  const int n = at.n;
+  const int qb = (n + kDqDropRows - 1) / kDqDropRows - 1 - lb % nqb;  // the longest blocks first
+  if (qb < 0) return;
+  const int hcan = canon_head(a.sq, bh);
+  const int qsr = a.sq.qsr, ksr = a.sq.ksr;
+  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + at.q;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + at.kv;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + at.kv;
+  const uint16_t* __restrict__ dOg = reinterpret_cast<const uint16_t*>(a.dout) + at.q;
+  const int q0 = qb * kDqDropRows;
+  const int qw0 = q0 + 32 * w;
+  const int my_q = qw0 + c32;
+  const int qr = min(my_q, n - 1);
+
+  u32x4 qreg[KS], oreg[KS];  // Q^T, dO^T fragments (B operands), in AGPRs
+  {
+    const size_t r = (size_t)qr * qsr + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      gload_agpr(qreg[ks], Qg + r + 16 * ks);
+      gload_agpr(oreg[ks], dOg + r + 16 * ks);
+    }
+  }
+  const float l = a.lse[at.l + qr];
+  const float Lq = (l == -INFINITY || my_q >= n) ? INFINITY : l * kLog2e;
+  const float Dq = a.dvec[at.l + qr];
+  vm_wait<0>();
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = 0.0f;
+  const float cs = a.c;
+  KD kd;
+  VD vd;
+  kd.init(w, lane);
+  vd.init(w, lane);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+  const lchar* krows = lds_opaque(lds_ptr(smem) + KL::row_base(c32, g));
+  const lchar* vrows = lds_opaque(lds_ptr(smem) + KD::kSlot + VL::row_base(c32, g));
+  const lchar* kcols = lds_opaque(lds_ptr(smem) + KL::tr_base(lane));
+  const int n_tiles = (n + BC - 1) / BC;
+  const int j_end = CAUSAL ? min(n_tiles, (min(q0 + kDqDropRows, n) - 1) / BC + 1) : n_tiles;
+
+  for (int j = 0; j < j_end; ++j) {
+    __syncthreads();  // every wave is done with the previous tile
+    {
+      const uint16_t* kt = Kg + (size_t)j * BC * ksr;
+      const uint16_t* vt = Vg + (size_t)j * BC * ksr;
+      const int last = n - 1 - j * BC;
+#pragma unroll
+      for (int k = 0; k < KD::kPer; ++k) kd.issue_at(k, kt, last, 2 * ksr, lds_base + 1024 * w);
+#pragma unroll
+      for (int k = 0; k < VD::kPer; ++k) vd.issue_at(k, vt, last, 2 * ksr, lds_base + KD::kSlot + 1024 * w);
+    }
+    vm_wait<0>();
+    __syncthreads();
+    if (CAUSAL && j * BC > qw0 + 31) continue;  // every key of the tile is after this wave's queries
+
+    f32x16 sv[1], dv[1];  // S^T, dP'^T
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 fk = ld_row(krows + KL::row_off(0, ks));
+      const u32x4 fv = ld_row(vrows + VL::row_off(0, ks));
+      if (ks == 0) {
+        mfma32_vd<Tag, true, true>(sv[0], fk, qreg[ks]);
+        mfma32_vd<Tag, true, true>(dv[0], fv, oreg[ks]);
+      } else {
+        mfma32_vd<Tag, false, true>(sv[0], fk, qreg[ks]);
+        mfma32_vd<Tag, false, true>(dv[0], fv, oreg[ks]);
+      }
+    }
+    // dropout bytes of this lane's query row (drawn and exchanged as in
+    // the forward)
+    const u32x4 ctr = {(uint32_t)my_q >> 2, (uint32_t)(8 * j + g + 2 * (c32 & 3)), (uint32_t)hcan, a.drop.offset};
+    const u32x4 kb = quad_transpose4(philox4x32_10(ctr, a.drop.k0, a.drop.k1), lane);
+    vgpr_drain(sv);
+    vgpr_drain(dv);
+    // element v holds key j*BC + 4g + 8(v/4) + v%4
+    const int lim = (CAUSAL ? min(n - 1, my_q) : n - 1) - j * BC - 4 * g;
+    f32x16 ds;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool dead = 8 * (v >> 2) + (v & 3) > lim;
+      const float p = dead ? 0.0f : fast_exp2(fmaf(sv[0][v], cs, -Lq));
+      const float zs = masked(a.drop.scale, keep_mask(kb, v, a.drop.thr));
+      ds[v] = p * fmaf(dv[0][v], zs, -Dq);
+    }
+    u32x4 db[PK];
+#pragma unroll
+    for (int kk = 0; kk < PK; ++kk) db[kk] = pack8<Tag>(ds, 8 * kk);
+    valu_to_mfma(db);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const u32x4 kt = ld_tr(kcols + KL::tr_off(0, f / MB, 0, f % MB), kcols + KL::tr_off(0, f / MB, 1, f % MB));
+      mfma32_acc<Tag>(acc[f % MB], kt, db[f / MB]);
+    }
+  }
+
+  agpr_drain(acc);
+  if (my_q < n) {
+    uint16_t* dqp = reinterpret_cast<uint16_t*>(a.dq) + at.q + (size_t)my_q * qsr;
+    const float sc = a.scale;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 pk;
+        pk[0] = pack2<Tag>(acc[mb][4 * r] * sc, acc[mb][4 * r + 1] * sc);
+        pk[1] = pack2<Tag>(acc[mb][4 * r + 2] * sc, acc[mb][4 * r + 3] * sc);
+        *reinterpret_cast<u32x2*>(dqp + 32 * mb + 8 * r + 4 * g) = pk;
+      }
+  }
+}
+
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool DROP = false>
 hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
   constexpr int rows_per_blk = kNT / (D / 8);
   const int blocks_per_head = (a.n + rows_per_blk - 1) / rows_per_blk;
@@ -970,10 +1150,10 @@ hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   timing_end(kBwdPre, st);
   if (e != hipSuccess) return e;
-  timing_begin(kBwdDkDv, st);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3(a.nblk_kv), dim3(kNT), 0, st, a);
+  timing_begin(DROP ? kBwdDkDvDrop : kBwdDkDv, st);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE, DROP>), dim3(a.nblk_kv), dim3(kNT), 0, st, a);
   e = hipGetLastError();
-  timing_end(kBwdDkDv, st);
+  timing_end(DROP ? kBwdDkDvDrop : kBwdDkDv, st);
   if (e != hipSuccess) return e;
   if (a.hsplit > 1) {
     const long n4 = (long)a.nbhkv * a.n * (D / 4);
@@ -984,10 +1164,19 @@ hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
     timing_end(kBwdDkDvReduce, st);
     if (e != hipSuccess) return e;
   }
-  timing_begin(kBwdDq, st);
-  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3(a.nblk_q), dim3(kNT), 0, st, a);
-  e = hipGetLastError();
-  timing_end(kBwdDq, st);
+  if constexpr (DROP) {
+    BwdArgs b = a;
+    b.nblk_q = (a.n + kDqDropRows - 1) / kDqDropRows * bh;
+    timing_begin(kBwdDqDrop, st);
+    hipLaunchKernelGGL((bwd_dq_drop_kernel<Tag, D, CAUSAL>), dim3(b.nblk_q), dim3(kNT), 0, st, b);
+    e = hipGetLastError();
+    timing_end(kBwdDqDrop, st);
+  } else {
+    timing_begin(kBwdDq, st);
+    hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3(a.nblk_q), dim3(kNT), 0, st, a);
+    e = hipGetLastError();
+    timing_end(kBwdDq, st);
+  }
   return e;
 }
 
@@ -1001,11 +1190,27 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const BwdArgs& a, hipStrea
 
 }  // namespace
 
-hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st) {
+template <typename Tag, int D>
+hipError_t launch_drop_d(bool causal, int bh, const BwdArgs& a, hipStream_t st) {
+  return causal ? launch_all<Tag, D, true, false, true>(bh, a, st) : launch_all<Tag, D, false, false, true>(bh, a, st);
+}
+
+static void grid_sizes(bool causal, int bh, BwdArgs& a) {
   a.nqb = (a.n + kDqRows - 1) / kDqRows;
   a.nblk_q = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   a.nkb = (a.n + 127) / 128;
   a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.sq.grp) * a.hsplit;  // per K/V head and range
+}
+
+hipError_t launch_bwd_dropout(Dt dt, int d, bool causal, int bh, BwdArgs a, hipStream_t st) {
+  grid_sizes(causal, bh, a);
+  if (dt == Dt::BF16) return d == 64 ? launch_drop_d<bf16_tag, 64>(causal, bh, a, st)
+                                     : launch_drop_d<bf16_tag, 128>(causal, bh, a, st);
+  return d == 64 ? launch_drop_d<f16_tag, 64>(causal, bh, a, st) : launch_drop_d<f16_tag, 128>(causal, bh, a, st);
+}
+
+hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st) {
+  grid_sizes(causal, bh, a);
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)

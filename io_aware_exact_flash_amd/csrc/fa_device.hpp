@@ -176,6 +176,10 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
   return r;
 }
 
+// pack8 with dropout: elements whose keep bit is clear become 0.
+template <typename Tag>
+__device__ __forceinline__ u32x4 pack8_keep(const f32x16& x, int base, const u32x4& kb, uint32_t thr);
+
 // Value held by lane (l % 32) combined with the value of lane (l % 32) + 32:
 // v_permlane32_swap returns, in every lane, the lower-half and upper-half
 // copies of the same column.
@@ -258,6 +262,94 @@ __device__ __forceinline__ float quad_bcast(float x, int i) {
     default: r = __builtin_amdgcn_mov_dpp(bits, 0xff, 0xf, 0xf, true); break;
   }
   return __builtin_bit_cast(float, r);
+}
+
+// ------------------------------------------------------------ dropout bits
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+// Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten
+// rounds of two 32x32->64-bit multiplies by fixed constants, the high
+// halves xor-ed into the other counter words together with the key, which
+// is bumped by two Weyl constants between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+  // the multipliers in vector registers too (no scalar registers taken)
+  uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
+  asm volatile("" : "+v"(m0), "+v"(m1));
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    // high and low halves by separate multiplies (the fused 64-bit
+    // multiply-add also writes a scalar carry register pair)
+    u32x4 n;
+    n[0] = __umulhi(m1, c[2]) ^ c[1] ^ k0;
+    n[1] = m1 * c[2];
+    n[2] = __umulhi(m0, c[0]) ^ c[3] ^ k1;
+    n[3] = m0 * c[0];
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+    // keep the key schedule in two vector registers (bumped each round)
+    // instead of twenty hoisted scalar constants
+    asm volatile("" : "+v"(k0), "+v"(k1));
+  }
+  return c;
+}
+
+// 4x4 transpose of dwords across the four lanes of a quad: word c of lane
+// a moves to word a of lane c.  Two exchange stages: words whose index
+// differs from the lane in bit 1 swap with lane ^ 2 (word ^ 2), then those
+// differing in bit 0 with lane ^ 1 (word ^ 1).
+__device__ __forceinline__ u32x4 quad_transpose4(u32x4 w, int lane) {
+  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+  u32x4 t, r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = (uint32_t)__builtin_amdgcn_mov_dpp((int)w[c ^ 2], 0x4e, 0xf, 0xf, true);  // lane ^ 2
+    t[c] = (((c >> 1) & 1) != (int)b1) ? x : w[c];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[c ^ 1], 0xb1, 0xf, 0xf, true);  // lane ^ 1
+    r[c] = ((c & 1) != (int)b0) ? x : t[c];
+  }
+  return r;
+}
+
+// 4x4 transpose of bytes within a lane: byte c of word b moves to byte b
+// of word c.
+__device__ __forceinline__ u32x4 byte_transpose4(u32x4 w) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    r[c] = ((w[0] >> (8 * c)) & 0xffu) | (((w[1] >> (8 * c)) & 0xffu) << 8) |
+           (((w[2] >> (8 * c)) & 0xffu) << 16) | (((w[3] >> (8 * c)) & 0xffu) << 24);
+  return r;
+}
+
+// Keep decision of element v (0..15) of a lane whose dropout bytes are kb:
+// byte v % 4 of word v / 4 at or above the drop threshold.
+__device__ __forceinline__ bool keep_bit(const u32x4& kb, int v, uint32_t thr) {
+  return ((kb[v >> 2] >> (8 * (v & 3))) & 0xffu) >= thr;
+}
+// The same decision as a bit mask (all ones: keep), formed with vector
+// integer operations only, so no scalar condition registers are taken.
+__device__ __forceinline__ uint32_t keep_mask(const u32x4& kb, int v, uint32_t thr) {
+  const int byte = (int)((kb[v >> 2] >> (8 * (v & 3))) & 0xffu);
+  return ~(uint32_t)((byte - (int)thr) >> 31);
+}
+__device__ __forceinline__ float masked(float x, uint32_t m) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & m);
+}
+
+template <typename Tag>
+__device__ __forceinline__ u32x4 pack8_keep(const f32x16& x, int base, const u32x4& kb, uint32_t thr) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = keep_bit(kb, base + i, thr) ? x[base + i] : 0.0f;
+  u32x4 r;
+  r[0] = pack2<Tag>(y[0], y[1]);
+  r[1] = pack2<Tag>(y[2], y[3]);
+  r[2] = pack2<Tag>(y[4], y[5]);
+  r[3] = pack2<Tag>(y[6], y[7]);
+  return r;
 }
 
 // 32-bit LDS pointers.  lds_opaque() hides a per-iteration base from the

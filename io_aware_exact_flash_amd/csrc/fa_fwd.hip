@@ -54,7 +54,7 @@ constexpr float kLazy = 8.0f;
 // rng-th of a.nsplit contiguous chunks of the row block's key tiles and
 // writes its partial output (normalised by its own row sums) and partial
 // log-sum-exp to a.po / a.plse; fwd_merge_kernel combines the ranges.
-template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT = false, bool DROP = false>
 __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = 32;              // keys per tile
   constexpr int KS = D / 16;          // k-steps of the S^T products
@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   const int bh = (lb / nsp) / per;
   const int pb_ = (lb / nsp) % per;
   const HeadAt at = query_head(a.sq, bh, a.n);
+  const int hcan = DROP ? canon_head(a.sq, bh) : 0;  // head index of the dropout counter
   const int n = at.n;           // this head's length
   const int qsr = a.sq.qsr;     // row strides (elements)
   const int ksr = a.sq.ksr;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
     f32x16 s[2][2];
     // packed P^T (B operands of the PV products) for two tiles
     u32x4 pb[2][2][PK];
-    constexpr int kPD = 6;  // LDS fragments run kPD products ahead
+    constexpr int kPD = DROP ? 4 : 6;  // LDS fragments run kPD products ahead (registers permitting)
     u32x4 fr[kPD + 1];      // K row fragments (ring)
     u32x4 kq[kPD + 1];      // V^T fragments (ring)
     auto rd_k = [&](const lchar* rows, int ks) { return ld_row(rows + KL::row_off(0, ks)); };
@@ -318,6 +319,19 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       constexpr bool MASK = decltype(mask_c)::value;
       int lim[2];
       if constexpr (MASK) limits(j, lim);
+      // dropout bytes of tile j: the quad's four lanes (rows 4m .. 4m+3)
+      // draw the four 4x4 blocks of keys 8a + 4g .. 8a + 4g + 3 (a = lane % 4)
+      // and exchange words, so each lane ends with its own row's 16 bytes
+      // in element order
+      u32x4 kb[2];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 ctr = {(uint32_t)(qw0 + 32 * h + c32) >> 2, (uint32_t)(8 * j + g + 2 * (c32 & 3)),
+                             (uint32_t)hcan, a.drop.offset};
+          kb[h] = quad_transpose4(philox4x32_10(ctr, a.drop.k0, a.drop.k1), lane);
+        }
+      }
       // ---- A
       // Per element of tile j: mask and running maximum in the first half of
       // the products (so the refresh test is known early), t = S c - m
@@ -398,7 +412,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
         l_part[h][v & 1] += s[X][h][v];
         asm volatile("" : "+v"(l_part[h][v & 1]));
         if ((v & 7) == 7) {
-          pb[X][h][v >> 3] = pack8<Tag>(s[X][h], v & 8);
+          if constexpr (DROP) pb[X][h][v >> 3] = pack8_keep<Tag>(s[X][h], v & 8, kb[h], a.drop.thr);
+          else pb[X][h][v >> 3] = pack8<Tag>(s[X][h], v & 8);
           asm volatile("" : "+v"(pb[X][h][v >> 3]));
         }
       };
@@ -473,7 +488,8 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float l = half_sum(l_part[h][0] + l_part[h][1]);
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      if constexpr (DROP) inv *= a.drop.scale;  // kept probabilities scaled by 1 / (1 - p)
       const int my_q = qw0 + 32 * h + c32;
       if (my_q < n && SPLIT) {
         const size_t row = ((size_t)rng * a.nbh + bh) * a.n + my_q;
@@ -570,6 +586,16 @@ hipError_t launch_split_d(bool causal, const FwdArgs& a, hipStream_t st) {
 }
 
 template <typename Tag, int D>
+hipError_t launch_drop_d(bool causal, const FwdArgs& a, hipStream_t st) {
+  timing_begin(kFwdDrop, st);
+  if (causal) hipLaunchKernelGGL((fwd_kernel<Tag, D, true, false, false, true>), dim3(a.nblk), dim3(kNT), 0, st, a);
+  else hipLaunchKernelGGL((fwd_kernel<Tag, D, false, false, false, true>), dim3(a.nblk), dim3(kNT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  timing_end(kFwdDrop, st);
+  return e;
+}
+
+template <typename Tag, int D>
 hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStream_t st) {
   dim3 grid(a.nblk), block(kNT);
   timing_begin(kFwd, st);
@@ -591,6 +617,14 @@ hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a,
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)
                  : launch_d<f16_tag, 128>(causal, sparse, bh, a, st);
+}
+
+hipError_t launch_fwd_dropout(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
+  a.nqb = (a.n + kBR - 1) / kBR;
+  a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
+  if (dt == Dt::BF16) return d == 64 ? launch_drop_d<bf16_tag, 64>(causal, a, st)
+                                     : launch_drop_d<bf16_tag, 128>(causal, a, st);
+  return d == 64 ? launch_drop_d<f16_tag, 64>(causal, a, st) : launch_drop_d<f16_tag, 128>(causal, a, st);
 }
 
 hipError_t launch_fwd_split(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {

@@ -75,6 +75,12 @@ __device__ __forceinline__ HeadAt query_head(const Seqs& s, int bh, int n_max) {
   split_bh(s, bh, s.hq, b, h);
   return head_at(s, b, h, n_max);
 }
+// b*H + h of query head bh (the head index of the dropout counter).
+__device__ __forceinline__ int canon_head(const Seqs& s, int bh) {
+  int b, h;
+  split_bh(s, bh, s.hq, b, h);
+  return b * s.hq + h;
+}
 // The first query head of K/V head bh (over B x Hkv, hkv per batch).
 __device__ __forceinline__ HeadAt group_head(const Seqs& s, int bh, int hkv, int n_max) {
   int b, hk;
@@ -101,6 +107,18 @@ __device__ __forceinline__ HeadAt head_at(const Seqs& s, int b, int h, int n_max
   return r;
 }
 
+// Dropout of the attention probabilities: element (query i, key j) of
+// query head bh (b*H + h) is kept iff byte j%4 of word i%4 of
+// Philox4x32-10(counter (i/4, j/4, bh, offset), key (k0, k1)) is at least
+// thr (drop probability thr/256); kept probabilities are scaled by
+// scale = 256 / (256 - thr).
+struct Drop {
+  uint32_t k0, k1;       // seed, low and high words
+  uint32_t offset;
+  uint32_t thr;          // 0 .. 255
+  float scale;
+};
+
 // Forward: heads of up to N rows (N = the longest sequence when packed).
 struct FwdArgs {
   const void* q;
@@ -115,6 +133,7 @@ struct FwdArgs {
   int nblk;              // total workgroups
   float c;               // scale * log2(e)
   Seqs sq;               // layout of the tensors and of lse
+  Drop drop;             // dropout kernels only
   // split-KV forward only (dense layout)
   int nsplit;            // key ranges per query row
   int nbh;               // B*H
@@ -147,6 +166,7 @@ struct BwdArgs {
   // the dK/dV pass runs per K/V head and sums over the grp query heads that
   // share it
   Seqs sq;
+  Drop drop;             // dropout kernels only
   // hsplit > 1: the group's query heads are cut into hsplit ranges swept by
   // separate workgroups, each writing scaled float32 partial dK, dV; a
   // reduction pass sums them into dk, dv
@@ -177,7 +197,7 @@ inline int dkdv_head_splits(long long bhkv, long long n, int grp) {
 // Kernel classes for the optional per-kernel timing hooks.
 enum KernelId : int {
   kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kFwdSplit = 5, kFwdMerge = 6,
-  kBwdDkDvReduce = 7, kNumKernels = 8
+  kBwdDkDvReduce = 7, kFwdDrop = 8, kBwdDkDvDrop = 9, kBwdDqDrop = 10, kNumKernels = 11
 };
 
 // Bracket one launch with events on its stream when timing is enabled
@@ -192,5 +212,8 @@ hipError_t launch_fwd_f32(int d, bool causal, bool sparse, int bh, FwdArgs a, hi
 // followed by the merge into a.o / a.lse.
 hipError_t launch_fwd_split(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st);
+// Dropout variants (dense or packed layouts, no block mask): a.drop set.
+hipError_t launch_fwd_dropout(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
+hipError_t launch_bwd_dropout(Dt dt, int d, bool causal, int bh, BwdArgs a, hipStream_t st);
 
 }  // namespace fa

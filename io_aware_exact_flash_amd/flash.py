@@ -44,13 +44,17 @@ SIGNATURES = {
     "flash_attn_varlen_bwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "flash_attn_varlen_bwd": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P,
                                    _P, _Z, _P]),
+    "flash_attn_fwd_dropout": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _F, ctypes.c_uint64, ctypes.c_uint32,
+                                    _P, _P, _P]),
+    "flash_attn_bwd_dropout": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _F, ctypes.c_uint64,
+                                    ctypes.c_uint32, _P, _P, _P, _P, _Z, _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
     "flash_attn_timing_collect": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), _I]),
     "flash_attn_kernel_name": (ctypes.c_char_p, [_I]),
 }
-KERNELS = 8  # timing classes: fwd, fwd_f32, bwd_pre, bwd_dkdv, bwd_dq, fwd_split, fwd_merge, bwd_dkdv_reduce
+KERNELS = 11  # timing classes (names from flash_attn_kernel_name)
 
 _lib = None
 _lock = threading.Lock()
@@ -309,4 +313,28 @@ def varlen_bwd(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, scale=None, causal
                                        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                                        lse.data_ptr(), _scale(scale, d), int(bool(causal)), dq.data_ptr(),
                                        dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes, _stream(q)))
+    return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False):
+    """(O, LSE) = flash_attn_fwd_dropout(...): dropout on P, decisions from Philox4x32-10(seed, offset)."""
+    B, H, N, d, dt = _shape(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib().flash_attn_fwd_dropout(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), _scale(scale, d),
+                                        int(bool(causal)), float(dropout_p), int(seed), int(offset), o.data_ptr(),
+                                        lse.data_ptr(), _stream(q)))
+    return o, lse
+
+
+def bwd_dropout(q, k, v, o, dout, lse, dropout_p, seed, offset=0, scale=None, causal=False, workspace=None):
+    """(dQ, dK, dV) = flash_attn_bwd_dropout(...) with the forward's dropout_p, seed and offset."""
+    B, H, N, d, dt = _shape(q, k, v, o, dout)
+    _lse_ok(lse, q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws, nbytes = _workspace(q) if workspace is None else (workspace, workspace.numel())
+    _check(lib().flash_attn_bwd_dropout(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        dout.data_ptr(), lse.data_ptr(), _scale(scale, d), int(bool(causal)),
+                                        float(dropout_p), int(seed), int(offset), dq.data_ptr(), dk.data_ptr(),
+                                        dv.data_ptr(), ws.data_ptr(), nbytes, _stream(q)))
     return dq, dk, dv

@@ -11,6 +11,8 @@ Modules
                    materialising S and P in float64 (the parity oracle).
 ``online``         the pages' blocked online-softmax recurrences, written out
                    step by step; used only to pin ``attention`` (Theorem 1).
+``philox``         the Philox4x32-10 counter-based generator (from its
+                   published definition) and the dropout keep decisions.
 
 Every function in ``attention`` is pinned by ``tests/test_oracle.py`` against
 facts the pages or mathematics fix (worked example, closed forms, finite

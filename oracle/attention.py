@@ -248,3 +248,33 @@ def backward_varlen(q, k, v, do, cu, scale, causal=False):
             dk[s:e, g] += gk
             dv[s:e, g] += gv
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- dropout
+# The pages name dropout among the operations fused into the attention
+# kernel (FlashAttention paper summary) without fixing it further; read
+# here as inverted dropout on the probabilities: with keep decisions Z and
+# drop probability p', O = (P o Z) V / (1 - p'), LSE unchanged.  The
+# gradient is the chain rule through the same Z.
+
+def forward_head_dropout(q, k, v, scale, causal, keep, p_drop):
+    """(O, LSE) with the probabilities P o keep / (1 - p_drop)."""
+    S = scores(q, k, scale, causal)
+    P, _, lse = _softmax_rows(S)
+    Pd = P * keep / (1.0 - p_drop)
+    return Pd @ np.asarray(v, dtype=np.float64), lse
+
+
+def backward_head_dropout(q, k, v, do, scale, causal, keep, p_drop):
+    """(dQ, dK, dV) of sum(O o dO) for the dropout forward above."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    P = probs_head(q, k, scale, causal)
+    zs = keep / (1.0 - p_drop)
+    dv = (P * zs).T @ do                      # O = (P zs) V
+    dP = (do @ v.T) * zs                      # gradient reaching P
+    rowdot = (P * dP).sum(axis=1)             # <p, dp> per row, eq. (30)
+    dS = P * (dP - rowdot[:, None])
+    return scale * (dS @ k), scale * (dS.T @ q), dv

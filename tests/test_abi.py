@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
                      "flash_attn_blocksparse_bwd", "flash_attn_bwd_workspace_size",
                      "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_size",
                      "flash_attn_fwd_gqa", "flash_attn_bwd_gqa", "flash_attn_varlen_fwd",
-                     "flash_attn_varlen_bwd", "flash_attn_varlen_bwd_workspace_size"):
+                     "flash_attn_varlen_bwd", "flash_attn_varlen_bwd_workspace_size",
+                     "flash_attn_fwd_dropout", "flash_attn_bwd_dropout"):
         assert required in names
 
 
@@ -275,6 +276,28 @@ def test_varlen_workspace_and_empty():
     # empty batches launch nothing
     assert _vl_fwd(total=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
     assert _vl_fwd(B=0, cu=None, total=0, max_seqlen=0, q=None, k=None, v=None, o=None, lse=None) == flash.FA_OK
+
+
+@pytest.mark.parametrize("p,code", [(-0.1, flash.FA_ERR_INVALID_ARGUMENT), (1.0, flash.FA_ERR_INVALID_ARGUMENT),
+                                    (0.999, flash.FA_ERR_INVALID_ARGUMENT), (float("nan"), flash.FA_ERR_INVALID_ARGUMENT)])
+def test_dropout_validation(p, code):
+    lib = flash.lib()
+    assert lib.flash_attn_fwd_dropout(1, 2, 256, 64, flash.FA_BF16, FAKE, FAKE, FAKE, 0.125, 0, p, 1, 0, FAKE, FAKE,
+                                      None) == code
+    assert lib.flash_attn_last_error().decode().startswith("flash_attn_fwd_dropout:")
+    need = lib.flash_attn_bwd_workspace_size(1, 2, 256, 64, flash.FA_BF16)
+    assert lib.flash_attn_bwd_dropout(1, 2, 256, 64, flash.FA_BF16, *[FAKE] * 6, 0.125, 0, p, 1, 0, *[FAKE] * 3,
+                                      FAKE, need, None) == code
+
+
+def test_dropout_other_checks():
+    lib = flash.lib()
+    assert lib.flash_attn_fwd_dropout(1, 2, 256, 64, flash.FA_F32, FAKE, FAKE, FAKE, 0.125, 0, 0.1, 1, 0, FAKE,
+                                      FAKE, None) == flash.FA_ERR_UNSUPPORTED
+    assert lib.flash_attn_fwd_dropout(1, 2, 256, 96, flash.FA_BF16, FAKE, FAKE, FAKE, 0.125, 0, 0.1, 1, 0, FAKE,
+                                      FAKE, None) == flash.FA_ERR_UNSUPPORTED
+    assert lib.flash_attn_fwd_dropout(0, 2, 256, 64, flash.FA_BF16, None, None, None, 0.125, 0, 0.1, 1, 0, None,
+                                      None, None) == flash.FA_OK
 
 
 def test_python_binding_refuses_cpu_tensors():

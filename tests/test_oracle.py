@@ -541,3 +541,85 @@ def test_varlen_gradients_by_central_differences():
                 X[idx] = old
                 num[idx] = (fp - fm) / (2 * eps)
             assert np.abs(num - G[name]).max() <= 1e-6 * max(1.0, np.abs(G[name]).max()), (name, causal)
+
+
+# ------------------------------------------------------- P11 dropout
+from oracle import philox as PX  # noqa: E402
+
+
+def test_philox_known_answers():
+    """Philox4x32-10 against the published known-answer vectors of the
+    Random123 library (counter, key) -> output."""
+    kat = [
+        ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+        ((0xFFFFFFFF,) * 4, (0xFFFFFFFF, 0xFFFFFFFF), (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+        ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+         (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+    ]
+    for ctr, key, out in kat:
+        assert tuple(int(w) for w in PX.philox4x32(ctr, key)) == out
+
+
+def test_dropout_threshold_and_keep_rate():
+    assert PX.drop_threshold(0.0) == 0 and PX.drop_threshold(0.1) == 26 and PX.drop_threshold(0.5) == 128
+    for bad in (-0.1, 1.0, 0.999):
+        with pytest.raises(ValueError):
+            PX.drop_threshold(bad)
+    assert PX.keep_matrix(64, 64, 0, 1, 0, 0).all()  # t = 0 keeps everything
+    t = PX.drop_threshold(0.3)
+    Z = PX.keep_matrix(512, 512, 3, 1234, 7, t)
+    rate, expect = Z.mean(), 1 - t / 256
+    assert abs(rate - expect) < 5 * math.sqrt(expect * (1 - expect) / Z.size)
+    # another head, offset or seed draws a different stream
+    for other in (PX.keep_matrix(512, 512, 4, 1234, 7, t), PX.keep_matrix(512, 512, 3, 1234, 8, t),
+                  PX.keep_matrix(512, 512, 3, 1235, 7, t)):
+        assert 0.4 < (other == Z).mean() < 0.7
+
+
+def test_dropout_keep_matrix_layout():
+    """Element (i, j) reads byte j % 4 of word i % 4 of the draw for counter
+    (i // 4, j // 4, head, offset)."""
+    seed, head, off, t = (7 << 32) | 99, 5, 3, 100
+    Z = PX.keep_matrix(9, 10, head, seed, off, t)
+    for i in range(9):
+        for j in range(10):
+            words = PX.philox4x32((i // 4, j // 4, head, off), (seed & 0xFFFFFFFF, seed >> 32))
+            assert Z[i, j] == (((int(words[i % 4]) >> (8 * (j % 4))) & 0xFF) >= t)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_zero_rate_is_plain_attention(causal):
+    r = _rng(61)
+    n, d = 37, 8
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    keep = np.ones((n, n), dtype=bool)
+    O, L = A.forward_head_dropout(q, k, v, 0.4, causal, keep, 0.0)
+    O0, L0 = A.forward_head(q, k, v, 0.4, causal)
+    np.testing.assert_array_equal(O, O0)
+    np.testing.assert_array_equal(L, L0)
+    for a, b in zip(A.backward_head_dropout(q, k, v, do, 0.4, causal, keep, 0.0),
+                    A.backward_head(q, k, v, do, 0.4, causal)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_gradients_by_central_differences(causal):
+    """With the keep decisions fixed the dropout forward is smooth; its
+    gradient against central differences of sum(O o dO)."""
+    r = _rng(67 + causal)
+    n, d, s, p = 6, 3, 0.8, 0.25
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    keep = r.random((n, n)) >= p
+    G = dict(zip("qkv", A.backward_head_dropout(q, k, v, do, s, causal, keep, p)))
+    eps = 1e-6
+    for name, X in (("q", q), ("k", k), ("v", v)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            old = X[idx]
+            X[idx] = old + eps
+            fp = float((A.forward_head_dropout(q, k, v, s, causal, keep, p)[0] * do).sum())
+            X[idx] = old - eps
+            fm = float((A.forward_head_dropout(q, k, v, s, causal, keep, p)[0] * do).sum())
+            X[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        assert np.abs(num - G[name]).max() <= 1e-6 * max(1.0, np.abs(G[name]).max()), name

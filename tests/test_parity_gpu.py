@@ -434,3 +434,100 @@ def test_varlen_empty_batches():
         dq, dk, dv = flash.varlen_bwd(q, q, q, o, q, lse, cu, max(lens, default=0))
         torch.cuda.synchronize()
         assert o.shape == q.shape and lse.shape == (2, 0)
+
+
+# ---------------------------------------------------------------- dropout
+from oracle import philox as PX  # noqa: E402
+
+
+def _oracle_dropout(f64, s, causal, p, seed, offset):
+    q, k, v, do = f64
+    B, H, N, _ = q.shape
+    t = PX.drop_threshold(p)
+    pd = t / 256.0
+    O = np.zeros(q.shape)
+    L = np.zeros(q.shape[:3])
+    G = [np.zeros(q.shape) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            keep = PX.keep_matrix(N, N, b * H + h, seed, offset, t)
+            O[b, h], L[b, h] = A.forward_head_dropout(q[b, h], k[b, h], v[b, h], s, causal, keep, pd)
+            g = A.backward_head_dropout(q[b, h], k[b, h], v[b, h], do[b, h], s, causal, keep, pd)
+            for i in range(3):
+                G[i][b, h] = g[i]
+    return O, L, G
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape,p", [((1, 2, 200), 0.1), ((2, 1, 519), 0.5), ((1, 3, 64), 0.2),
+                                     ((1, 1, 1), 0.3), ((1, 2, 300), 0.0)],
+                         ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else str(x))
+def test_dropout_forward_backward(dtype, d, causal, shape, p):
+    """Dropout decisions drawn inside the kernels from Philox4x32-10 equal
+    the oracle's draws (any mismatch moves O by O(1)); the gradient is the
+    exact gradient through the same decisions.  Kept probabilities carry a
+    factor 1/(1-p) <= 2, so O and the gradients get twice the plain bounds."""
+    B, H, N = shape
+    seed, offset = 0x1234_5678_9ABC + N, 17 + d
+    (q, k, v, do), f64 = make(B, H, N, d, dtype, seed=700 + N + d)
+    s = fp32_scale(d)
+    o, lse = flash.fwd_dropout(q, k, v, p, seed, offset, scale=s, causal=causal)
+    dq, dk, dv = flash.bwd_dropout(q, k, v, o, do, lse, p, seed, offset, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    O, L, (gQ, gK, gV) = _oracle_dropout(f64, s, causal, p, seed, offset)
+    tol = TOL[dtype]
+    compare("O", o, O, 2 * tol["o"], REL_RMS[dtype])
+    compare_lse("LSE", lse, L, tol["lse"])
+    # With one key the exact dQ and dK are zero (a one-element softmax has no
+    # gradient); the kernels' D = rowsum(dO o O) reads the stored, rounded O,
+    # which no longer equals dP exactly once O carries the 1/(1-p) factor, so
+    # only the absolute bound is meaningful there.
+    rg = REL_RMS[dtype] if N > 1 else None
+    compare("dQ", dq, gQ, 2 * tol["grad"], rg)
+    compare("dK", dk, gK, 2 * tol["grad"], rg)
+    compare("dV", dv, gV, 2 * tol["grad"], REL_RMS[dtype])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_decisions_read_off_the_output(causal):
+    """With V = the identity (N = d = 64), row i of O is row i of
+    P o Z / (1 - p): its zero pattern is the dropout decisions, compared
+    entry by entry with the oracle's (every allowed P is > 0)."""
+    N, d, p, seed, offset = 64, 64, 0.3, 987654321, 5
+    q, k, _, _ = workloads.qkvdo(2, 3, N, d, "bf16", seed=42)
+    v = torch.eye(N, dtype=torch.bfloat16).expand(2, 3, N, d).contiguous()
+    o, _ = flash.fwd_dropout(q.cuda(), k.cuda(), v.cuda(), p, seed, offset, causal=causal)
+    torch.cuda.synchronize()
+    t = PX.drop_threshold(p)
+    allowed = A.allowed(N, N, causal)
+    for b in range(2):
+        for h in range(3):
+            keep = PX.keep_matrix(N, N, b * 3 + h, seed, offset, t)
+            nz = to64(o[b, h]) != 0
+            assert (nz == (keep & allowed)).all(), (b, h, int((nz != (keep & allowed)).sum()))
+
+
+def test_dropout_zero_rate_matches_plain_calls():
+    """p = 0 keeps every element with factor 1: the forward and dK/dV are
+    bit-identical to the plain calls; dQ (a separate, simpler pass) within
+    the gradient bound."""
+    (q, k, v, do), _ = make(2, 2, 400, 128, "bf16", seed=3)
+    o, lse = flash.fwd(q, k, v, causal=True)
+    dq, dk, dv = flash.bwd(q, k, v, o, do, lse, causal=True)
+    o2, lse2 = flash.fwd_dropout(q, k, v, 0.0, 11, 0, causal=True)
+    dq2, dk2, dv2 = flash.bwd_dropout(q, k, v, o2, do, lse2, 0.0, 11, 0, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    compare("dQ", dq2, to64(dq), TOL["bf16"]["grad"])
+
+
+def test_dropout_seed_and_offset_select_the_stream():
+    (q, k, v, _), _ = make(1, 2, 256, 64, "f16", seed=8)
+    a = flash.fwd_dropout(q, k, v, 0.5, 1, 0)[0]
+    b = flash.fwd_dropout(q, k, v, 0.5, 1, 0)[0]
+    c = flash.fwd_dropout(q, k, v, 0.5, 2, 0)[0]
+    e = flash.fwd_dropout(q, k, v, 0.5, 1, 1)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and not torch.equal(a, c) and not torch.equal(a, e)
