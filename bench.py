@@ -236,6 +236,7 @@ VARIANTS = {
                 dtype="bf16", causal=True, seed=12),
     "mqa": dict(name="multi-query (one K/V head)", B=4, H=32, Hkv=1, N=4096, d=128,
                 dtype="bf16", causal=True, seed=13),
+    "dropout": dict(name="dropout p=0.1", B=4, H=32, N=2048, d=128, dtype="bf16", causal=True, p=0.1, seed=15),
     "varlen": dict(name="packed variable-length batch", B=8, H=16, Hkv=16, max_len=4096, d=128,
                    dtype="bf16", causal=True, seed=14),
 }
@@ -334,6 +335,28 @@ def run_variants(steps, warmup):
                                        for n, t in res.items()}}
     log(f"variant varlen: {out['varlen']}")
     del q, k, vv, do, cu, o, lse, qp, kp, vp, dop, op, lsep, ws, wsv
+
+    v = VARIANTS["dropout"]
+    q, k, vv, do = (t.cuda() for t in workloads.qkvdo(v["B"], v["H"], v["N"], v["d"], v["dtype"], seed=v["seed"]))
+    c, pd = v["causal"], v["p"]
+    f = 4.0 * v["B"] * v["H"] * v["N"] ** 2 * v["d"] * (0.5 if c else 1.0)
+    ws = torch.empty(flash.bwd_workspace_size(v["B"], v["H"], v["N"], v["d"], q.dtype), dtype=torch.uint8,
+                     device=q.device)
+    o, lse = flash.fwd(q, k, vv, causal=c)
+    od, lsed = flash.fwd_dropout(q, k, vv, pd, 1, 0, causal=c)
+    res = {
+        "plain_fwd": (time_ms(lambda: flash.fwd(q, k, vv, causal=c), steps, warmup), f),
+        "dropout_fwd": (time_ms(lambda: flash.fwd_dropout(q, k, vv, pd, 1, 0, causal=c), steps, warmup), f),
+        "plain_bwd": (time_ms(lambda: flash.bwd(q, k, vv, o, do, lse, causal=c, workspace=ws), steps, warmup),
+                      2.5 * f),
+        "dropout_bwd": (time_ms(lambda: flash.bwd_dropout(q, k, vv, od, do, lsed, pd, 1, 0, causal=c, workspace=ws),
+                                steps, warmup), 2.5 * f),
+    }
+    out["dropout"] = {"workload": f"{v['name']}: B={v['B']} H={v['H']} N={v['N']} d={v['d']} {v['dtype']} causal",
+                      "ms": {n: round(t, 4) for n, (t, _) in res.items()},
+                      "tflops": {n: round(fl / (t * 1e-3) / 1e12, 1) for n, (t, fl) in res.items()}}
+    log(f"variant dropout: {out['dropout']}")
+    del q, k, vv, do, ws, o, lse, od, lsed
     torch.cuda.empty_cache()
     return out
 
@@ -349,8 +372,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=10, help="(batch, head) pairs the oracle baseline runs (about 1 s each at N=8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
-                    help="also time the split-KV forward, grouped K/V heads and a packed variable-length "
-                         "batch (adds a 'variants' object)")
+                    help="also time the split-KV forward, grouped K/V heads, a packed variable-length "
+                         "batch and dropout (adds a 'variants' object)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy a device buffer of this many bytes 3 times "
                          "(calibrates the HBM byte counters of a profiling run)")
