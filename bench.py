@@ -73,10 +73,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, bytes per launch)
-    ("fwd", 4): ("be93282b97dd6192", 1887637504),
-    ("bwd_pre", 4): ("e73a793ec9810a43", 692099072),
-    ("bwd_dkdv", 4): ("e73a793ec9810a43", 2121271296),
-    ("bwd_dq", 4): ("e73a793ec9810a43", 2461702144),
+    ("fwd", 4): ("909593a38bbe8c5e", 1892201888),
+    ("bwd_pre", 4): ("9a5ff644f73909ec", 692115712),
+    ("bwd_dkdv", 4): ("9a5ff644f73909ec", 2122240608),
+    ("bwd_dq", 4): ("9a5ff644f73909ec", 2375014112),
 }
 
 
