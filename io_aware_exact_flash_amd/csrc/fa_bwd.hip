@@ -1003,9 +1003,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
 // ------------------------------------------------------------ dQ pass with dropout
 // dS^T = P^T o (dP'^T Z / (1 - p) - D) with dP'^T = V dO^T and Z the
 // dropout decisions (drawn as in the forward: lane = query).  One wave per
-// 32 queries (four per workgroup), K/V tiles of 32 keys moved into LDS one
-// at a time; simpler than the pipelined pass above, whose registers leave
-// no room for the dropout decisions.
+// 32 queries (four per workgroup), K/V tiles of 32 keys in two LDS slots
+// (the next tile's DMA runs while the current one is computed); simpler
+// than the pipelined pass above, whose registers leave no room for the
+// dropout decisions.
 constexpr int kDqDropRows = 128;
 
 template <typename Tag, int D, bool CAUSAL>
@@ -1016,7 +1017,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
   using VL = Pad<D, false>;
   using KD = Dma<BC, D, true, kNT / 64>;
   using VD = Dma<BC, D, false, kNT / 64>;
-  __shared__ __attribute__((aligned(16))) char smem[KD::kSlot + VD::kSlot];
+  constexpr int SLOT = KD::kSlot + VD::kSlot;
+  constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
+  static_assert(C < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem[2 * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1063,65 +1067,74 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
   kd.init(w, lane);
   vd.init(w, lane);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
-  const lchar* krows = lds_opaque(lds_ptr(smem) + KL::row_base(c32, g));
-  const lchar* vrows = lds_opaque(lds_ptr(smem) + KD::kSlot + VL::row_base(c32, g));
-  const lchar* kcols = lds_opaque(lds_ptr(smem) + KL::tr_base(lane));
   const int n_tiles = (n + BC - 1) / BC;
   const int j_end = CAUSAL ? min(n_tiles, (min(q0 + kDqDropRows, n) - 1) / BC + 1) : n_tiles;
+  auto dma = [&](int jt) {  // tile jt into slot jt % 2
+    const uint16_t* kt = Kg + (size_t)jt * BC * ksr;
+    const uint16_t* vt = Vg + (size_t)jt * BC * ksr;
+    const int last = n - 1 - jt * BC;
+    const uint32_t slot = lds_base + (jt & 1) * SLOT + 1024 * w;
+#pragma unroll
+    for (int k = 0; k < KD::kPer; ++k) kd.issue_at(k, kt, last, 2 * ksr, slot);
+#pragma unroll
+    for (int k = 0; k < VD::kPer; ++k) vd.issue_at(k, vt, last, 2 * ksr, slot + KD::kSlot);
+  };
+  dma(0);
 
   for (int j = 0; j < j_end; ++j) {
-    __syncthreads();  // every wave is done with the previous tile
-    {
-      const uint16_t* kt = Kg + (size_t)j * BC * ksr;
-      const uint16_t* vt = Vg + (size_t)j * BC * ksr;
-      const int last = n - 1 - j * BC;
-#pragma unroll
-      for (int k = 0; k < KD::kPer; ++k) kd.issue_at(k, kt, last, 2 * ksr, lds_base + 1024 * w);
-#pragma unroll
-      for (int k = 0; k < VD::kPer; ++k) vd.issue_at(k, vt, last, 2 * ksr, lds_base + KD::kSlot + 1024 * w);
+    if (j + 1 < j_end) {
+      dma(j + 1);      // into the slot every wave left at the end of the previous iteration
+      vm_wait<C>();    // tile j has landed (for this wave's share) ...
+    } else {
+      vm_wait<0>();
     }
-    vm_wait<0>();
-    __syncthreads();
-    if (CAUSAL && j * BC > qw0 + 31) continue;  // every key of the tile is after this wave's queries
+    __syncthreads();   // ... for every wave
+    const int so = (j & 1) * SLOT;
+    const lchar* krows = lds_opaque(lds_ptr(smem) + so + KL::row_base(c32, g));
+    const lchar* vrows = lds_opaque(lds_ptr(smem) + so + KD::kSlot + VL::row_base(c32, g));
+    const lchar* kcols = lds_opaque(lds_ptr(smem) + so + KL::tr_base(lane));
+    if (!(CAUSAL && j * BC > qw0 + 31)) {  // (else every key of the tile is after this wave's queries)
 
-    f32x16 sv[1], dv[1];  // S^T, dP'^T
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 fk = ld_row(krows + KL::row_off(0, ks));
-      const u32x4 fv = ld_row(vrows + VL::row_off(0, ks));
-      if (ks == 0) {
-        mfma32_vd<Tag, true, true>(sv[0], fk, qreg[ks]);
-        mfma32_vd<Tag, true, true>(dv[0], fv, oreg[ks]);
-      } else {
-        mfma32_vd<Tag, false, true>(sv[0], fk, qreg[ks]);
-        mfma32_vd<Tag, false, true>(dv[0], fv, oreg[ks]);
+      f32x16 sv[1], dv[1];  // S^T, dP'^T
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 fk = ld_row(krows + KL::row_off(0, ks));
+        const u32x4 fv = ld_row(vrows + VL::row_off(0, ks));
+        if (ks == 0) {
+          mfma32_vd<Tag, true, true>(sv[0], fk, qreg[ks]);
+          mfma32_vd<Tag, true, true>(dv[0], fv, oreg[ks]);
+        } else {
+          mfma32_vd<Tag, false, true>(sv[0], fk, qreg[ks]);
+          mfma32_vd<Tag, false, true>(dv[0], fv, oreg[ks]);
+        }
+      }
+      // dropout bytes of this lane's query row (drawn and exchanged as in
+      // the forward)
+      const u32x4 ctr = {(uint32_t)my_q >> 2, (uint32_t)(8 * j + g + 2 * (c32 & 3)), (uint32_t)hcan, a.drop.offset};
+      const u32x4 kb = quad_transpose4(philox4x32_10(ctr, a.drop.k0, a.drop.k1), lane);
+      vgpr_drain(sv);
+      vgpr_drain(dv);
+      // element v holds key j*BC + 4g + 8(v/4) + v%4
+      const int lim = (CAUSAL ? min(n - 1, my_q) : n - 1) - j * BC - 4 * g;
+      f32x16 ds;
+  #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool dead = 8 * (v >> 2) + (v & 3) > lim;
+        const float p = dead ? 0.0f : fast_exp2(fmaf(sv[0][v], cs, -Lq));
+        const float zs = masked(a.drop.scale, keep_mask(kb, v, a.drop.thr));
+        ds[v] = p * fmaf(dv[0][v], zs, -Dq);
+      }
+      u32x4 db[PK];
+  #pragma unroll
+      for (int kk = 0; kk < PK; ++kk) db[kk] = pack8<Tag>(ds, 8 * kk);
+      valu_to_mfma(db);
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const u32x4 kt = ld_tr(kcols + KL::tr_off(0, f / MB, 0, f % MB), kcols + KL::tr_off(0, f / MB, 1, f % MB));
+        mfma32_acc<Tag>(acc[f % MB], kt, db[f / MB]);
       }
     }
-    // dropout bytes of this lane's query row (drawn and exchanged as in
-    // the forward)
-    const u32x4 ctr = {(uint32_t)my_q >> 2, (uint32_t)(8 * j + g + 2 * (c32 & 3)), (uint32_t)hcan, a.drop.offset};
-    const u32x4 kb = quad_transpose4(philox4x32_10(ctr, a.drop.k0, a.drop.k1), lane);
-    vgpr_drain(sv);
-    vgpr_drain(dv);
-    // element v holds key j*BC + 4g + 8(v/4) + v%4
-    const int lim = (CAUSAL ? min(n - 1, my_q) : n - 1) - j * BC - 4 * g;
-    f32x16 ds;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool dead = 8 * (v >> 2) + (v & 3) > lim;
-      const float p = dead ? 0.0f : fast_exp2(fmaf(sv[0][v], cs, -Lq));
-      const float zs = masked(a.drop.scale, keep_mask(kb, v, a.drop.thr));
-      ds[v] = p * fmaf(dv[0][v], zs, -Dq);
-    }
-    u32x4 db[PK];
-#pragma unroll
-    for (int kk = 0; kk < PK; ++kk) db[kk] = pack8<Tag>(ds, 8 * kk);
-    valu_to_mfma(db);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const u32x4 kt = ld_tr(kcols + KL::tr_off(0, f / MB, 0, f % MB), kcols + KL::tr_off(0, f / MB, 1, f % MB));
-      mfma32_acc<Tag>(acc[f % MB], kt, db[f / MB]);
-    }
+    __syncthreads();  // every wave is done with slot j % 2 before tile j + 2 goes there
   }
 
   agpr_drain(acc);
