@@ -54,11 +54,20 @@ def kernel_flops(w, mask):
 
 
 def kernel_bytes(w):
-    """Compulsory HBM bytes of the memory-bound pre-pass: read O, dO and LSE,
-    write D and the base-2 LSE."""
+    """Compulsory HBM bytes per launch: what each kernel must read and write
+    at least once (tensor T = B H N d elements, a per-row array = B H N
+    float32).  Forward: Q, K, V read, O written (4T) plus LSE.  Pre-pass: O,
+    dO, LSE read; D and the base-2 LSE written.  dK/dV pass: Q, K, V, dO
+    and the two per-row arrays read, dK and dV written (6T + 2 rows).  dQ
+    pass: Q, K, V, dO, LSE, D read, dQ written (5T + 2 rows).  Only the
+    pre-pass is memory bound; for the others the figure gives the achieved
+    HBM rate the compulsory traffic implies."""
     el = {"bf16": 2, "f16": 2, "f32": 4}[w["dtype"]]
     rows = w["B"] * w["H"] * w["N"]
-    return {"bwd_pre": rows * (2 * w["d"] * el + 12)}
+    t = rows * w["d"] * el
+    fwd = 4 * t + 4 * rows
+    return {"fwd": fwd, "fwd_f32": fwd, "bwd_pre": rows * (2 * w["d"] * el + 12),
+            "bwd_dkdv": 6 * t + 8 * rows, "bwd_dq": 5 * t + 8 * rows}
 
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
@@ -178,6 +187,7 @@ def run_workload(num, steps, warmup, quiet=False):
     kt = flash.timing_collect()
 
     ms_step = (t1 - t0) * 1e3 / steps
+    per_step = sorted(starts[i].elapsed_time(ends[i]) for i in range(steps))
     fwd_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(steps)) / steps
     bwd_ms = sum(mids[i].elapsed_time(ends[i]) for i in range(steps)) / steps
     ff, fb = flop_counts(w, mask)
@@ -212,6 +222,7 @@ def run_workload(num, steps, warmup, quiet=False):
         "fwd_tflops": ff / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": (fb / (bwd_ms * 1e-3) / 1e12) if fb else None,
         "peak": peak, "kernels": kernels, "roofline": roof,
+        "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
         "density": None if mask is None else float(mask.float().mean()),
     }
     res["fwd_frac_of_peak"] = res["fwd_tflops"] / peak
@@ -418,6 +429,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_per_step"], 4),
+        "step_ms_median": round(r["step_ms_median"], 4),   # HIP events around each step
+        "step_ms_min": round(r["step_ms_min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
