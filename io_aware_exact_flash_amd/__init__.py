@@ -11,10 +11,21 @@ from .flash import (  # noqa: F401
     blocksparse_bwd,
     blocksparse_fwd,
     bwd,
+    bwd_dropout,
+    bwd_gqa,
+    bwd_gqa_workspace_size,
     bwd_workspace_size,
     fwd,
+    fwd_dropout,
+    fwd_gqa,
+    fwd_splitkv,
+    fwd_splitkv_workspace_size,
     lib,
+    varlen_bwd,
+    varlen_bwd_workspace_size,
+    varlen_fwd,
 )
 
-__all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "lib",
-           "FlashAttnError"]
+__all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "fwd_splitkv",
+           "fwd_splitkv_workspace_size", "fwd_gqa", "bwd_gqa", "bwd_gqa_workspace_size", "varlen_fwd",
+           "varlen_bwd", "varlen_bwd_workspace_size", "fwd_dropout", "bwd_dropout", "lib", "FlashAttnError"]
