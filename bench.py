@@ -82,10 +82,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, bytes per launch)
-    ("fwd", 4): ("909593a38bbe8c5e", 1892201888),
-    ("bwd_pre", 4): ("9a5ff644f73909ec", 692115712),
-    ("bwd_dkdv", 4): ("9a5ff644f73909ec", 2122240608),
-    ("bwd_dq", 4): ("9a5ff644f73909ec", 2375014112),
+    ("fwd", 4): ("909593a38bbe8c5e", 1883307031),
+    ("bwd_pre", 4): ("e90f174dd2834aa4", 692098969),
+    ("bwd_dkdv", 4): ("e90f174dd2834aa4", 2122018799),
+    ("bwd_dq", 4): ("e90f174dd2834aa4", 2366753207),
 }
 
 
