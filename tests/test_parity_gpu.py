@@ -531,3 +531,36 @@ def test_dropout_seed_and_offset_select_the_stream():
     e = flash.fwd_dropout(q, k, v, 0.5, 1, 1)[0]
     torch.cuda.synchronize()
     assert torch.equal(a, b) and not torch.equal(a, c) and not torch.equal(a, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_very_long_sequence_sampled_rows(d):
+    """One head of 2^17 + 37 tokens (ragged tail, row offsets past 2^24
+    elements): O, LSE and dQ of sampled rows against the oracle row by row
+    (each depends only on its own scores), dK/dV against the softmax
+    Jacobian's column identities (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i)."""
+    N = (1 << 17) + 37
+    (q, k, v, do), _ = make(1, 1, N, d, "bf16", seed=123 + d, gain=0.5)
+    s = fp32_scale(d)
+    o, lse = flash.fwd(q, k, v, scale=s, causal=True)
+    dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=True)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t).all()
+    qc, kc, vc, doc = (t[0, 0].to(torch.float64).cpu().numpy() for t in (q, k, v, do))
+    rows = np.array([0, 1, 31, 32, 4095, 65536, N - 38, N - 2, N - 1])
+    O, L = A.forward_head(qc, kc, vc, s, True, rows=rows)
+    tol = TOL["bf16"]
+    compare("O rows", to64(o[0, 0])[rows], O, tol["o"])
+    compare_lse("LSE rows", to64(lse[0, 0])[rows], L, tol["lse"])
+    gq = A.grad_q_rows(qc, kc, vc, doc, s, True, rows=rows)
+    compare("dQ rows", to64(dq[0, 0])[rows], gq, tol["grad"])
+    sum_dk = dk[0, 0].double().sum(0).cpu().numpy()
+    sum_dv = dv[0, 0].double().sum(0).cpu().numpy()
+    sum_do = do[0, 0].double().sum(0).cpu().numpy()
+    rms_k = float(dk.double().pow(2).mean().sqrt())
+    rms_v = float(dv.double().pow(2).mean().sqrt())
+    # each column sum adds N values rounded to bf16 (relative 2^-9): the
+    # residual grows like sqrt(N) times their size
+    assert np.abs(sum_dk).max() <= 4 * np.sqrt(N) * rms_k * 2.0 ** -8
+    assert np.abs(sum_dv - sum_do).max() <= 4 * np.sqrt(N) * rms_v * 2.0 ** -8 + 1e-3 * np.abs(sum_do).max()
