@@ -575,9 +575,11 @@ __device__ __forceinline__ void wait_ahead(int ahead) {  // ahead: tiles issued 
 // work of the current one.  K/V tiles stream through a ring of four LDS
 // slots; DMA runs two tiles ahead, one barrier per iteration makes the next
 // tile visible and frees the slot refilled in the same iteration.
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BR = kDqRows;         // queries per workgroup (4 waves x 64)
+// NW: waves per workgroup.  Block-sparse runs at d = 64 use two, so that a
+// workgroup covers exactly one 128-row mask row (see fwd_kernel).
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, int NW = 4>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BR = NW * 64;         // queries per workgroup (NW waves x 64)
   constexpr int BC = 32;              // keys per tile
   constexpr int KS = D / 16;          // k-steps of the S/dP products
   constexpr int MB = D / 32;          // 32-row blocks of dQ^T
@@ -586,12 +588,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int kRing = 6;            // LDS tile slots
   using KL = Pad<D, true>;            // K: row reads (S^T) and transpose reads (dQ^T)
   using VL = Pad<D, false>;           // V: row reads (dP^T)
-  using KD = Dma<BC, D, true, kNT / 64>;
-  using VD = Dma<BC, D, false, kNT / 64>;
+  using KD = Dma<BC, D, true, NW>;
+  using VD = Dma<BC, D, false, NW>;
   constexpr int SLOT = KD::kSlot + VD::kSlot;
   constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
   static_assert(4 * C < 64, "vmcnt range");
-  static_assert(C <= NF, "DMA issue slots");
+  static_assert(C / 2 <= NF - 1 && C - C / 2 <= 4 * KS - 2, "DMA issue slots");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
   const int tid = threadIdx.x;
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_kernel(BwdArgs a) {
     const uint8_t* mwave = nullptr;
     if constexpr (SPARSE) {
       const int t0 = q0 / kMaskBlock;
-      const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
+      const int t1 = min((q0 + BR - 1) / kMaskBlock, (n - 1) / kMaskBlock);
       mrow0 = a.mask + (size_t)t0 * a.mask_t;
       mrow1 = a.mask + (size_t)t1 * a.mask_t;
       mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
@@ -1153,6 +1155,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
   }
 }
 
+// Waves per dQ workgroup (two for block-sparse runs at d = 64).
+template <int D, bool SPARSE>
+constexpr int dq_waves() { return (SPARSE && D == 64) ? 2 : 4; }
+
 template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool DROP = false>
 hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
   constexpr int rows_per_blk = kNT / (D / 8);
@@ -1185,8 +1191,9 @@ hipError_t launch_all(int bh, const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     timing_end(kBwdDqDrop, st);
   } else {
+    constexpr int NWQ = dq_waves<D, SPARSE>();
     timing_begin(kBwdDq, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3(a.nblk_q), dim3(kNT), 0, st, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, SPARSE, NWQ>), dim3(a.nblk_q), dim3(64 * NWQ), 0, st, a);
     e = hipGetLastError();
     timing_end(kBwdDq, st);
   }
@@ -1208,22 +1215,23 @@ hipError_t launch_drop_d(bool causal, int bh, const BwdArgs& a, hipStream_t st) 
   return causal ? launch_all<Tag, D, true, false, true>(bh, a, st) : launch_all<Tag, D, false, false, true>(bh, a, st);
 }
 
-static void grid_sizes(bool causal, int bh, BwdArgs& a) {
-  a.nqb = (a.n + kDqRows - 1) / kDqRows;
+static void grid_sizes(bool causal, bool sparse, int d, int bh, BwdArgs& a) {
+  const int rows = (sparse && d == 64) ? 64 * dq_waves<64, true>() : kDqRows;
+  a.nqb = (a.n + rows - 1) / rows;
   a.nblk_q = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   a.nkb = (a.n + 127) / 128;
   a.nblk_kv = (causal ? (a.nkb + 1) / 2 : a.nkb) * (bh / a.sq.grp) * a.hsplit;  // per K/V head and range
 }
 
 hipError_t launch_bwd_dropout(Dt dt, int d, bool causal, int bh, BwdArgs a, hipStream_t st) {
-  grid_sizes(causal, bh, a);
+  grid_sizes(causal, false, d, bh, a);
   if (dt == Dt::BF16) return d == 64 ? launch_drop_d<bf16_tag, 64>(causal, bh, a, st)
                                      : launch_drop_d<bf16_tag, 128>(causal, bh, a, st);
   return d == 64 ? launch_drop_d<f16_tag, 64>(causal, bh, a, st) : launch_drop_d<f16_tag, 128>(causal, bh, a, st);
 }
 
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a, hipStream_t st) {
-  grid_sizes(causal, bh, a);
+  grid_sizes(causal, sparse, d, bh, a);
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
   return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)

@@ -54,8 +54,13 @@ constexpr float kLazy = 8.0f;
 // rng-th of a.nsplit contiguous chunks of the row block's key tiles and
 // writes its partial output (normalised by its own row sums) and partial
 // log-sum-exp to a.po / a.plse; fwd_merge_kernel combines the ranges.
-template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT = false, bool DROP = false>
-__global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
+// NW: waves per workgroup (rows per workgroup 64 NW).  Block-sparse runs at
+// d = 64 use two: a workgroup then covers exactly one 128-row mask row, so
+// it loads only that row's kept key tiles (with four waves it spans two mask
+// rows and must sweep the union of their kept tiles), and two workgroups
+// share a compute unit.
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT = false, bool DROP = false, int NW = 4>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = 32;              // keys per tile
   constexpr int KS = D / 16;          // k-steps of the S^T products
   constexpr int MB = D / 32;          // 32-row blocks of O^T
@@ -64,12 +69,13 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   constexpr int kRing = 6;            // LDS tile slots
   using KL = Pad<D, false>;           // K: row reads
   using VL = Pad<D, true>;            // V: transpose reads
-  using KD = Dma<BC, D, false, kNT / 64>;
-  using VD = Dma<BC, D, true, kNT / 64>;
+  constexpr int BRW = NW * kWQ;       // query rows per workgroup
+  using KD = Dma<BC, D, false, NW>;
+  using VD = Dma<BC, D, true, NW>;
   constexpr int SLOT = KD::kSlot + VD::kSlot;
   constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
   static_assert(4 * C < 64, "vmcnt range");
-  static_assert(C <= NF, "DMA issue slots");
+  static_assert(C / 2 <= NF - 1 && C - C / 2 <= 2 * KS - 2, "DMA issue slots");
   static_assert(2 * KS == 2 * NF, "both phases hold the same number of products");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
   float* __restrict__ Lg = a.lse + at.l;
 
   auto run = [&](const int qb) {
-    const int q0 = qb * kBR;
+    const int q0 = qb * BRW;
     const int qw0 = q0 + w * kWQ;       // the wave's first query; block h starts at qw0 + 32h
 
     u32x4 qreg[2][KS];                  // Q^T fragments, in AGPRs
@@ -112,20 +118,21 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
 
     const int n_tiles = (n + BC - 1) / BC;
     int j_end = n_tiles;
-    if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + kBR, n) - 1) / BC + 1);
+    if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + BRW, n) - 1) / BC + 1);
     int j_lo = 0;
     if constexpr (SPLIT) {  // this workgroup's chunk of the key tiles
       const int chunk = (j_end + nsp - 1) / nsp;
       j_lo = min(rng * chunk, j_end);
       j_end = min(j_lo + chunk, j_end);
     }
-    // block-sparse: the workgroup spans two 128-query mask rows, each wave one
+    // block-sparse: the workgroup spans one or two 128-query mask rows, each
+    // wave lies in one of them
     const uint8_t* mrow0 = nullptr;
     const uint8_t* mrow1 = nullptr;
     const uint8_t* mwave = nullptr;
     if constexpr (SPARSE) {
       const int t0 = q0 / kMaskBlock;
-      const int t1 = min(t0 + 1, (n - 1) / kMaskBlock);
+      const int t1 = min((q0 + BRW - 1) / kMaskBlock, (n - 1) / kMaskBlock);
       mrow0 = a.mask + (size_t)t0 * a.mask_t;
       mrow1 = a.mask + (size_t)t1 * a.mask_t;
       mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(kNT, 1) void fwd_kernel(FwdArgs a) {
       }
     }
   };
-  const int nqb = (n + kBR - 1) / kBR;  // this head's query blocks
+  const int nqb = (n + BRW - 1) / BRW;  // this head's query blocks
   const int qa = nqb - 1 - pb_;         // the longer block first
   // blocks qa and pb_ (paired causal), or qa alone; none past the end of a
   // shorter sequence
@@ -595,13 +602,20 @@ hipError_t launch_drop_d(bool causal, const FwdArgs& a, hipStream_t st) {
   return e;
 }
 
+// Waves per workgroup of the block-sparse forward (see fwd_kernel).
+template <int D>
+constexpr int sparse_waves() { return D == 64 ? 2 : 4; }
+
 template <typename Tag, int D>
 hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStream_t st) {
   dim3 grid(a.nblk), block(kNT);
+  constexpr int SW = sparse_waves<D>();
   timing_begin(kFwd, st);
-  if (causal && sparse) hipLaunchKernelGGL((fwd_kernel<Tag, D, true, true>), grid, block, 0, st, a);
+  if (causal && sparse)
+    hipLaunchKernelGGL((fwd_kernel<Tag, D, true, true, false, false, SW>), grid, dim3(64 * SW), 0, st, a);
   else if (causal) hipLaunchKernelGGL((fwd_kernel<Tag, D, true, false>), grid, block, 0, st, a);
-  else if (sparse) hipLaunchKernelGGL((fwd_kernel<Tag, D, false, true>), grid, block, 0, st, a);
+  else if (sparse)
+    hipLaunchKernelGGL((fwd_kernel<Tag, D, false, true, false, false, SW>), grid, dim3(64 * SW), 0, st, a);
   else hipLaunchKernelGGL((fwd_kernel<Tag, D, false, false>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   timing_end(kFwd, st);
@@ -611,7 +625,8 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStrea
 }  // namespace
 
 hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st) {
-  a.nqb = (a.n + kBR - 1) / kBR;
+  const int rows = sparse ? kWQ * (d == 64 ? sparse_waves<64>() : sparse_waves<128>()) : kBR;
+  a.nqb = (a.n + rows - 1) / rows;
   a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
   if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
                                      : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
