@@ -82,10 +82,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, bytes per launch)
-    ("fwd", 4): ("909593a38bbe8c5e", 1883307031),
-    ("bwd_pre", 4): ("e90f174dd2834aa4", 692098969),
-    ("bwd_dkdv", 4): ("e90f174dd2834aa4", 2122018799),
-    ("bwd_dq", 4): ("e90f174dd2834aa4", 2366753207),
+    ("fwd", 4): ("c0f18f7ffd65f24f", 1842014049),
+    ("bwd_pre", 4): ("9f1d786000fbbb8d", 692101209),
+    ("bwd_dkdv", 4): ("9f1d786000fbbb8d", 2120914183),
+    ("bwd_dq", 4): ("9f1d786000fbbb8d", 2476277269),
 }
 
 
