@@ -564,3 +564,72 @@ def test_very_long_sequence_sampled_rows(d):
     # residual grows like sqrt(N) times their size
     assert np.abs(sum_dk).max() <= 4 * np.sqrt(N) * rms_k * 2.0 ** -8
     assert np.abs(sum_dv - sum_do).max() <= 4 * np.sqrt(N) * rms_v * 2.0 ** -8 + 1e-3 * np.abs(sum_do).max()
+
+
+def _random_case(i):
+    g = np.random.default_rng(1000 + i)
+    H = int(g.choice([1, 2, 3, 4, 6]))
+    Hkv = int(g.choice([h for h in range(1, H + 1) if H % h == 0]))
+    return dict(B=int(g.integers(1, 4)), H=H, Hkv=Hkv, N=int(g.integers(1, 700)), d=int(g.choice([64, 128])),
+                dtype=str(g.choice(["bf16", "f16"])), causal=bool(g.integers(0, 2)),
+                api=str(g.choice(["dense", "gqa", "varlen", "splitkv", "dropout"])), seed=2000 + i)
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_random_shapes_sweep(i):
+    """Seeded random shapes through every entry point family, against the
+    oracle (grouped-head gradient bound as in the grouped-head test)."""
+    c = _random_case(i)
+    B, H, Hkv, N, d, dt, causal = c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["dtype"], c["causal"]
+    s = fp32_scale(d)
+    tol = TOL[dt]
+    G = max(1.0, (H // Hkv) ** 0.5)
+    if c["api"] == "varlen":
+        g = np.random.default_rng(c["seed"])
+        lens = [int(x) for x in g.integers(0, N + 1, B)]
+        lens[0] = N
+        q, k, v, do, cu = workloads.packed_qkvdo(lens, H, Hkv, d, dt, seed=c["seed"])
+        f64 = [t.to(torch.float64).numpy() for t in (q, k, v, do)]
+        gq, gk, gv, gdo, gcu = (t.cuda() for t in (q, k, v, do, cu))
+        o, lse = flash.varlen_fwd(gq, gk, gv, gcu, N, scale=s, causal=causal)
+        dq, dk, dv = flash.varlen_bwd(gq, gk, gv, o, gdo, lse, gcu, N, scale=s, causal=causal)
+        torch.cuda.synchronize()
+        O, L = A.forward_varlen(*f64[:3], cu.numpy(), s, causal)
+        gQ, gK, gV = A.backward_varlen(*f64, cu.numpy(), s, causal)
+    elif c["api"] == "gqa":
+        cpu = workloads.qkvdo_grouped(B, H, Hkv, N, d, dt, seed=c["seed"])
+        q, k, v, do = (t.cuda() for t in cpu)
+        f64 = tuple(t.to(torch.float64).numpy() for t in cpu)
+        o, lse = flash.fwd_gqa(q, k, v, scale=s, causal=causal)
+        dq, dk, dv = flash.bwd_gqa(q, k, v, o, do, lse, scale=s, causal=causal)
+        torch.cuda.synchronize()
+        O, L, gQ, gK, gV = _oracle_gqa(f64, s, causal)
+    else:
+        (q, k, v, do), f64 = make(B, H, N, d, dt, seed=c["seed"])
+        if c["api"] == "splitkv":
+            o, lse = flash.fwd_splitkv(q, k, v, 1 + c["seed"] % 7, scale=s, causal=causal)
+            torch.cuda.synchronize()
+            O, L = _oracle_fwd(f64, s, causal)
+            compare("O", o, O, tol["o"], REL_RMS[dt])
+            compare_lse("LSE", lse, L, tol["lse"])
+            return
+        if c["api"] == "dropout":
+            p, seed = 0.25, c["seed"]
+            o, lse = flash.fwd_dropout(q, k, v, p, seed, 3, scale=s, causal=causal)
+            dq, dk, dv = flash.bwd_dropout(q, k, v, o, do, lse, p, seed, 3, scale=s, causal=causal)
+            torch.cuda.synchronize()
+            O, L, (gQ, gK, gV) = _oracle_dropout(f64, s, causal, p, seed, 3)
+            G = 2.0  # the 1/(1-p) factor
+            tol = dict(o=2 * tol["o"], lse=tol["lse"], grad=tol["grad"])
+        else:
+            o, lse = flash.fwd(q, k, v, scale=s, causal=causal)
+            dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=causal)
+            torch.cuda.synchronize()
+            O, L = _oracle_fwd(f64, s, causal)
+            gQ, gK, gV = _oracle_bwd(f64, s, causal)
+    rg = REL_RMS[dt] if N > 1 else None
+    compare("O", o, O, tol["o"], REL_RMS[dt])
+    compare_lse("LSE", lse, L, tol["lse"])
+    compare("dQ", dq, gQ, tol["grad"] * (2.0 if c["api"] == "dropout" else 1.0), rg)
+    compare("dK", dk, gK, tol["grad"] * G, rg)
+    compare("dV", dv, gV, tol["grad"] * G, REL_RMS[dt])
