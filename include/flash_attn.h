@@ -107,6 +107,11 @@ fa_status flash_attn_fwd(int B, int H, int N, int d, fa_dtype dtype,
  */
 size_t flash_attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, fa_dtype dtype,
                                              int num_splits);
+/* A num_splits for flash_attn_fwd_splitkv: enough key ranges for about two
+ * workgroups per compute unit (512 in all), at least eight 32-key tiles per
+ * range, at most 64; 1 when the plain forward already fills the GPU.
+ * Depends on the shape only; never fails (1 for empty shapes). */
+int flash_attn_fwd_splitkv_num_splits(int B, int H, int N, int d, int causal);
 fa_status flash_attn_fwd_splitkv(int B, int H, int N, int d, fa_dtype dtype,
                                  const void* q, const void* k, const void* v,
                                  float scale, int causal, int num_splits,

@@ -19,6 +19,7 @@ from .flash import (  # noqa: F401
     fwd_dropout,
     fwd_gqa,
     fwd_splitkv,
+    fwd_splitkv_num_splits,
     fwd_splitkv_workspace_size,
     lib,
     varlen_bwd,
@@ -26,6 +27,6 @@ from .flash import (  # noqa: F401
     varlen_fwd,
 )
 
-__all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "fwd_splitkv",
+__all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "fwd_splitkv", "fwd_splitkv_num_splits",
            "fwd_splitkv_workspace_size", "fwd_gqa", "bwd_gqa", "bwd_gqa_workspace_size", "varlen_fwd",
            "varlen_bwd", "varlen_bwd_workspace_size", "fwd_dropout", "bwd_dropout", "lib", "FlashAttnError"]

@@ -421,6 +421,23 @@ FA_EXPORT size_t flash_attn_fwd_splitkv_workspace_size(int B, int H, int N, int 
   return splitkv_workspace_bytes((long long)B * H, N, d, num_splits);
 }
 
+// Ranges that bring the forward to about two workgroups per compute unit
+// (512 on a 256-CU MI355X) while every range keeps at least eight 32-key
+// tiles; 1 when the plain forward already has that many workgroups.
+FA_EXPORT int flash_attn_fwd_splitkv_num_splits(int B, int H, int N, int d, int causal) {
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 1;
+  const long long nqb = (N + 255) / 256;
+  const long long plain = (causal ? (nqb + 1) / 2 : nqb) * (long long)B * H;  // paired causal blocks
+  if (plain >= 512) return 1;
+  const long long split_wgs = nqb * (long long)B * H;  // split mode does not pair blocks
+  long long s = (512 + split_wgs - 1) / split_wgs;
+  const long long by_tiles = ((N + 31) / 32) / 8;
+  if (s > by_tiles) s = by_tiles;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
 FA_EXPORT fa_status flash_attn_fwd_splitkv(int B, int H, int N, int d, fa_dtype dtype, const void* q,
                                            const void* k, const void* v, float scale, int causal,
                                            int num_splits, void* o, float* lse, void* workspace,

@@ -35,6 +35,7 @@ SIGNATURES = {
     "flash_attn_blocksparse_bwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _U8P, _I,
                                         _P, _P, _P, _P, _Z, _P]),
     "flash_attn_fwd_splitkv_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "flash_attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "flash_attn_fwd_splitkv": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _I, _P, _P, _P, _Z, _P]),
     "flash_attn_fwd_gqa": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _F, _I, _P, _P, _P]),
     "flash_attn_bwd_gqa_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
@@ -165,9 +166,16 @@ def fwd_splitkv_workspace_size(B, H, N, d, num_splits, dtype=torch.bfloat16) -> 
     return int(lib().flash_attn_fwd_splitkv_workspace_size(B, H, N, d, _DT[dtype], int(num_splits)))
 
 
-def fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, workspace=None):
-    """(O, LSE) = flash_attn_fwd_splitkv(q, k, v, scale, causal, num_splits)."""
+def fwd_splitkv_num_splits(B, H, N, d, causal=False) -> int:
+    return int(lib().flash_attn_fwd_splitkv_num_splits(B, H, N, d, int(bool(causal))))
+
+
+def fwd_splitkv(q, k, v, num_splits=None, scale=None, causal=False, workspace=None):
+    """(O, LSE) = flash_attn_fwd_splitkv(q, k, v, scale, causal, num_splits);
+    num_splits None: flash_attn_fwd_splitkv_num_splits()."""
     B, H, N, d, dt = _shape(q, k, v)
+    if num_splits is None:
+        num_splits = fwd_splitkv_num_splits(B, H, N, d, causal)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if workspace is None:

@@ -300,6 +300,16 @@ def test_dropout_other_checks():
                                       None, None) == flash.FA_OK
 
 
+def test_splitkv_num_splits_heuristic():
+    ns = flash.lib().flash_attn_fwd_splitkv_num_splits
+    assert ns(1, 8, 8192, 128, 1) == 2      # 32 row blocks x 8 heads = 256 split-mode workgroups
+    assert ns(4, 40, 8192, 128, 1) == 1     # the plain forward already has 2560 workgroups
+    assert ns(1, 1, 512, 64, 0) == 2        # 16 key tiles: at most two ranges of eight
+    assert ns(1, 1, 100, 64, 0) == 1
+    assert ns(1, 1, 16384, 128, 1) == 8     # 64 row blocks: 8 ranges make 512 workgroups
+    assert ns(0, 8, 8192, 128, 1) == 1
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)

@@ -633,3 +633,16 @@ def test_random_shapes_sweep(i):
     compare("dQ", dq, gQ, tol["grad"] * (2.0 if c["api"] == "dropout" else 1.0), rg)
     compare("dK", dk, gK, tol["grad"] * G, rg)
     compare("dV", dv, gV, tol["grad"] * G, REL_RMS[dt])
+
+
+def test_splitkv_default_split_count():
+    """num_splits left to the library (its shape heuristic) gives the plain
+    forward's result."""
+    (q, k, v, _), f64 = make(1, 2, 3000, 128, "bf16", seed=808)
+    s = fp32_scale(128)
+    o, lse = flash.fwd_splitkv(q, k, v, scale=s, causal=True)
+    torch.cuda.synchronize()
+    assert flash.fwd_splitkv_num_splits(1, 2, 3000, 128, True) > 1
+    O, L = _oracle_fwd(f64, s, True)
+    compare("O", o, O, TOL["bf16"]["o"], REL_RMS["bf16"])
+    compare_lse("LSE", lse, L, TOL["bf16"]["lse"])
