@@ -283,6 +283,28 @@ fa_status flash_attn_bwd_dropout(int B, int H, int N, int d, fa_dtype dtype,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dropout on packed variable-length batches (with grouped K/V heads): the
+ * dropout above applied to flash_attn_varlen_fwd / flash_attn_varlen_bwd.
+ * Positions i, j in the counter count from the start of each sequence and
+ * the head index is b*H + h with b the sequence.  Arguments as the varlen
+ * calls plus dropout_p, seed and offset; the same backward workspace.
+ */
+fa_status flash_attn_varlen_fwd_dropout(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                        fa_dtype dtype, const int* cu_seqlens,
+                                        const void* q, const void* k, const void* v,
+                                        float scale, int causal,
+                                        float dropout_p, uint64_t seed, uint32_t offset,
+                                        void* o, float* lse, hipStream_t stream);
+fa_status flash_attn_varlen_bwd_dropout(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                        fa_dtype dtype, const int* cu_seqlens,
+                                        const void* q, const void* k, const void* v,
+                                        const void* o, const void* dout, const float* lse,
+                                        float scale, int causal,
+                                        float dropout_p, uint64_t seed, uint32_t offset,
+                                        void* dq, void* dk, void* dv,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-kernel timing (diagnostics; not part of the method).  While enabled,
  * every kernel the library launches is bracketed by two HIP events recorded
  * on its launch stream.  flash_attn_timing_collect waits for the recorded

@@ -25,8 +25,10 @@ from .flash import (  # noqa: F401
     varlen_bwd,
     varlen_bwd_workspace_size,
     varlen_fwd,
+    varlen_fwd_dropout,
+    varlen_bwd_dropout,
 )
 
 __all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "fwd_splitkv", "fwd_splitkv_num_splits",
            "fwd_splitkv_workspace_size", "fwd_gqa", "bwd_gqa", "bwd_gqa_workspace_size", "varlen_fwd",
-           "varlen_bwd", "varlen_bwd_workspace_size", "fwd_dropout", "bwd_dropout", "lib", "FlashAttnError"]
+           "varlen_bwd", "varlen_bwd_workspace_size", "fwd_dropout", "bwd_dropout", "varlen_fwd_dropout", "varlen_bwd_dropout", "lib", "FlashAttnError"]

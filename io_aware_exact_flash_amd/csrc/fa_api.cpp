@@ -562,6 +562,37 @@ FA_EXPORT fa_status flash_attn_bwd_dropout(int B, int H, int N, int d, fa_dtype 
                  workspace, workspace_bytes_, stream, nullptr, &dr);
 }
 
+FA_EXPORT fa_status flash_attn_varlen_fwd_dropout(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                                  fa_dtype dtype, const int* cu_seqlens, const void* q,
+                                                  const void* k, const void* v, float scale, int causal,
+                                                  float dropout_p, uint64_t seed, uint32_t offset, void* o,
+                                                  float* lse, hipStream_t stream) {
+  const char* fn = "flash_attn_varlen_fwd_dropout";
+  fa::Seqs sq;
+  fa::Drop dr;
+  fa_status s = check_varlen(fn, B, H, Hkv, total, max_seqlen, d, cu_seqlens, &sq);
+  if (s != FA_OK) return s;
+  if ((s = make_drop(fn, dropout_p, seed, offset, &dr)) != FA_OK) return s;
+  return run_fwd(fn, B, H, Hkv, max_seqlen, d, dtype, q, k, v, scale, causal, nullptr, 0, false, o, lse, stream,
+                 &sq, &dr);
+}
+
+FA_EXPORT fa_status flash_attn_varlen_bwd_dropout(int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                                  fa_dtype dtype, const int* cu_seqlens, const void* q,
+                                                  const void* k, const void* v, const void* o, const void* dout,
+                                                  const float* lse, float scale, int causal, float dropout_p,
+                                                  uint64_t seed, uint32_t offset, void* dq, void* dk, void* dv,
+                                                  void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  const char* fn = "flash_attn_varlen_bwd_dropout";
+  fa::Seqs sq;
+  fa::Drop dr;
+  fa_status s = check_varlen(fn, B, H, Hkv, total, max_seqlen, d, cu_seqlens, &sq);
+  if (s != FA_OK) return s;
+  if ((s = make_drop(fn, dropout_p, seed, offset, &dr)) != FA_OK) return s;
+  return run_bwd(fn, B, H, Hkv, max_seqlen, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0, false, dq,
+                 dk, dv, workspace, workspace_bytes_, stream, &sq, &dr);
+}
+
 FA_EXPORT const char* flash_attn_status_string(fa_status status) {
   switch (status) {
     case FA_OK: return "FA_OK";

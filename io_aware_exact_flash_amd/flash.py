@@ -49,6 +49,10 @@ SIGNATURES = {
                                     _P, _P, _P]),
     "flash_attn_bwd_dropout": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _F, ctypes.c_uint64,
                                     ctypes.c_uint32, _P, _P, _P, _P, _Z, _P]),
+    "flash_attn_varlen_fwd_dropout": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _I, _F, ctypes.c_uint64,
+                                           ctypes.c_uint32, _P, _P, _P]),
+    "flash_attn_varlen_bwd_dropout": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _F, _I, _F,
+                                           ctypes.c_uint64, ctypes.c_uint32, _P, _P, _P, _P, _Z, _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
@@ -345,4 +349,37 @@ def bwd_dropout(q, k, v, o, dout, lse, dropout_p, seed, offset=0, scale=None, ca
                                         dout.data_ptr(), lse.data_ptr(), _scale(scale, d), int(bool(causal)),
                                         float(dropout_p), int(seed), int(offset), dq.data_ptr(), dk.data_ptr(),
                                         dv.data_ptr(), ws.data_ptr(), nbytes, _stream(q)))
+    return dq, dk, dv
+
+
+def varlen_fwd_dropout(q, k, v, cu_seqlens, max_seqlen, dropout_p, seed, offset=0, scale=None, causal=False):
+    """(O [total, H, d], LSE [H, total]) = flash_attn_varlen_fwd_dropout(...)."""
+    B, H, Hkv, total, d, dt = _varlen(q, k, v, cu_seqlens)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    _check(lib().flash_attn_varlen_fwd_dropout(B, H, Hkv, total, int(max_seqlen), d, dt, cu_seqlens.data_ptr(),
+                                               q.data_ptr(), k.data_ptr(), v.data_ptr(), _scale(scale, d),
+                                               int(bool(causal)), float(dropout_p), int(seed), int(offset),
+                                               o.data_ptr(), lse.data_ptr(), _stream(q)))
+    return o, lse
+
+
+def varlen_bwd_dropout(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, dropout_p, seed, offset=0, scale=None,
+                       causal=False, workspace=None):
+    """(dQ, dK, dV) = flash_attn_varlen_bwd_dropout(...)."""
+    B, H, Hkv, total, d, dt = _varlen(q, k, v, cu_seqlens, o, dout)
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, total] tensor on the inputs' device")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        nbytes = varlen_bwd_workspace_size(B, H, Hkv, total, int(max_seqlen), d, q.dtype)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        ws, nbytes = workspace, workspace.numel()
+    _check(lib().flash_attn_varlen_bwd_dropout(B, H, Hkv, total, int(max_seqlen), d, dt, cu_seqlens.data_ptr(),
+                                               q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                               dout.data_ptr(), lse.data_ptr(), _scale(scale, d),
+                                               int(bool(causal)), float(dropout_p), int(seed), int(offset),
+                                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,
+                                               _stream(q)))
     return dq, dk, dv

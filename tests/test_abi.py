@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
                      "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_size",
                      "flash_attn_fwd_gqa", "flash_attn_bwd_gqa", "flash_attn_varlen_fwd",
                      "flash_attn_varlen_bwd", "flash_attn_varlen_bwd_workspace_size",
-                     "flash_attn_fwd_dropout", "flash_attn_bwd_dropout"):
+                     "flash_attn_fwd_dropout", "flash_attn_bwd_dropout", "flash_attn_varlen_fwd_dropout",
+                     "flash_attn_varlen_bwd_dropout"):
         assert required in names
 
 

@@ -646,3 +646,52 @@ def test_splitkv_default_split_count():
     O, L = _oracle_fwd(f64, s, True)
     compare("O", o, O, TOL["bf16"]["o"], REL_RMS["bf16"])
     compare_lse("LSE", lse, L, TOL["bf16"]["lse"])
+
+
+def _oracle_varlen_dropout(f64, cu, s, causal, p, seed, offset):
+    q, k, v, do = f64
+    T, H, _ = q.shape
+    Hkv = k.shape[1]
+    t = PX.drop_threshold(p)
+    pd = t / 256.0
+    O, L = np.zeros(q.shape), np.full((H, T), -np.inf)
+    gQ, gK, gV = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(len(cu) - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        if e <= a:
+            continue
+        for h in range(H):
+            g = A.kv_head_of(h, H, Hkv)
+            keep = PX.keep_matrix(e - a, e - a, b * H + h, seed, offset, t)
+            O[a:e, h], L[h, a:e] = A.forward_head_dropout(q[a:e, h], k[a:e, g], v[a:e, g], s, causal, keep, pd)
+            dq_, dk_, dv_ = A.backward_head_dropout(q[a:e, h], k[a:e, g], v[a:e, g], do[a:e, h], s, causal, keep, pd)
+            gQ[a:e, h] = dq_
+            gK[a:e, g] += dk_
+            gV[a:e, g] += dv_
+    return O, L, gQ, gK, gV
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", [([300, 0, 129, 1], 4, 2), ([500, 77], 3, 1)])
+def test_varlen_dropout(d, causal, case):
+    """Dropout on a packed batch with grouped heads: positions in the
+    counter count from each sequence's start, the head index is b*H + h."""
+    lens, H, Hkv = case
+    p, seed, offset = 0.2, 4242 + d, 9
+    q, k, v, do, cu = workloads.packed_qkvdo(lens, H, Hkv, d, "bf16", seed=900 + d + H)
+    f64 = [t.to(torch.float64).numpy() for t in (q, k, v, do)]
+    gq, gk, gv, gdo, gcu = (t.cuda() for t in (q, k, v, do, cu))
+    s = fp32_scale(d)
+    o, lse = flash.varlen_fwd_dropout(gq, gk, gv, gcu, max(lens), p, seed, offset, scale=s, causal=causal)
+    dq, dk, dv = flash.varlen_bwd_dropout(gq, gk, gv, o, gdo, lse, gcu, max(lens), p, seed, offset, scale=s,
+                                          causal=causal)
+    torch.cuda.synchronize()
+    O, L, gQ, gK, gV = _oracle_varlen_dropout(f64, cu.numpy(), s, causal, p, seed, offset)
+    tol = TOL["bf16"]
+    G = 2.0 * (H // Hkv) ** 0.5
+    compare("O", o, O, 2 * tol["o"], REL_RMS["bf16"])
+    compare_lse("LSE", lse, L, tol["lse"])
+    compare("dQ", dq, gQ, 2 * tol["grad"], REL_RMS["bf16"])
+    compare("dK", dk, gK, G * tol["grad"], REL_RMS["bf16"])
+    compare("dV", dv, gV, G * tol["grad"], REL_RMS["bf16"])
