@@ -63,11 +63,17 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
     if constexpr (SPARSE)
       if (!mrow[k0 / kMaskBlock]) continue;
     __syncthreads();
-    for (int e = lane; e < kBC * D; e += 64) {
-      int r = e / D, col = e % D;
-      int row = min(k0 + r, n - 1);
-      ks_[r * LD + col] = K[(size_t)row * ksr + col];
-      vs_[r * LD + col] = V[(size_t)row * ksr + col];
+    // 16-byte loads (four columns per lane), scattered into the padded rows
+    for (int e = 4 * lane; e < kBC * D; e += 4 * 64) {
+      const int r = e / D, col = e % D;
+      const int row = min(k0 + r, n - 1);
+      const f32x4 kx = *reinterpret_cast<const f32x4*>(K + (size_t)row * ksr + col);
+      const f32x4 vx = *reinterpret_cast<const f32x4*>(V + (size_t)row * ksr + col);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ks_[r * LD + col + t] = kx[t];
+        vs_[r * LD + col + t] = vx[t];
+      }
     }
     __syncthreads();
     f32x16 s = 0.0f;
