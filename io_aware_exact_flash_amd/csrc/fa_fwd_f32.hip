@@ -3,10 +3,12 @@
 // Same online-softmax pass as the 16-bit kernel (FlashAttention-2 notes,
 // Algorithm 1), but every operand stays float32: the two contractions use
 // v_mfma_f32_32x32x2_f32 and P is never rounded, so the result agrees with
-// a float64 evaluation to float32 accuracy.  One wave owns 32 query rows and
-// the workgroup is that single wave: float32 inputs are used for small
-// problems where latency, not throughput, decides, so the grid is made as
-// wide as the query count allows.
+// a float64 evaluation to float32 accuracy.  Float32 inputs are used for
+// small problems where latency, not throughput, decides: a workgroup owns 32
+// query rows, and its four waves take every fourth key tile each (own LDS
+// buffers, no barriers in the sweep), keeping their own running max, sum and
+// output; at the end the four partial states are merged with the
+// statistics merge of the v1 notes (max, rescaled sums and outputs).
 //
 // Operands of v_mfma_f32_32x32x2_f32 (g = lane / 32, c = lane % 32):
 //   A: lane holds A[c][g]   B: lane holds B[g][c]
@@ -17,17 +19,22 @@
 namespace fa {
 namespace {
 
-constexpr int kBC = 32;  // keys per tile
+constexpr int kBC = 32;    // keys per tile
+constexpr int kWaves = 4;  // waves per workgroup, each on every fourth key tile
 
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(FwdArgs a) {
   constexpr int LD = D + 1;  // padded LDS row (floats)
   constexpr int MB = D / 32;
-  __shared__ float ks_[kBC * LD];
-  __shared__ float vs_[kBC * LD];
+  constexpr int TILE = kBC * LD;
+  static_assert(kWaves * 64 * (MB * 16 + 2) <= kWaves * 2 * TILE, "merge area fits the tile buffers");
+  __shared__ float smem[kWaves * 2 * TILE];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c32 = lane & 31, g = lane >> 5;
+  float* ks_ = smem + w * 2 * TILE;  // this wave's K and V tiles
+  float* vs_ = ks_ + TILE;
   const int lb = xcd_remap(blockIdx.x, a.nblk);
   const int bh = lb / a.nqb;
   const HeadAt at = query_head(a.sq, bh, a.n);
@@ -58,11 +65,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_part = 0.0f;
   const float cs = a.c;
 
-  for (int j = 0; j < j_end; ++j) {
+  for (int j = w; j < j_end; j += kWaves) {
     const int k0 = j * kBC;
     if constexpr (SPARSE)
       if (!mrow[k0 / kMaskBlock]) continue;
-    __syncthreads();
+    // The buffers are this wave's own and a wave's LDS accesses complete in
+    // order, so the previous tile's reads are done before these writes and
+    // the writes before the reads below; the wave barriers only keep the
+    // compiler from moving accesses across.
+    __builtin_amdgcn_wave_barrier();
     // 16-byte loads (four columns per lane), scattered into the padded rows
     for (int e = 4 * lane; e < kBC * D; e += 4 * 64) {
       const int r = e / D, col = e % D;
@@ -75,7 +86,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
         vs_[r * LD + col + t] = vx[t];
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     f32x16 s = 0.0f;
 #pragma unroll
     for (int t = 0; t < D / 2; ++t)
@@ -115,7 +126,45 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
     }
   }
 
-  const float l = half_sum(l_part);
+  // merge the four waves' states: m = max_w m_w, l = sum_w e^{m_w - m} l_w,
+  // O = sum_w e^{m_w - m} O_w / l (m in exp2 units; a wave that saw no key
+  // has m_w = -inf and weight 0)
+  __syncthreads();  // every wave is done with its tiles: the LDS is reused
+  constexpr int PART = MB * 16;
+  float* part = smem;                            // [wave][lane][PART] partial O^T
+  float* stat = smem + kWaves * 64 * PART;       // [wave][lane][2] m, partial l
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[(w * 64 + lane) * PART + 16 * mb + v] = oacc[mb][v];
+  stat[(w * 64 + lane) * 2] = m_run;
+  stat[(w * 64 + lane) * 2 + 1] = l_part;
+  __syncthreads();
+  if (w != 0) return;
+  float mw[kWaves], alpha_w[kWaves];
+  float mstar = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    mw[u] = stat[(u * 64 + lane) * 2];
+    mstar = fmaxf(mstar, mw[u]);
+  }
+  float lsum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    alpha_w[u] = (mw[u] == -INFINITY) ? 0.0f : fast_exp2(mw[u] - mstar);
+    lsum = fmaf(alpha_w[u], stat[(u * 64 + lane) * 2 + 1], lsum);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float o = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kWaves; ++u) o = fmaf(alpha_w[u], part[(u * 64 + lane) * PART + 16 * mb + v], o);
+      oacc[mb][v] = o;
+    }
+  m_run = mstar;
+  const float l = half_sum(lsum);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (my_q < n) {
     float* op = reinterpret_cast<float*>(a.o) + at.q + (size_t)my_q * qsr;
@@ -134,7 +183,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
 
 template <int D>
 hipError_t launch_d(bool causal, bool sparse, const FwdArgs& a, hipStream_t st) {
-  dim3 grid(a.nblk), block(64);
+  dim3 grid(a.nblk), block(64 * kWaves);
   timing_begin(kFwdF32, st);
   if (causal && sparse) hipLaunchKernelGGL((fwd_f32_kernel<D, true, true>), grid, block, 0, st, a);
   else if (causal) hipLaunchKernelGGL((fwd_f32_kernel<D, true, false>), grid, block, 0, st, a);
