@@ -40,7 +40,11 @@ def allowed(n_q: int, n_k: int, causal: bool, block_mask=None,
             mask_block: int = MASK_BLOCK, rows=None) -> np.ndarray:
     """Boolean matrix [len(rows), n_k]: True where query row i may see key j.
 
-    causal: j <= i (query and key positions share one index space, n_q == n_k).
+    causal: j <= i + (n_k - n_q).  With equal lengths this is j <= i (query
+    and key positions share one index space).  With fewer queries than keys
+    (a KV cache) the queries are the last n_q positions of the sequence, so
+    query i sits at position n_k - n_q + i: the last query sees every key,
+    and a query with n_k - n_q + i < 0 sees none.
     block_mask: 0/1 array [ceil(n_q/mask_block), ceil(n_k/mask_block)]; entry
     (i // mask_block, j // mask_block) must be 1.
     """
@@ -48,7 +52,7 @@ def allowed(n_q: int, n_k: int, causal: bool, block_mask=None,
     j = np.arange(n_k)
     ok = np.ones((i.shape[0], n_k), dtype=bool)
     if causal:
-        ok &= j[None, :] <= i[:, None]
+        ok &= j[None, :] <= i[:, None] + (n_k - n_q)
     if block_mask is not None:
         bm = np.asarray(block_mask).astype(bool)
         ok &= bm[i[:, None] // mask_block, j[None, :] // mask_block]
@@ -278,3 +282,28 @@ def backward_head_dropout(q, k, v, do, scale, causal, keep, p_drop):
     rowdot = (P * dP).sum(axis=1)             # <p, dp> per row, eq. (30)
     dS = P * (dP - rowdot[:, None])
     return scale * (dS @ k), scale * (dS.T @ q), dv
+
+
+# ---------------------------------------------------------------- KV cache: fewer queries than keys
+# FlashAttention-2 notes, "impact on the KV cache" (MQA/GQA shrink the
+# cache that decoding reads): at a decoding step a few new queries (often
+# one) attend to every cached key of their sequence.  q [B, H, Nq, d];
+# k, v [B, Hkv, Nk, d] hold Nk cache slots, of which the first L_b are
+# valid for sequence b (cache_lens, default all Nk).  The queries are the
+# last Nq positions of a sequence of L_b tokens: under the causal rule,
+# query i sees key j iff j <= i + L_b - Nq (``allowed`` above).
+
+def forward_kvcache(q, k, v, scale, causal=False, cache_lens=None, heads=None):
+    """-> {(b, h): (O [Nq, d], LSE [Nq])}; each query head attends over its
+    group's K/V head, keys 0 .. L_b - 1."""
+    B, H, Nq = q.shape[:3]
+    Hkv, Nk = k.shape[1], k.shape[2]
+    out = {}
+    for (b, h) in _heads(B, H, heads):
+        L = Nk if cache_lens is None else int(cache_lens[b])
+        g = kv_head_of(h, H, Hkv)
+        if L == 0:
+            out[(b, h)] = (np.zeros((Nq, q.shape[3])), np.full(Nq, -np.inf))
+            continue
+        out[(b, h)] = forward_head(q[b, h], k[b, g, :L], v[b, g, :L], scale, causal)
+    return out

@@ -33,6 +33,13 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+# Achieved errors of every comparison in this process, {test: [(name, max
+# abs error, relative RMS error, bound)]}; tests/conftest.py writes them to
+# the JSON file named by FA_PARITY_LOG at the end of the session.
+RECORD = {}
+CURRENT_TEST = ["(none)"]
+
+
 def compare(name, got, ref, atol, rel_rms=None, mask=None):
     """Assert max|got - ref| <= atol (and the relative RMS gate); returns stats."""
     g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
@@ -46,6 +53,7 @@ def compare(name, got, ref, atol, rel_rms=None, mask=None):
     err = float(np.abs(g - r).max())
     nr = float(np.linalg.norm(r))
     rel = float(np.linalg.norm(g - r) / nr) if nr > 0 else float(np.linalg.norm(g - r))
+    RECORD.setdefault(CURRENT_TEST[0], []).append((name, err, rel, float(atol)))
     assert err <= atol, f"{name}: max abs error {err:.3e} > {atol:.1e} (rel rms {rel:.2e})"
     if rel_rms is not None:
         assert rel <= rel_rms, f"{name}: relative RMS error {rel:.2e} > {rel_rms:.1e} (max abs {err:.2e})"

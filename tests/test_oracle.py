@@ -623,3 +623,134 @@ def test_dropout_gradients_by_central_differences(causal):
             X[idx] = old
             num[idx] = (fp - fm) / (2 * eps)
         assert np.abs(num - G[name]).max() <= 1e-6 * max(1.0, np.abs(G[name]).max()), name
+
+
+# Inverted dropout is defined so that the dropped output is an unbiased
+# estimate of the plain one: E_Z[(P o Z) V / (1 - p')] = P V because each
+# keep decision holds with probability 1 - p'.  O, and through it D and dS,
+# are linear in Z, so the same holds for every gradient.  Averaging over
+# independent Philox streams (offsets) must reproduce the plain attention;
+# a wrong factor (multiplying by 1 - p' instead of dividing, or no factor)
+# leaves a bias many standard errors wide.
+def _dropout_average(fn, n_draws, n, t, seed):
+    outs = []
+    for off in range(n_draws):
+        keep = PX.keep_matrix(n, n, 0, seed, off, t)
+        outs.append(np.concatenate([np.ravel(x) for x in fn(keep)]))
+    X = np.stack(outs)
+    return X.mean(0), X.std(0, ddof=1) / math.sqrt(n_draws)
+
+
+def _bias_statistic(mean, sem, ref):
+    """(mean squared z-score, max |z|) over elements with spread; elements
+    with none must already equal the reference."""
+    live = sem > 1e-12
+    assert np.allclose(mean[~live], ref[~live], atol=1e-12)
+    z = (mean[live] - ref[live]) / sem[live]
+    return float(np.mean(z * z)), float(np.abs(z).max())
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_is_unbiased_and_wrong_factors_are_caught(p, causal):
+    r = _rng(71 + int(10 * p) + causal)
+    n, d, s, draws = 20, 3, 0.7, 600
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    t = PX.drop_threshold(p)
+    pd = t / 256.0
+    plain = np.concatenate([np.ravel(x) for x in (A.forward_head(q, k, v, s, causal)[0],
+                                                  *A.backward_head(q, k, v, do, s, causal))])
+
+    def right(keep):
+        return (A.forward_head_dropout(q, k, v, s, causal, keep, pd)[0],
+                *A.backward_head_dropout(q, k, v, do, s, causal, keep, pd))
+
+    mean, sem = _dropout_average(right, draws, n, t, seed=99)
+    chi2, zmax = _bias_statistic(mean, sem, plain)
+    # z-scores of an unbiased estimate: mean square about 1, none beyond ~5
+    assert chi2 < 2.0 and zmax < 5.5, (chi2, zmax)
+
+    # planted mistakes, applied to the oracle's outputs on the CPU: every
+    # output of the dropout path is linear in the factor, so scaling the
+    # results by (1 - p')^2 is the multiply-instead-of-divide mistake and by
+    # (1 - p') the dropped factor
+    for wrong in ((1.0 - pd) ** 2, 1.0 - pd):
+        def planted(keep, f=wrong):
+            return tuple(f * x for x in right(keep))
+        mean_b, sem_b = _dropout_average(planted, draws, n, t, seed=99)
+        chi2_b, _ = _bias_statistic(mean_b, sem_b, plain)
+        assert chi2_b > 10.0, (wrong, chi2_b)
+
+
+# ------------------------------------------------------- P12 fewer queries than keys (KV cache)
+def test_kvcache_causal_reading_reduces_to_square_case_and_last_query_sees_all():
+    """With n_q = n_k the causal rule is j <= i; with n_q < n_k the last
+    query sees every key and query i sees keys 0 .. n_k - n_q + i."""
+    for n in (1, 5, 33):
+        ok = A.allowed(n, n, True)
+        assert (ok == np.tril(np.ones((n, n), dtype=bool))).all()
+    for nq, nk in ((1, 40), (3, 17), (7, 7), (5, 2)):
+        ok = A.allowed(nq, nk, True)
+        for i in range(nq):
+            assert ok[i].sum() == max(0, min(nk, nk - nq + i + 1))
+        if nk >= nq:
+            assert ok[-1].all()
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 37), (4, 37), (37, 37), (6, 3)])
+def test_kvcache_forward_against_bruteforce(nq, nk):
+    r = _rng(101 + nq + nk)
+    d, s = 5, 0.6
+    q = r.standard_normal((nq, d))
+    k, v = r.standard_normal((nk, d)), r.standard_normal((nk, d))
+    for causal in (False, True):
+        O, L = A.forward_head(q, k, v, s, causal)
+        Ob, Lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), s,
+                                 lambda i, j: (not causal) or j <= i + nk - nq)
+        np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(np.isneginf(L), np.isneginf(Lb))
+        fin = np.isfinite(Lb)
+        np.testing.assert_allclose(L[fin], Lb[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_kvcache_decoding_continues_the_sequence():
+    """The reading that the queries are the last positions of their
+    sequence: attending the last n_q queries of a causal self-attention
+    problem over the whole key set reproduces that problem's last n_q rows
+    (computed with equal lengths, j <= i)."""
+    r = _rng(107)
+    n, d, s = 29, 6, 0.45
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    Ofull, Lfull = A.forward_head(q, k, v, s, True)
+    for nq in (1, 2, 9, n):
+        O, L = A.forward_head(q[n - nq:], k, v, s, True)
+        np.testing.assert_allclose(O, Ofull[n - nq:], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(L, Lfull[n - nq:], rtol=1e-13, atol=1e-13)
+
+
+def test_kvcache_grouped_heads_and_cache_lengths():
+    """forward_kvcache: query head h reads K/V head h // (H / Hkv) over the
+    first L_b cache slots only; slots past L_b never matter; an empty cache
+    gives O = 0, LSE = -inf."""
+    r = _rng(109)
+    B, H, Hkv, nq, nk, d, s = 3, 4, 2, 2, 11, 4, 0.7
+    q = r.standard_normal((B, H, nq, d))
+    k, v = r.standard_normal((B, Hkv, nk, d)), r.standard_normal((B, Hkv, nk, d))
+    lens = [11, 6, 0]
+    out = A.forward_kvcache(q, k, v, s, True, lens)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, 6:] = 1e3  # garbage past the valid slots
+    v2[1, :, 6:] = -7.0
+    out2 = A.forward_kvcache(q, k2, v2, s, True, lens)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hkv)
+            if lens[b] == 0:
+                assert (out[(b, h)][0] == 0).all() and np.isneginf(out[(b, h)][1]).all()
+                continue
+            L = lens[b]
+            Ob, Lb = brute_attention(q[b, h].tolist(), k[b, g, :L].tolist(), v[b, g, :L].tolist(), s,
+                                     lambda i, j: j <= i + L - nq)
+            np.testing.assert_allclose(out[(b, h)][0], Ob, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(out[(b, h)][1], Lb, rtol=1e-12, atol=1e-12)
+            np.testing.assert_array_equal(out2[(b, h)][0], out[(b, h)][0])

@@ -168,20 +168,50 @@ def test_empty_inputs():
         assert o.shape == q.shape and lse.shape == (B, H, N) and dq.shape == q.shape
 
 
-def test_large_magnitude_scores_stay_finite():
-    """Scores of magnitude ~1e3 exercise the max subtraction (safe softmax)."""
+def test_large_magnitude_scores():
+    """Scores of magnitude ~1e3 (Q, K drawn with gain 6, scale 1) exercise the
+    max subtraction of the safe softmax; V and dO keep unit scale.
+
+    Bounds: O and dV are the stated 16-bit bounds (their size is set by V and
+    dO).  dQ = scale dS K and dK = scale dS^T Q are not: with scale 1 and
+    gain-6 operands they reach ~1e2 instead of ~1.  Rounding errors of 16-bit
+    arithmetic are relative to the size of the result, so their bound is
+    stated relative to the largest gradient element: 2^-6 max|ref| (the
+    ratio of the stated 5e-2 to the largest gradients, ~3, of unit-scale
+    inputs), with the usual relative-RMS gate.  LSE: each score is a
+    float32 dot product of d exactly representable products, so its
+    rounding error is at most gamma_d sum_c |q_c| |k_c| (gamma_d = d u /
+    (1 - d u), u = 2^-24, the classical dot-product bound); LSE is a smooth
+    maximum of the scores (1-Lipschitz in their max norm), and the final
+    m ln 2 + ln l adds a few roundings of |LSE|.  The bound per row is that
+    sum over its allowed keys plus 8 u |LSE_i|."""
     N, d = 300, 128
-    (q, k, v, do), f64 = make(1, 2, N, d, "bf16", seed=21, gain=6.0)
+    qk = workloads.qkvdo(1, 2, N, d, "bf16", seed=21, gain=6.0)
+    vd = workloads.qkvdo(1, 2, N, d, "bf16", seed=22)
+    cpu = (qk[0], qk[1], vd[2], vd[3])
+    q, k, v, do = (t.cuda() for t in cpu)
+    f64 = tuple(t.to(torch.float64).numpy() for t in cpu)
     s = 1.0
     o, lse = flash.fwd(q, k, v, scale=s, causal=True)
     dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=True)
     torch.cuda.synchronize()
     O, L = _oracle_fwd(f64, s, True)
-    # O is linear in V: inputs 6x larger scale the stated 2e-2 bound by 6
-    compare("O", o, O, 6 * TOL["bf16"]["o"], REL_RMS["bf16"])
-    compare_lse("LSE", lse, L, 2e-2)  # |LSE| ~ 1e3: a few float32 ulps of 1e3
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all()
+    gQ, gK, gV = _oracle_bwd(f64, s, True)
+    tol = TOL["bf16"]
+    compare("O", o, O, tol["o"], REL_RMS["bf16"])
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    ok = A.allowed(N, N, True)
+    lg = to64(lse)
+    for h in range(2):
+        a = np.where(ok, s * (np.abs(f64[0][0, h]) @ np.abs(f64[1][0, h]).T), 0.0).max(1)
+        bound = gamma * a + 8 * u * np.abs(L[0, h])
+        err = np.abs(lg[0, h] - L[0, h])
+        assert (err <= bound).all(), f"LSE head {h}: error {err.max():.3e} vs bound {bound.min():.3e}"
+        compare(f"LSE[{h}]", lg[0, h], L[0, h], float(bound.max()))
+    compare("dQ", dq, gQ, 2.0 ** -6 * np.abs(gQ).max(), REL_RMS["bf16"])
+    compare("dK", dk, gK, 2.0 ** -6 * np.abs(gK).max(), REL_RMS["bf16"])
+    compare("dV", dv, gV, tol["grad"], REL_RMS["bf16"])
 
 
 def test_stream_and_repeatability():
@@ -695,3 +725,72 @@ def test_varlen_dropout(d, causal, case):
     compare("dQ", dq, gQ, 2 * tol["grad"], REL_RMS["bf16"])
     compare("dK", dk, gK, G * tol["grad"], REL_RMS["bf16"])
     compare("dV", dv, gV, G * tol["grad"], REL_RMS["bf16"])
+
+
+def _identity_rows(B, H, N, d, dtype):
+    """[B, H, N, d] whose row i is the unit vector e_i (N <= d)."""
+    x = torch.zeros((B, H, N, d), dtype=DT[dtype])
+    x[:, :, torch.arange(N), torch.arange(N)] = 1
+    return x
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,N", [(64, 61), (128, 125), (64, 7)])
+def test_dropout_decisions_of_the_dkdv_pass(causal, d, N):
+    """Keep decisions drawn by the dK/dV pass, element by element.  With
+    dO = [I | 0] (row i of dO is e_i), dV = (P o Z)^T dO / (1 - p') has
+    dV[j, i] = P_ij Z_ij / (1 - p') for i < N: its zero pattern is
+    (Z and allowed)^T exactly (every allowed P_ij > 0).  N is ragged against
+    the 4 x 4 decision blocks and the 32-row tiles; several heads check the
+    head index of the counter."""
+    B, H, p, seed, offset = 2, 3, 0.3, 0x0BAD_5EED_1234 + N, 11 + d
+    q, k, v, _ = workloads.qkvdo(B, H, N, d, "bf16", seed=17 + N)
+    do = _identity_rows(B, H, N, d, "bf16")
+    gq, gk, gv, gdo = (t.cuda() for t in (q, k, v, do))
+    o, lse = flash.fwd_dropout(gq, gk, gv, p, seed, offset, causal=causal)
+    _, _, dv = flash.bwd_dropout(gq, gk, gv, o, gdo, lse, p, seed, offset, causal=causal)
+    torch.cuda.synchronize()
+    t = PX.drop_threshold(p)
+    allowed = A.allowed(N, N, causal)
+    dvc = to64(dv)
+    assert (dvc[..., N:] == 0).all()
+    for b in range(B):
+        for h in range(H):
+            keep = PX.keep_matrix(N, N, b * H + h, seed, offset, t)
+            got = dvc[b, h, :, :N] != 0            # [key j, query i]
+            want = (keep & allowed).T
+            assert (got == want).all(), (b, h, int((got != want).sum()))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,N", [(64, 61), (128, 125), (64, 7)])
+def test_dropout_decisions_of_the_dq_pass(causal, d, N):
+    """Keep decisions drawn by the dQ pass, element by element.  With Q = 0
+    every allowed probability is 1/n_i (n_i allowed keys of row i); with
+    K = V = [I | 0] and dO = 1, dP'_ij = 1, O_ic = Z_ic / (n_i (1 - p')) and
+    D_i = sum_c O_ic, so dQ[i, j] = scale dS_ij = scale (Z_ij / (1 - p') - D_i) / n_i
+    for j < N.  Solving for Z_ij (threshold 1/2, far from the rounding
+    error) gives the decisions, which must equal the oracle's draws."""
+    B, H, p, seed, offset = 2, 3, 0.3, 0x51DE_CAFE + N, 5 + d
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    k = _identity_rows(B, H, N, d, "bf16")
+    v = k.clone()
+    do = torch.ones((B, H, N, d), dtype=torch.bfloat16)
+    s = 0.5
+    gq, gk, gv, gdo = (t.cuda() for t in (q, k, v, do))
+    o, lse = flash.fwd_dropout(gq, gk, gv, p, seed, offset, scale=s, causal=causal)
+    dq, _, _ = flash.bwd_dropout(gq, gk, gv, o, gdo, lse, p, seed, offset, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    t = PX.drop_threshold(p)
+    pd = t / 256.0
+    allowed = A.allowed(N, N, causal)
+    n_i = allowed.sum(1).astype(np.float64)
+    oc, dqc = to64(o), to64(dq)
+    for b in range(B):
+        for h in range(H):
+            keep = PX.keep_matrix(N, N, b * H + h, seed, offset, t)
+            D = oc[b, h].sum(1)                      # rowsum(dO o O) with dO = 1
+            z = (dqc[b, h, :, :N] * n_i[:, None] / s + D[:, None]) * (1.0 - pd)
+            got = z > 0.5
+            assert (got[allowed] == keep[allowed]).all(), (b, h, int((got[allowed] != keep[allowed]).sum()))
+            assert (dqc[b, h, :, :N][~allowed] == 0).all()
