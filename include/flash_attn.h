@@ -31,7 +31,9 @@
  * Pointers.  All tensor, mask and workspace pointers are DEVICE pointers,
  *   owned by the caller, 16-byte aligned, and must stay valid until the
  *   stream reaches the enqueued work.  The library never allocates or frees
- *   device memory and keeps no pointer after a call returns.
+ *   device memory and keeps no caller pointer after a call returns; the
+ *   only device memory it holds is the static scratch array of
+ *   flash_attn_bwd_noalloc (32 MiB per GPU, part of the loaded code object).
  * Streams.  Every call enqueues its kernels on `stream` (0 = null stream)
  *   and returns without synchronising.
  * Domain.  d in {64, 128}; N >= 0 (any value, no tile-multiple needed);
@@ -142,6 +144,27 @@ fa_status flash_attn_bwd(int B, int H, int N, int d, fa_dtype dtype,
                          float scale, int causal,
                          void* dq, void* dk, void* dv,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward pass without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it).  Same arguments,
+ * layouts, result and errors as flash_attn_bwd minus the workspace, which
+ * here is a buffer the library holds: one static device array of 32 MiB per
+ * GPU, held by each GPU the library runs on until the process ends, enough
+ * for B*H*N up to about 4.1 million query rows.  Larger problems return
+ * FA_ERR_UNSUPPORTED (use flash_attn_bwd).  The call allocates nothing; on
+ * its first use on a device it looks up that device's copy of the array
+ * (hipGetSymbolAddress).  `stream` (if not 0) must belong to the current
+ * device (FA_ERR_INVALID_ARGUMENT otherwise).  All calls on one GPU share
+ * the array: calls that overlap on one GPU (different streams, no ordering
+ * between them) race and give undefined results.
+ */
+fa_status flash_attn_bwd_noalloc(int B, int H, int N, int d, fa_dtype dtype,
+                                 const void* q, const void* k, const void* v,
+                                 const void* o, const void* dout, const float* lse,
+                                 float scale, int causal,
+                                 void* dq, void* dk, void* dv, hipStream_t stream);
 
 /*
  * Block-sparse forward [FA1 "Block-Sparse FlashAttention"; WALK

@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "fa_api_internal.hpp"
 #include "fa_kernels.hpp"
 
 #define FA_EXPORT extern "C" __attribute__((visibility("default")))
@@ -20,13 +21,17 @@ namespace {
 thread_local std::string g_last_error;
 
 fa_status fail(fa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-fa_status fail(fa_status s, const char* fmt, ...) {
+fa_status vfail(fa_status s, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  g_last_error = buf;
+  return s;
+}
+fa_status fail(fa_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(s, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return s;
 }
 
@@ -184,7 +189,8 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
                   const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   float scale, int causal, const uint8_t* mask, int mask_block, bool sparse,
                   void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream,
-                  const fa::Seqs* seqs = nullptr, const fa::Drop* drop = nullptr) {
+                  const fa::Seqs* seqs = nullptr, const fa::Drop* drop = nullptr,
+                  fa::WorkspaceFn get_ws = nullptr) {
   Problem p;
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, true, &p);
   if (s != FA_OK) return s;
@@ -193,13 +199,19 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   if (p.empty || (seqs && seqs->total == 0)) return FA_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace"};
-  if ((s = check_ptrs(fn, ptrs, names, 10)) != FA_OK) return s;
+  // (a workspace from get_ws is checked once it has been supplied)
+  if ((s = check_ptrs(fn, ptrs, names, get_ws ? 9 : 10)) != FA_OK) return s;
   const int grp = H / Hkv;
   const long long bhkv = (long long)B * Hkv;
   const int hsplit = fa::dkdv_head_splits(bhkv, N, grp);
   // per-row arrays: one per query row of every head (dense B*H*N, packed H*total)
   const long long lrows = seqs ? (long long)H * seqs->total : p.bh * (long long)N;
   const size_t need = gqa_workspace_bytes(lrows, bhkv, N, d, grp);
+  if (get_ws) {
+    if ((s = get_ws(fn, need, stream, &ws, &ws_bytes)) != FA_OK) return s;
+    const void* wp[] = {ws};
+    if ((s = check_ptrs(fn, wp, names + 9, 1)) != FA_OK) return s;
+  }
   if (ws_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
 
@@ -350,6 +362,21 @@ const char* kKernelNames[fa::kNumKernels] = {"fwd",          "fwd_f32",   "bwd_p
 }  // namespace
 
 namespace fa {
+fa_status fail_status(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(s, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fa_status bwd_dense_with(const char* fn, int B, int H, int N, int d, fa_dtype dtype, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout, const float* lse, float scale, int causal,
+                         void* dq, void* dk, void* dv, WorkspaceFn get_ws, hipStream_t stream) {
+  return run_bwd(fn, B, H, H, N, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0, false, dq, dk, dv,
+                 nullptr, 0, stream, nullptr, nullptr, get_ws);
+}
+
 void timing_begin(int kernel, hipStream_t st) {
   std::lock_guard<std::mutex> g(g_timing_mu);
   if (!g_timing_on) return;

@@ -53,6 +53,7 @@ SIGNATURES = {
                                            ctypes.c_uint32, _P, _P, _P]),
     "flash_attn_varlen_bwd_dropout": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _F, _I, _F,
                                            ctypes.c_uint64, ctypes.c_uint32, _P, _P, _P, _P, _Z, _P]),
+    "flash_attn_bwd_noalloc": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
@@ -211,6 +212,24 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal=False, workspace=None):
                                 dout.data_ptr(), lse.data_ptr(), _scale(scale, d), int(bool(causal)),
                                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes,
                                 _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None):
+    """(dQ, dK, dV) = flash_attn_bwd_noalloc(...): the backward with its
+    workspace held by the library (no device allocation in the call; pass
+    dq, dk, dv to avoid torch allocating the outputs too)."""
+    B, H, N, d, dt = _shape(q, k, v, o, dout)
+    _lse_ok(lse, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous tensors shaped like q")
+    _check(lib().flash_attn_bwd_noalloc(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        dout.data_ptr(), lse.data_ptr(), _scale(scale, d), int(bool(causal)),
+                                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(q)))
     return dq, dk, dv
 
 
