@@ -174,6 +174,8 @@ fa_status flash_attn_bwd_noalloc(int B, int H, int N, int d, fa_dtype dtype,
  *   block_mask  in  device uint8 [T][T], T = ceil(N / mask_block), row-major,
  *               shared by every (batch, head); nonzero = keep.
  *   mask_block  tokens per mask entry; must be 128 (FA_ERR_UNSUPPORTED else).
+ * N is limited to 128 * 2048 = 262144 tokens (T <= 2048; FA_ERR_UNSUPPORTED
+ * beyond): the kernels keep tables of one row or column of the mask on chip.
  * causal may be combined with the mask (both must allow a key).
  */
 fa_status flash_attn_blocksparse_fwd(int B, int H, int N, int d, fa_dtype dtype,

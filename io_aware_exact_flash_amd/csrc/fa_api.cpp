@@ -107,10 +107,16 @@ fa_status make_drop(const char* fn, float p, uint64_t seed, uint32_t offset, fa:
   return FA_OK;
 }
 
-fa_status check_mask(const char* fn, const uint8_t* mask, int mask_block) {
+// The kernels hold one row (or column) of the mask as bits in LDS: at most
+// kMaskMaxEntries entries, i.e. N up to 128 * kMaskMaxEntries tokens.
+constexpr int kMaskMaxEntries = 2048;
+
+fa_status check_mask(const char* fn, const uint8_t* mask, int mask_block, int N) {
   if (!mask) return fail(FA_ERR_INVALID_ARGUMENT, "%s: block_mask is null", fn);
   if (mask_block != fa::kMaskBlockTokens)
     return fail(FA_ERR_UNSUPPORTED, "%s: mask_block %d not supported (must be 128)", fn, mask_block);
+  if ((N + fa::kMaskBlockTokens - 1) / fa::kMaskBlockTokens > kMaskMaxEntries)
+    return fail(FA_ERR_UNSUPPORTED, "%s: N = %d needs more than %d mask entries per row", fn, N, kMaskMaxEntries);
   return FA_OK;
 }
 
@@ -156,7 +162,7 @@ fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   if (s != FA_OK) return s;
   if (drop && dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "%s: float32 dropout is not supported", fn);
   if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
-  if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
+  if (sparse && (s = check_mask(fn, mask, mask_block, N)) != FA_OK) return s;
   if (p.empty || (seqs && seqs->total == 0)) return FA_OK;
   const void* ptrs[] = {q, k, v, o, lse};
   const char* names[] = {"q", "k", "v", "o", "lse"};
@@ -195,7 +201,7 @@ fa_status run_bwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
   fa_status s = check_common(fn, B, H, N, d, dtype, scale, causal, true, &p);
   if (s != FA_OK) return s;
   if ((s = check_heads(fn, H, Hkv)) != FA_OK) return s;
-  if (sparse && (s = check_mask(fn, mask, mask_block)) != FA_OK) return s;
+  if (sparse && (s = check_mask(fn, mask, mask_block, N)) != FA_OK) return s;
   if (p.empty || (seqs && seqs->total == 0)) return FA_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
   const char* names[] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace"};

@@ -98,6 +98,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(3 * C < 64, "vmcnt range");
   static_assert(SLOT % 256 == 0, "slot alignment");
   __shared__ __attribute__((aligned(256))) char smem[kRing * SLOT];
+  __shared__ uint64_t mbits[SPARSE ? kMaskWords : 1];  // kept mask blocks of this key block's column
+  __shared__ uint16_t mnext[SPARSE ? kMaskMaxT : 1];   // next kept block, kept flag
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,14 +174,25 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     vm_wait<0>();  // operand loads done: from here vmcnt counts DMA only
 
     const int n_tiles = (n + BQ - 1) / BQ;
+    // block-sparse: the kept entries of this key block's mask column, as
+    // bits in LDS (built once)
+    constexpr int TPB = kMaskBlock / BQ;  // query tiles per mask block
+    lds_u64* mb = (lds_u64*)mbits;
+    lds_u16* mn = (lds_u16*)mnext;
+    if constexpr (SPARSE) {
+      mask_bits_build(mb, a.mask + kb, a.mask_t, a.mask_t, w, kNT / 64, lane);
+      __syncthreads();
+      mask_table_build(mn, mb, -1, a.mask_t, 64 * w + lane, kNT);
+      __syncthreads();
+    }
     auto tile_live = [&](int i) {
-      if constexpr (SPARSE) return a.mask[(size_t)((i * BQ) / kMaskBlock) * a.mask_t + kb] != 0;
+      if constexpr (SPARSE) return mask_kept(mn, 0, i / TPB);
       return true;
     };
     auto next_tile = [&](int i) {
       ++i;
       if constexpr (SPARSE)
-        while (i < n_tiles && !tile_live(i)) ++i;
+        if (i < n_tiles) i = min(max(i, TPB * mask_next(mn, i / TPB)), n_tiles);
       return i;
     };
     int i_first = CAUSAL ? k0 / BQ : 0;
@@ -572,7 +585,7 @@ __device__ __forceinline__ void wait_ahead(int ahead) {  // ahead: tiles issued 
 // interleaved, and each tile's steps depend on each other (S, dP -> dS ->
 // dQ), so the sweep is software-pipelined by one tile: the products S^T,
 // dP^T of the next tile run interleaved with the softmax-gradient vector
-// work of the current one.  K/V tiles stream through a ring of four LDS
+// work of the current one.  K/V tiles stream through a ring of six LDS
 // slots; DMA runs two tiles ahead, one barrier per iteration makes the next
 // tile visible and frees the slot refilled in the same iteration.
 // NW: waves per workgroup.  Block-sparse runs at d = 64 use two, so that a
@@ -595,6 +608,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
   static_assert(4 * C < 64, "vmcnt range");
   static_assert(C / 2 <= NF - 1 && C - C / 2 <= 4 * KS - 2, "DMA issue slots");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
+  __shared__ uint64_t mbits[SPARSE ? 2 * kMaskWords : 1];  // kept mask blocks of the two mask rows
+  __shared__ uint16_t mnext[SPARSE ? kMaskMaxT : 1];       // next kept block, kept flags per row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -641,28 +656,50 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     const int n_tiles = (n + BC - 1) / BC;
     int j_end = n_tiles;
     if constexpr (CAUSAL) j_end = min(n_tiles, (min(q0 + BR, n) - 1) / BC + 1);
-    // block-sparse: the workgroup spans two 128-query mask rows, each wave one
+    // block-sparse: the workgroup spans one or two 128-query mask rows, each
+    // wave lies in one of them; their kept entries go to LDS tables once
+    // (kTable).  The causal block-sparse variant at d = 128 (no benchmark
+    // shape) has no registers to spare for them and reads the mask bytes
+    // from memory in the sweep instead.
+    constexpr bool kTable = !(CAUSAL && D == 128);
+    constexpr int TPB = kMaskBlock / BC;  // key tiles per mask block
+    lds_u64* mb = (lds_u64*)mbits;
+    lds_u16* mn = (lds_u16*)mnext;
+    int mwave = 0;   // this wave's mask row: 0 or 1
     const uint8_t* mrow0 = nullptr;
     const uint8_t* mrow1 = nullptr;
-    const uint8_t* mwave = nullptr;
+    const uint8_t* mrw = nullptr;
     if constexpr (SPARSE) {
       const int t0 = q0 / kMaskBlock;
       const int t1 = min((q0 + BR - 1) / kMaskBlock, (n - 1) / kMaskBlock);
-      mrow0 = a.mask + (size_t)t0 * a.mask_t;
-      mrow1 = a.mask + (size_t)t1 * a.mask_t;
-      mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+      if constexpr (kTable) {
+        mask_bits_build(mb, a.mask + (size_t)t0 * a.mask_t, 1, a.mask_t, w, NW, lane);
+        if (t1 != t0) mask_bits_build(mb + kMaskWords, a.mask + (size_t)t1 * a.mask_t, 1, a.mask_t, w, NW, lane);
+        __syncthreads();
+        mask_table_build(mn, mb, t1 != t0 ? kMaskWords : -1, a.mask_t, 64 * w + lane, NW * 64);
+        __syncthreads();
+        mwave = (qw0 / kMaskBlock == t0) ? 0 : 1;
+      } else {
+        mrow0 = a.mask + (size_t)t0 * a.mask_t;
+        mrow1 = a.mask + (size_t)t1 * a.mask_t;
+        mrw = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+      }
     }
+    // the next tile after j whose mask block either row keeps (j_end if none)
     auto next_tile = [&](int j) {
       ++j;
-      if constexpr (SPARSE)
-        while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
+      if constexpr (SPARSE && kTable)
+        if (j < j_end) j = min(max(j, TPB * mask_next(mn, j / TPB)), j_end);
+      if constexpr (SPARSE && !kTable)
+        while (j < j_end && !(mrow0[j / TPB] | mrow1[j / TPB])) ++j;
       return j;
     };
     // tiles of this wave's queries that have allowed keys
     auto live = [&](int jt) {
       bool l = jt < j_end;
       if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + 63);
-      if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
+      if constexpr (SPARSE && kTable) l = l && mask_kept(mn, mwave, jt / TPB);
+      if constexpr (SPARSE && !kTable) l = l && mrw[jt / TPB];
       return l;
     };
 

@@ -462,6 +462,60 @@ __device__ __forceinline__ void wg_barrier() {
 #endif
 }
 
+// ------------------------------------------------------------ block-mask tables
+// The kept entries of one or two rows (or one column) of the block mask,
+// built in LDS once per sweep: bits per row (is this tile's block kept for
+// my rows?) and, for the union of the rows, the next kept entry at or after
+// each entry.  Finding the next kept tile then costs one LDS read (counted
+// by lgkmcnt) instead of global byte loads inside the sweep: a global load
+// makes the wave wait on vmcnt, which also counts every outstanding tile
+// DMA, so each lookup would drain the prefetch ring.
+constexpr int kMaskMaxT = 2048;             // mask entries per row the kernels accept (< 4096)
+constexpr int kMaskWords = kMaskMaxT / 64;  // LDS words per row of bits
+
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// Wave w of nw fills words w, w + nw, ... with bit b = (src[b * stride] != 0)
+// for b < T (0 beyond).  A workgroup barrier must follow before any wave
+// reads the words.
+__device__ __forceinline__ void mask_bits_build(lds_u64* words, const uint8_t* src, long stride, int T, int w, int nw,
+                                                int lane) {
+  for (int wd = w; wd < (T + 63) / 64; wd += nw) {
+    const int b = 64 * wd + lane;
+    const bool kept = b < T && src[(size_t)b * stride] != 0;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(kept);
+    if (lane == 0) words[wd] = bits;
+  }
+}
+// After the bits are visible: thread t of nt fills entry e (e = t, t + nt,
+// ...) of `table` with the smallest entry >= e kept in the bits at words
+// (or, with rb >= 0, in their union with the bits at words + rb; T if none)
+// in bits 0-11, and whether e itself is kept in the first row (bit 12) and
+// in the second (bit 13).  A workgroup barrier must follow.
+__device__ __forceinline__ void mask_table_build(lds_u16* table, const lds_u64* words, int rb, int T, int t, int nt) {
+  const int nwd = (T + 63) >> 6;
+  for (int e = t; e < T; e += nt) {
+    int wd = e >> 6;
+    auto word = [&](int i) { return rb >= 0 ? (words[i] | words[rb + i]) : words[i]; };
+    uint64_t x = word(wd) & (~0ull << (e & 63));
+    while (!x && ++wd < nwd) x = word(wd);
+    const int nxt = x ? 64 * wd + (int)__builtin_ctzll(x) : T;
+    const int k0 = (words[e >> 6] >> (e & 63)) & 1;
+    const int k1 = rb >= 0 ? (words[rb + (e >> 6)] >> (e & 63)) & 1 : k0;
+    table[e] = (uint16_t)(nxt | (k0 << 12) | (k1 << 13));
+  }
+}
+// Table entry e (wave-uniform e < T).
+__device__ __forceinline__ int mask_entry(const lds_u16* table, int e) {
+  return __builtin_amdgcn_readfirstlane((int)table[e]);
+}
+// The next kept entry at or after e, and whether e is kept in row r (0, 1).
+__device__ __forceinline__ int mask_next(const lds_u16* table, int e) { return mask_entry(table, e) & 0xfff; }
+__device__ __forceinline__ bool mask_kept(const lds_u16* table, int r, int e) {
+  return (mask_entry(table, e) >> (12 + r)) & 1;
+}
+
 // Map a linear workgroup id so that each XCD (ids are dealt round-robin to
 // the 8 XCDs) receives a contiguous range of logical work items, keeping the
 // K/V of one head in one XCD's L2.

@@ -18,7 +18,7 @@
 //    accumulator as the B operand; V_j^T is fetched from the row-major V
 //    tile with LDS transpose reads (ds_read_b64_tr_b16).  Q^T and O^T live
 //    in the accumulation registers (AGPRs) for the whole sweep.
-//  * 32-key tiles stream through a ring of four LDS slots by global->LDS
+//  * 32-key tiles stream through a ring of six LDS slots by global->LDS
 //    DMA two tiles ahead; one barrier per tile.
 //  * A lone wave per SIMD overlaps its matrix products with its own vector
 //    work only when the two are interleaved, and a tile's steps depend on
@@ -78,6 +78,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
   static_assert(C / 2 <= NF - 1 && C - C / 2 <= 2 * KS - 2, "DMA issue slots");
   static_assert(2 * KS == 2 * NF, "both phases hold the same number of products");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
+  __shared__ uint64_t mbits[SPARSE ? 2 * kMaskWords : 1];  // kept mask blocks of the two mask rows
+  __shared__ uint16_t mnext[SPARSE ? kMaskMaxT : 1];       // next kept block, kept flags per row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -126,28 +128,33 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
       j_end = min(j_lo + chunk, j_end);
     }
     // block-sparse: the workgroup spans one or two 128-query mask rows, each
-    // wave lies in one of them
-    const uint8_t* mrow0 = nullptr;
-    const uint8_t* mrow1 = nullptr;
-    const uint8_t* mwave = nullptr;
+    // wave lies in one of them; their kept entries go to LDS as bits once
+    constexpr int TPB = kMaskBlock / BC;  // key tiles per mask block
+    lds_u64* mb = (lds_u64*)mbits;
+    lds_u16* mn = (lds_u16*)mnext;
+    int mwave = 0;   // this wave's mask row: 0 or 1
     if constexpr (SPARSE) {
       const int t0 = q0 / kMaskBlock;
       const int t1 = min((q0 + BRW - 1) / kMaskBlock, (n - 1) / kMaskBlock);
-      mrow0 = a.mask + (size_t)t0 * a.mask_t;
-      mrow1 = a.mask + (size_t)t1 * a.mask_t;
-      mwave = (qw0 / kMaskBlock == t0) ? mrow0 : mrow1;
+      mask_bits_build(mb, a.mask + (size_t)t0 * a.mask_t, 1, a.mask_t, w, NW, lane);
+      if (t1 != t0) mask_bits_build(mb + kMaskWords, a.mask + (size_t)t1 * a.mask_t, 1, a.mask_t, w, NW, lane);
+      __syncthreads();
+      mask_table_build(mn, mb, t1 != t0 ? kMaskWords : -1, a.mask_t, 64 * w + lane, NW * 64);
+      __syncthreads();
+      mwave = (qw0 / kMaskBlock == t0) ? 0 : 1;
     }
+    // the next tile after j whose mask block either row keeps (j_end if none)
     auto next_tile = [&](int j) {
       ++j;
       if constexpr (SPARSE)
-        while (j < j_end && !(mrow0[(j * BC) / kMaskBlock] | mrow1[(j * BC) / kMaskBlock])) ++j;
+        if (j < j_end) j = min(max(j, TPB * mask_next(mn, j / TPB)), j_end);
       return j;
     };
     // tiles of this wave's queries that have allowed keys
     auto live = [&](int jt) {
       bool l = jt < j_end;
       if constexpr (CAUSAL) l = l && (jt * BC <= qw0 + kWQ - 1);
-      if constexpr (SPARSE) l = l && mwave[(jt * BC) / kMaskBlock];
+      if constexpr (SPARSE) l = l && mask_kept(mn, mwave, jt / TPB);
       return l;
     };
     // Element v of block h of tile jt holds key jt*BC + 4g + 8(v/4) + v%4; it

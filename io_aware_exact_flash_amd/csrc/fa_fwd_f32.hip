@@ -69,11 +69,14 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(FwdArgs a) {
     const int k0 = j * kBC;
     if constexpr (SPARSE)
       if (!mrow[k0 / kMaskBlock]) continue;
-    // The buffers are this wave's own and a wave's LDS accesses complete in
-    // order, so the previous tile's reads are done before these writes and
-    // the writes before the reads below; the wave barriers only keep the
-    // compiler from moving accesses across.
+    // The buffers are this wave's own: lanes write what other lanes of the
+    // same wave read.  Wavefront-scope release/acquire fences around the
+    // wave barrier order those LDS accesses in the memory model (the
+    // barrier alone carries no memory semantics); at wave scope they cost
+    // no instructions beyond the waits the accesses need anyway.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // 16-byte loads (four columns per lane), scattered into the padded rows
     for (int e = 4 * lane; e < kBC * D; e += 4 * 64) {
       const int r = e / D, col = e % D;
@@ -86,7 +89,9 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(FwdArgs a) {
         vs_[r * LD + col + t] = vx[t];
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x16 s = 0.0f;
 #pragma unroll
     for (int t = 0; t < D / 2; ++t)
