@@ -31,6 +31,65 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Samples the shader clock amdsmi reports (current_gfxclks, MHz, mean
+    over the XCDs) while the timed region runs; median() is None when it
+    cannot be read.  This is the clock the firmware reports; the effective
+    rate under the attention kernels (GRBM_GUI_ACTIVE cycles over kernel
+    time, in the counter summaries) can be lower."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+                if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+                    clks = [m["current_gfxclk"]]
+                return sum(clks) / len(clks) if clks else None
+            read()
+            self._read = read
+        except Exception:  # pragma: no cover - no amdsmi or no permission
+            self._read = None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._read:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def median(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return float(v[len(v) // 2])
+
+
 def flop_counts(w, mask):
     """(forward, backward) FLOPs of one step by the pages' convention."""
     f = 4.0 * w["B"] * w["H"] * w["N"] ** 2 * w["d"]
@@ -137,7 +196,50 @@ def cpu_baseline(num, heads):
                       f"forward{'+backward' if w['backward'] else ''} in float64 (NumPy), {dt:.1f} s"}
 
 
-def run_workload(num, steps, warmup, quiet=False):
+def step_bytes(w):
+    """Compulsory HBM bytes of one step: the forward reads Q, K, V and writes
+    O and LSE; the backward reads Q, K, V, O, dO and LSE and writes dQ, dK,
+    dV (tensor T = B H N d elements, per-row arrays B H N float32)."""
+    el = {"bf16": 2, "f16": 2, "f32": 4}[w["dtype"]]
+    rows = w["B"] * w["H"] * w["N"]
+    t = rows * w["d"] * el
+    return 4 * t + 4 * rows + ((8 * t + 4 * rows) if w["backward"] else 0)
+
+
+def _time_steps(step, steps, warmup, e_mid_holder, sampler=None):
+    """Run `steps` timed steps after `warmup` untimed ones; HIP events on
+    torch's current stream (the library's launch stream) around each step
+    and at the forward/backward boundary."""
+    import contextlib
+    import torch
+    from io_aware_exact_flash_amd import flash
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    flash.timing_collect()          # drop anything recorded before the timed region
+    flash.timing_enable(True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    with (sampler if sampler is not None else contextlib.nullcontext()):
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record()
+            e_mid_holder[0] = mids[i]
+            step()
+            ends[i].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    flash.timing_enable(False)
+    kt = flash.timing_collect()
+    per_step = sorted(starts[i].elapsed_time(ends[i]) for i in range(steps))
+    fwd_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(steps)) / steps
+    bwd_ms = sum(mids[i].elapsed_time(ends[i]) for i in range(steps)) / steps
+    return (t1 - t0) * 1e3 / steps, per_step, fwd_ms, bwd_ms, kt
+
+
+def run_workload(num, steps, warmup, quiet=False, sample_clock=False):
     import torch
     from io_aware_exact_flash_amd import flash, workloads
 
@@ -148,48 +250,28 @@ def run_workload(num, steps, warmup, quiet=False):
     gm = None if mask is None else mask.to(dev)
     s = float(1.0 / math.sqrt(w["d"]))
     causal = w["causal"]
-
-    def step():
-        if gm is None:
-            o, lse = flash.fwd(q, k, v, scale=s, causal=causal)
-        else:
-            o, lse = flash.blocksparse_fwd(q, k, v, gm, scale=s, causal=causal)
-        e_mid.record()
-        if w["backward"]:
-            if gm is None:
-                flash.bwd(q, k, v, o, do, lse, scale=s, causal=causal, workspace=ws)
-            else:
-                flash.blocksparse_bwd(q, k, v, o, do, lse, gm, scale=s, causal=causal, workspace=ws)
-        return o
-
     ws = torch.empty(max(1, flash.bwd_workspace_size(w["B"], w["H"], w["N"], w["d"], q.dtype)),
                      dtype=torch.uint8, device=dev)
-    e_mid = torch.cuda.Event(enable_timing=True)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    e_mid = [None]
 
-    flash.timing_collect()          # drop anything recorded before the timed region
-    flash.timing_enable(True)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
-        e_mid = mids[i]
-        step()
-        ends[i].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    flash.timing_enable(False)
-    kt = flash.timing_collect()
+    def make_step(sparse):
+        def step():
+            if sparse:
+                o, lse = flash.blocksparse_fwd(q, k, v, gm, scale=s, causal=causal)
+            else:
+                o, lse = flash.fwd(q, k, v, scale=s, causal=causal)
+            if e_mid[0] is not None:
+                e_mid[0].record()
+            if w["backward"]:
+                if sparse:
+                    flash.blocksparse_bwd(q, k, v, o, do, lse, gm, scale=s, causal=causal, workspace=ws)
+                else:
+                    flash.bwd(q, k, v, o, do, lse, scale=s, causal=causal, workspace=ws)
+            return o
+        return step
 
-    ms_step = (t1 - t0) * 1e3 / steps
-    per_step = sorted(starts[i].elapsed_time(ends[i]) for i in range(steps))
-    fwd_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(steps)) / steps
-    bwd_ms = sum(mids[i].elapsed_time(ends[i]) for i in range(steps)) / steps
+    sampler = ClockSampler() if sample_clock else None
+    ms_step, per_step, fwd_ms, bwd_ms, kt = _time_steps(make_step(gm is not None), steps, warmup, e_mid, sampler)
     ff, fb = flop_counts(w, mask)
     peak = PEAK_TFLOPS[w["dtype"]]
     kf = kernel_flops(w, mask)
@@ -224,17 +306,58 @@ def run_workload(num, steps, warmup, quiet=False):
         "peak": peak, "kernels": kernels, "roofline": roof,
         "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
         "density": None if mask is None else float(mask.float().mean()),
+        # compulsory HBM bytes of the step over its time (the small shapes'
+        # memory-side figure; the MFMA-bound shapes sit far below 8 TB/s)
+        "hbm_gbs": step_bytes(w) / (per_step[len(per_step) // 2] * 1e-3) / 1e9,
+        "sclk_mhz": None if sampler is None else sampler.median(),
     }
     res["fwd_frac_of_peak"] = res["fwd_tflops"] / peak
     res["bwd_frac_of_peak"] = res["bwd_tflops"] / peak if fb else None
+    if mask is not None:
+        # every kernel visits exactly the kept tiles of its mask row or column
+        # (one 128-row mask row per forward/dQ workgroup at d = 64), so the
+        # visited fraction is the realized density; the skip efficiency is
+        # the sparse kernels' throughput on the work they do over the dense
+        # kernels' throughput at the same shape
+        e_mid[0] = None
+        d_ms, d_per, d_fwd, d_bwd, _ = _time_steps(make_step(False), max(3, steps // 2), 2, e_mid)
+        dense_f, dense_b = flop_counts(w, None)
+        dense_tf = (dense_f + dense_b) / (d_per[len(d_per) // 2] * 1e-3) / 1e12
+        sparse_tf = (ff + fb) / (per_step[len(per_step) // 2] * 1e-3) / 1e12
+        res["tiles_visited_frac"] = res["density"]
+        res["dense_same_shape"] = {"ms_per_step": round(d_per[len(d_per) // 2], 4), "tflops": round(dense_tf, 2)}
+        res["skip_efficiency"] = sparse_tf / dense_tf
     if not quiet:
         log(f"workload {num} ({w['name']}): {ms_step:.3f} ms/step, fwd {res['fwd_tflops']:.1f} TF/s "
             f"({100 * res['fwd_frac_of_peak']:.1f}%), bwd "
             + (f"{res['bwd_tflops']:.1f} TF/s ({100 * res['bwd_frac_of_peak']:.1f}%)" if fb else "-")
-            + f", kernels {kernels}")
+            + f", {res['hbm_gbs']:.0f} GB/s compulsory, kernels {kernels}"
+            + (f", skip efficiency {res['skip_efficiency']:.2f}" if mask is not None else ""))
     del q, k, v, do, ws
     torch.cuda.empty_cache()
     return w, res
+
+
+def workload_summary(num, w, r):
+    """Per-workload entry of the JSON line."""
+    out = {"workload": f"{w['name']}: B={w['B']} H={w['H']} N={w['N']} d={w['d']} {w['dtype']}, "
+                       f"{'causal' if w['causal'] else 'non-causal'}"
+                       + (", block-sparse" if w["density"] else "")
+                       + (", forward+backward" if w["backward"] else ", forward"),
+           "ms_per_step": round(r["step_ms_median"], 4),
+           "fwd_ms": round(r["fwd_ms"], 4),
+           "bwd_ms": None if not w["backward"] else round(r["bwd_ms"], 4),
+           "fwd_tflops": round(r["fwd_tflops"], 2),
+           "bwd_tflops": None if r["bwd_tflops"] is None else round(r["bwd_tflops"], 2),
+           "fwd_frac_of_peak": round(r["fwd_frac_of_peak"], 4),
+           "bwd_frac_of_peak": None if r["bwd_frac_of_peak"] is None else round(r["bwd_frac_of_peak"], 4),
+           "peak_tflops": r["peak"],
+           "hbm_gbs": round(r["hbm_gbs"], 1),
+           "kernels": r["kernels"]}
+    if r["density"] is not None:
+        out.update(density=round(r["density"], 4), tiles_visited_frac=round(r["tiles_visited_frac"], 4),
+                   dense_same_shape=r["dense_same_shape"], skip_efficiency=round(r["skip_efficiency"], 3))
+    return out
 
 
 # Shapes for the variants that widen the path (timed with --variants; stderr
@@ -379,7 +502,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="workload timed for the JSON line (default 4: 4x40x8192x128 causal bf16)")
-    ap.add_argument("--all", action="store_true", help="also time every other workload (stderr lines)")
+    ap.add_argument("--only", action="store_true",
+                    help="time only the headline workload (default: all five, the others under 'workloads')")
+    ap.add_argument("--all", action="store_true", help=argparse.SUPPRESS)  # the default now
     ap.add_argument("--cpu-heads", type=int, default=10, help="(batch, head) pairs the oracle baseline runs (about 1 s each at N=8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
@@ -402,12 +527,15 @@ def main():
         sys.exit(3)
     torch.cuda.set_device(0)
 
-    if args.all:
+    # the other workloads first (their entries go to "workloads"), then the
+    # headline workload, whose timed region the top-level fields describe
+    others = {}
+    if not args.only:
         for num in (1, 2, 3, 5, 4):
             if num != args.workload:
-                w, r = run_workload(num, args.steps, args.warmup)
-                log(json.dumps({"workload": num, **{k: v for k, v in r.items()}}))
-    w, r = run_workload(args.workload, args.steps, args.warmup)
+                ow, r = run_workload(num, args.steps, args.warmup)
+                others[num] = workload_summary(num, ow, r)
+    w, r = run_workload(args.workload, args.steps, args.warmup, sample_clock=True)
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -449,6 +577,12 @@ def main():
         "kernels": r["kernels"],
         "roofline": r["roofline"],
         "cpu_baseline": cpu,
+        # shader clock sampled (amdsmi) during the headline timed region: the
+        # fixed 2516.6 TF/s peak assumes 2.4 GHz
+        "sclk_mhz": None if r["sclk_mhz"] is None else round(r["sclk_mhz"], 1),
+        "hbm_gbs": round(r["hbm_gbs"], 1),
+        "workloads": {str(n): e for n, e in sorted({**others, args.workload: workload_summary(
+            args.workload, w, r)}.items())},
     }
     if variants is not None:
         line["variants"] = variants
