@@ -373,6 +373,12 @@ VARIANTS = {
     "dropout": dict(name="dropout p=0.1", B=4, H=32, N=2048, d=128, dtype="bf16", causal=True, p=0.1, seed=15),
     "varlen": dict(name="packed variable-length batch", B=8, H=16, Hkv=16, max_len=4096, d=128,
                    dtype="bf16", causal=True, seed=14),
+    # one new query per head against a key/value cache (decoding), grouped
+    # heads; HBM bound: every cached byte is read once
+    "decode": [dict(name="decode, 32k-token cache", B=8, H=64, Hkv=8, Nq=1, Nk=32768, d=128, dtype="bf16",
+                    causal=True, seed=16),
+               dict(name="decode, 8k-token cache", B=32, H=32, Hkv=8, Nq=1, Nk=8192, d=128, dtype="bf16",
+                    causal=True, seed=17)],
 }
 
 
@@ -469,6 +475,28 @@ def run_variants(steps, warmup):
                                        for n, t in res.items()}}
     log(f"variant varlen: {out['varlen']}")
     del q, k, vv, do, cu, o, lse, qp, kp, vp, dop, op, lsep, ws, wsv
+
+    out["decode"] = []
+    for v in VARIANTS["decode"]:
+        q, k, vv = (t.cuda() for t in workloads.kvcache_qkv(v["B"], v["H"], v["Hkv"], v["Nq"], v["Nk"], v["d"],
+                                                             v["dtype"], seed=v["seed"]))
+        sp = flash.fwd_kvcache_num_splits(v["B"], v["H"], v["Hkv"], v["Nq"], v["Nk"], v["d"])
+        ws = torch.empty(max(1, flash.fwd_kvcache_workspace_size(v["B"], v["H"], v["Hkv"], v["Nq"], v["Nk"], v["d"],
+                                                                  sp, q.dtype)), dtype=torch.uint8, device=q.device)
+        t = time_ms(lambda: flash.fwd_kvcache(q, k, vv, num_splits=sp, causal=v["causal"], workspace=ws),
+                    max(steps, 20), warmup)
+        el = 2
+        byts = (2 * v["B"] * v["Hkv"] * v["Nk"] * v["d"] + 2 * v["B"] * v["H"] * v["Nq"] * v["d"]) * el \
+            + 4 * v["B"] * v["H"] * v["Nq"]
+        flops = 4.0 * v["B"] * v["H"] * v["Nq"] * v["Nk"] * v["d"]
+        e = {"workload": f"{v['name']}: B={v['B']} H={v['H']} Hkv={v['Hkv']} Nq={v['Nq']} Nk={v['Nk']} "
+                         f"d={v['d']} {v['dtype']}, {sp} key splits",
+             "ms": round(t, 4), "gbs": round(byts / (t * 1e-3) / 1e9, 1),
+             "frac_of_hbm_peak": round(byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "tflops": round(flops / (t * 1e-3) / 1e12, 2), "bytes": byts}
+        out["decode"].append(e)
+        log(f"variant decode: {e}")
+        del q, k, vv, ws
 
     v = VARIANTS["dropout"]
     q, k, vv, do = (t.cuda() for t in workloads.qkvdo(v["B"], v["H"], v["N"], v["d"], v["dtype"], seed=v["seed"]))

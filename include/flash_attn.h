@@ -330,6 +330,44 @@ fa_status flash_attn_varlen_bwd_dropout(int B, int H, int Hkv, int total, int ma
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decoding against a key/value cache [FA2 "impact on the KV cache": a
+ * decoding step attends a few new queries per head to every cached key and
+ * value of the sequence; grouped K/V heads as in "MQA and GQA support"]:
+ * exact attention of Nq queries per query head against the first L_b of the
+ * Nk cache slots of sequence b,
+ *   q      in   [B][H][Nq][d]  dtype
+ *   k, v   in   [B][Hkv][Nk][d] dtype   (the cache; slots >= L_b are never read)
+ *   cache_seqlens in  device int32 [B]: L_b (clamped to [0, Nk]), or NULL
+ *          for L_b = Nk; 4-byte aligned
+ *   o      out  [B][H][Nq][d]  dtype
+ *   lse    out  [B][H][Nq]     float32
+ * Query head h reads K/V head floor(h / (H / Hkv)).  Causal rule: the Nq
+ * queries are the last Nq positions of the sequence, so query i sees key j
+ * iff j <= i + L_b - Nq (the last query sees all L_b keys; with L_b < Nq
+ * the first queries see none and give O = 0, LSE = -inf, as do all rows
+ * when L_b = 0).  The cache is read once per K/V head: the H/Hkv query
+ * heads of a group and their Nq queries are processed together, and the
+ * key range is cut into num_splits parts (1..64) whose partial results a
+ * merge pass combines as in flash_attn_fwd_splitkv.  Bound by HBM
+ * bandwidth (the cache is read once); meant for Nq much smaller than Nk.
+ *   workspace  >= flash_attn_fwd_kvcache_workspace_size() bytes (0 when
+ *          num_splits = 1, then workspace may be NULL): num_splits float32
+ *          partial outputs [B*H*Nq][d] then partial log-sum-exps [B*H*Nq].
+ * flash_attn_fwd_kvcache_num_splits gives a split count for the shape
+ * (about four single-wave workgroups per compute unit, at least four
+ * 32-key tiles per split).  dtype FA_F16 or FA_BF16; other conventions and
+ * errors as flash_attn_fwd.
+ */
+size_t flash_attn_fwd_kvcache_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype dtype,
+                                             int num_splits);
+int flash_attn_fwd_kvcache_num_splits(int B, int H, int Hkv, int Nq, int Nk, int d);
+fa_status flash_attn_fwd_kvcache(int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype dtype,
+                                 const void* q, const void* k, const void* v, const int* cache_seqlens,
+                                 float scale, int causal, int num_splits,
+                                 void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-kernel timing (diagnostics; not part of the method).  While enabled,
  * every kernel the library launches is bracketed by two HIP events recorded
  * on its launch stream.  flash_attn_timing_collect waits for the recorded
@@ -338,8 +376,8 @@ fa_status flash_attn_varlen_bwd_dropout(int B, int H, int Hkv, int total, int ma
  * classes: 0 forward (16-bit), 1 forward (float32), 2 backward D pre-pass,
  * 3 backward dK/dV pass, 4 backward dQ pass, 5 split-KV forward ranges,
  * 6 split-KV merge, 7 dK/dV range sum (grouped heads), 8 forward with
- * dropout, 9 dK/dV pass with dropout, 10 dQ pass with dropout;
- * flash_attn_kernel_name(k) names them.  Events are created on first use
+ * dropout, 9 dK/dV pass with dropout, 10 dQ pass with dropout, 11 KV-cache
+ * decoding, 12 its merge pass; flash_attn_kernel_name(k) names them.  Events are created on first use
  * and reused; no device memory is allocated.  Process-wide, guarded by a
  * mutex.
  */

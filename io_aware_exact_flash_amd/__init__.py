@@ -14,8 +14,12 @@ from .flash import (  # noqa: F401
     bwd_dropout,
     bwd_gqa,
     bwd_gqa_workspace_size,
+    bwd_noalloc,
     bwd_workspace_size,
     fwd,
+    fwd_kvcache,
+    fwd_kvcache_num_splits,
+    fwd_kvcache_workspace_size,
     fwd_dropout,
     fwd_gqa,
     fwd_splitkv,
@@ -31,4 +35,5 @@ from .flash import (  # noqa: F401
 
 __all__ = ["fwd", "bwd", "blocksparse_fwd", "blocksparse_bwd", "bwd_workspace_size", "fwd_splitkv", "fwd_splitkv_num_splits",
            "fwd_splitkv_workspace_size", "fwd_gqa", "bwd_gqa", "bwd_gqa_workspace_size", "varlen_fwd",
-           "varlen_bwd", "varlen_bwd_workspace_size", "fwd_dropout", "bwd_dropout", "varlen_fwd_dropout", "varlen_bwd_dropout", "lib", "FlashAttnError"]
+           "varlen_bwd", "varlen_bwd_workspace_size", "fwd_dropout", "bwd_dropout", "varlen_fwd_dropout", "varlen_bwd_dropout", "bwd_noalloc", "fwd_kvcache",
+           "fwd_kvcache_num_splits", "fwd_kvcache_workspace_size", "lib", "FlashAttnError"]

@@ -338,6 +338,42 @@ fa_status run_fwd_split(const char* fn, int B, int H, int N, int d, fa_dtype dty
   return hip_status(fn, e);
 }
 
+// ---------------------------------------------------------------- KV-cache decoding
+// Workspace of flash_attn_fwd_kvcache: with num_splits > 1, num_splits
+// float32 partial outputs [B*H*Nq][d] then num_splits float32 partial
+// log-sum-exps [B*H*Nq] (256-byte aligned); none with one range.
+size_t kvcache_workspace_bytes(long long rows, int d, int splits) {
+  if (rows <= 0 || splits <= 1) return 0;
+  const size_t po = ((size_t)splits * (size_t)rows * (size_t)d * sizeof(float) + 255) & ~(size_t)255;
+  return po + (size_t)splits * (size_t)rows * sizeof(float);
+}
+
+fa_status check_kvcache(const char* fn, int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype dtype, float scale,
+                        int causal, int splits) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: negative size (B=%d H=%d Nq=%d Nk=%d)", fn, B, H, Nq, Nk);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: scale must be finite and > 0 (got %g)", fn, (double)scale);
+  if (causal != 0 && causal != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1 (got %d)", fn, causal);
+  if (splits < 1 || splits > kMaxSplits)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: num_splits %d outside 1..%d", fn, splits, kMaxSplits);
+  fa_status s = check_heads(fn, H, Hkv);
+  if (s != FA_OK) return s;
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s: head dimension %d not supported (64 or 128)", fn, d);
+  if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "%s: float32 is not supported", fn);
+  const long long rows = (long long)B * H * Nq;
+  const long long grp_rows = Hkv > 0 ? (long long)(H / Hkv) * Nq : 0;
+  const long long wgs = (long long)B * Hkv * fa::decode_row_tiles(grp_rows) * splits;
+  if (rows * d >= (1LL << 40) || grp_rows >= (1LL << 30) || wgs >= (1LL << 31) ||
+      (long long)B * Hkv * Nk * (long long)d >= (1LL << 40))
+    return fail(FA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  return FA_OK;
+}
+
 // ---------------------------------------------------------------- timing
 struct Mark {
   int kernel;
@@ -363,7 +399,8 @@ hipEvent_t take_event() {
 
 const char* kKernelNames[fa::kNumKernels] = {"fwd",          "fwd_f32",   "bwd_pre",         "bwd_dkdv",
                                             "bwd_dq",       "fwd_split", "fwd_merge",       "bwd_dkdv_reduce",
-                                            "fwd_dropout",  "bwd_dkdv_dropout", "bwd_dq_dropout"};
+                                            "fwd_dropout",  "bwd_dkdv_dropout", "bwd_dq_dropout", "fwd_decode",
+                                            "fwd_decode_merge"};
 
 }  // namespace
 
@@ -624,6 +661,80 @@ FA_EXPORT fa_status flash_attn_varlen_bwd_dropout(int B, int H, int Hkv, int tot
   if ((s = make_drop(fn, dropout_p, seed, offset, &dr)) != FA_OK) return s;
   return run_bwd(fn, B, H, Hkv, max_seqlen, d, dtype, q, k, v, o, dout, lse, scale, causal, nullptr, 0, false, dq,
                  dk, dv, workspace, workspace_bytes_, stream, &sq, &dr);
+}
+
+FA_EXPORT size_t flash_attn_fwd_kvcache_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype dtype,
+                                                       int num_splits) {
+  (void)dtype;
+  (void)Nk;
+  if (B <= 0 || H <= 0 || Nq <= 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return kvcache_workspace_bytes((long long)B * H * Nq, d, num_splits);
+}
+
+// Ranges that give about four workgroups (one wave each) per compute unit
+// of a 256-CU MI355X, each range keeping at least four 32-key tiles of the
+// cache, at most 64.
+FA_EXPORT int flash_attn_fwd_kvcache_num_splits(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || Nq <= 0 || Nk <= 0) return 1;
+  const long long wgs = (long long)B * Hkv * fa::decode_row_tiles((long long)(H / Hkv) * Nq);
+  long long s = (1024 + wgs - 1) / wgs;
+  const long long by_tiles = ((Nk + 31) / 32 + 3) / 4;
+  if (s > by_tiles) s = by_tiles;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+FA_EXPORT fa_status flash_attn_fwd_kvcache(int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype dtype,
+                                           const void* q, const void* k, const void* v, const int* cache_seqlens,
+                                           float scale, int causal, int num_splits, void* o, float* lse,
+                                           void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  const char* fn = "flash_attn_fwd_kvcache";
+  fa_status s = check_kvcache(fn, B, H, Hkv, Nq, Nk, d, dtype, scale, causal, num_splits);
+  if (s != FA_OK) return s;
+  const long long rows = (long long)B * H * Nq;
+  if (rows == 0) return FA_OK;
+  const void* ptrs[] = {q, o, lse};
+  const char* names[] = {"q", "o", "lse"};
+  if ((s = check_ptrs(fn, ptrs, names, 3)) != FA_OK) return s;
+  if (Nk > 0) {
+    const void* kv[] = {k, v};
+    const char* kvn[] = {"k", "v"};
+    if ((s = check_ptrs(fn, kv, kvn, 2)) != FA_OK) return s;
+  }
+  if (cache_seqlens && (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: cache_seqlens is not 4-byte aligned", fn);
+  const size_t need = kvcache_workspace_bytes(rows, d, num_splits);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace is null", fn);
+    if (workspace_bytes_ < need)
+      return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes_, need);
+    if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARGUMENT, "%s: workspace is not 16-byte aligned", fn);
+  }
+  fa::DecArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cache_lens = cache_seqlens;
+  a.h = H;
+  a.hkv = Hkv;
+  a.grp = H / Hkv;
+  a.nq = Nq;
+  a.nk = Nk;
+  a.nbkv = B * Hkv;
+  a.nsplit = num_splits;
+  a.rows = rows;
+  a.c = scale * 1.4426950408889634f;
+  if (num_splits > 1) {
+    a.po = static_cast<float*>(workspace);
+    a.plse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      (((size_t)num_splits * (size_t)rows * (size_t)d * sizeof(float) + 255) &
+                                       ~(size_t)255));
+  }
+  return hip_status(fn, fa::launch_fwd_decode(dtype == FA_BF16 ? fa::Dt::BF16 : fa::Dt::F16, d, causal != 0, a,
+                                              stream));
 }
 
 FA_EXPORT const char* flash_attn_status_string(fa_status status) {

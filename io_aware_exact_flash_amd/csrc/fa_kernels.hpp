@@ -177,6 +177,28 @@ struct BwdArgs {
   int hkv;               // K/V heads per batch
 };
 
+// Decoding against a key/value cache: q [B][H][nq][d], k, v [B][Hkv][nk][d]
+// (nk cache slots, the first cache_lens[b] valid), o [B][H][nq][d], lse
+// [B][H][nq].  The grp query heads of a K/V head and their nq queries are
+// the group's grp*nq rows (contiguous in q, o and lse).
+struct DecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* cache_lens;  // [B] device, or nullptr (every sequence holds nk keys)
+  int h, hkv, grp;        // query heads, K/V heads, query heads per K/V head
+  int nq, nk;             // queries per head, cache slots per head
+  int nbkv;               // B * Hkv
+  int nrt;                // row tiles per group (set by the launcher)
+  int nsplit;             // key ranges
+  long long rows;         // B * H * nq
+  float c;                // scale * log2(e)
+  float* po;              // [nsplit][rows][d] partial outputs (nsplit > 1)
+  float* plse;            // [nsplit][rows] partial log-sum-exps
+};
+
 // (K/V head, key block) units the dK/dV pass aims for before it cuts groups
 // of query heads into ranges: four per compute unit of a 256-CU MI355X (a
 // causal launch pairs two units per workgroup, so two workgroups per unit).
@@ -197,7 +219,8 @@ inline int dkdv_head_splits(long long bhkv, long long n, int grp) {
 // Kernel classes for the optional per-kernel timing hooks.
 enum KernelId : int {
   kFwd = 0, kFwdF32 = 1, kBwdPre = 2, kBwdDkDv = 3, kBwdDq = 4, kFwdSplit = 5, kFwdMerge = 6,
-  kBwdDkDvReduce = 7, kFwdDrop = 8, kBwdDkDvDrop = 9, kBwdDqDrop = 10, kNumKernels = 11
+  kBwdDkDvReduce = 7, kFwdDrop = 8, kBwdDkDvDrop = 9, kBwdDqDrop = 10, kDecode = 11, kDecodeMerge = 12,
+  kNumKernels = 13
 };
 
 // Bracket one launch with events on its stream when timing is enabled
@@ -215,5 +238,10 @@ hipError_t launch_bwd(Dt dt, int d, bool causal, bool sparse, int bh, BwdArgs a,
 // Dropout variants (dense or packed layouts, no block mask): a.drop set.
 hipError_t launch_fwd_dropout(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
 hipError_t launch_bwd_dropout(Dt dt, int d, bool causal, int bh, BwdArgs a, hipStream_t st);
+// Decoding against a key/value cache (a.nsplit key ranges, merged when > 1).
+hipError_t launch_fwd_decode(Dt dt, int d, bool causal, DecArgs a, hipStream_t st);
+// Row tiles (workgroups per K/V head and key range) for groups of
+// rows_per_group rows.
+int decode_row_tiles(long long rows_per_group);
 
 }  // namespace fa

@@ -54,13 +54,16 @@ SIGNATURES = {
     "flash_attn_varlen_bwd_dropout": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _F, _I, _F,
                                            ctypes.c_uint64, ctypes.c_uint32, _P, _P, _P, _P, _Z, _P]),
     "flash_attn_bwd_noalloc": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _P]),
+    "flash_attn_fwd_kvcache_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "flash_attn_fwd_kvcache_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "flash_attn_fwd_kvcache": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _I, _I, _P, _P, _P, _Z, _P]),
     "flash_attn_status_string": (ctypes.c_char_p, [_I]),
     "flash_attn_last_error": (ctypes.c_char_p, []),
     "flash_attn_timing_enable": (_I, [_I]),
     "flash_attn_timing_collect": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), _I]),
     "flash_attn_kernel_name": (ctypes.c_char_p, [_I]),
 }
-KERNELS = 11  # timing classes (names from flash_attn_kernel_name)
+KERNELS = 13  # timing classes (names from flash_attn_kernel_name)
 
 _lib = None
 _lock = threading.Lock()
@@ -189,6 +192,49 @@ def fwd_splitkv(q, k, v, num_splits=None, scale=None, causal=False, workspace=No
     _check(lib().flash_attn_fwd_splitkv(B, H, N, d, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                         _scale(scale, d), int(bool(causal)), int(num_splits), o.data_ptr(),
                                         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return o, lse
+
+
+def fwd_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, num_splits, dtype=torch.bfloat16) -> int:
+    return int(lib().flash_attn_fwd_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, _DT[dtype], int(num_splits)))
+
+
+def fwd_kvcache_num_splits(B, H, Hkv, Nq, Nk, d) -> int:
+    return int(lib().flash_attn_fwd_kvcache_num_splits(B, H, Hkv, Nq, Nk, d))
+
+
+def fwd_kvcache(q, k, v, cache_seqlens=None, num_splits=None, scale=None, causal=False, workspace=None):
+    """(O [B, H, Nq, d], LSE [B, H, Nq]) = flash_attn_fwd_kvcache(...): q [B, H, Nq, d] against the
+    key/value cache k, v [B, Hkv, Nk, d] (first cache_seqlens[b] slots valid, int32 [B] on the device,
+    or all Nk); num_splits None: flash_attn_fwd_kvcache_num_splits()."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
+    if q.dtype not in _DT or not q.is_cuda:
+        raise ValueError("tensors must be float16/bfloat16 on a HIP device (no CPU path exists)")
+    B, H, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    for t in (k, v):
+        if t.shape[0] != B or t.shape[3] != d or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("k, v must be contiguous [B, Hkv, Nk, d] with q's batch, head size, dtype and device")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    lens = 0
+    if cache_seqlens is not None:
+        if cache_seqlens.dtype != torch.int32 or cache_seqlens.shape != (B,) or cache_seqlens.device != q.device \
+                or not cache_seqlens.is_contiguous():
+            raise ValueError("cache_seqlens must be a contiguous int32 [B] tensor on the inputs' device")
+        lens = cache_seqlens.data_ptr()
+    if num_splits is None:
+        num_splits = fwd_kvcache_num_splits(B, H, Hkv, Nq, Nk, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fwd_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, num_splits, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().flash_attn_fwd_kvcache(B, H, Hkv, Nq, Nk, d, _DT[q.dtype], q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), lens, _scale(scale, d), int(bool(causal)), int(num_splits),
+                                        o.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        _stream(q)))
     return o, lse
 
 

@@ -19,6 +19,9 @@ Recipe (one generator per purpose, CPU ``torch.Generator``):
   draws Q ``[T, H, d]``, K, V ``[T, Hkv, d]``, dO ``[T, H, d]`` (T = the
   sum of the lengths) in that order and returns them with the int32
   offsets ``cu`` = 0, l0, l0 + l1, ... .
+* ``kvcache_qkv(B, H, Hkv, Nq, Nk, d, dtype, seed, gain)`` draws, for a
+  decoding step, Q ``[B, H, Nq, d]`` then the cache K, V ``[B, Hkv, Nk, d]``
+  in that order.
 * ``block_mask(T, density, seed)`` keeps every diagonal block and each
   off-diagonal block with probability p = (density T^2 - T) / (T^2 - T), so
   the expected kept fraction is ``density``; drawn as ``rand(T, T) < p``.
@@ -69,6 +72,19 @@ def qkvdo_grouped(B, H, Hkv, N, d, dtype="bf16", seed=0, gain=1.0):
     out = []
     for heads in (H, Hkv, Hkv, H):
         x = torch.randn((B, heads, N, d), generator=g, dtype=torch.float32)
+        if gain != 1.0:
+            x = x * gain
+        out.append(x.to(_DTYPES[dtype]))
+    return tuple(out)
+
+
+def kvcache_qkv(B, H, Hkv, Nq, Nk, d, dtype="bf16", seed=0, gain=1.0):
+    """Q [B, H, Nq, d] and the key/value cache K, V [B, Hkv, Nk, d] as CPU
+    tensors of ``dtype``, drawn in that order."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = []
+    for heads, n in ((H, Nq), (Hkv, Nk), (Hkv, Nk)):
+        x = torch.randn((B, heads, n, d), generator=g, dtype=torch.float32)
         if gain != 1.0:
             x = x * gain
         out.append(x.to(_DTYPES[dtype]))

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
                      "flash_attn_fwd_gqa", "flash_attn_bwd_gqa", "flash_attn_varlen_fwd",
                      "flash_attn_varlen_bwd", "flash_attn_varlen_bwd_workspace_size",
                      "flash_attn_fwd_dropout", "flash_attn_bwd_dropout", "flash_attn_varlen_fwd_dropout",
-                     "flash_attn_varlen_bwd_dropout"):
+                     "flash_attn_varlen_bwd_dropout", "flash_attn_fwd_kvcache", "flash_attn_bwd_noalloc"):
         assert required in names
 
 
@@ -323,3 +323,49 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(flash, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         flash.lib()
+
+
+def _kv(**kw):
+    a = dict(B=2, H=4, Hkv=2, Nq=1, Nk=100, d=128, dt=flash.FA_BF16, q=FAKE, k=FAKE, v=FAKE, lens=None,
+             scale=0.1, causal=1, splits=1, o=FAKE, lse=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return flash.lib().flash_attn_fwd_kvcache(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["dt"], a["q"],
+                                              a["k"], a["v"], a["lens"], a["scale"], a["causal"], a["splits"],
+                                              a["o"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), flash.FA_ERR_UNSUPPORTED),
+    (dict(dt=flash.FA_F32), flash.FA_ERR_UNSUPPORTED),
+    (dict(H=3), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(Nq=-1), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(splits=0), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(splits=65), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=0), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(k=FAKE_MISALIGNED), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(lens=FAKE + 2), flash.FA_ERR_INVALID_ARGUMENT),
+    (dict(splits=4), flash.FA_ERR_INVALID_ARGUMENT),          # workspace needed, none given
+    (dict(splits=4, ws=FAKE, wsb=16), flash.FA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_kvcache_validation(kw, code):
+    assert _kv(**kw) == code
+
+
+def test_kvcache_workspace_size_and_splits():
+    lib = flash.lib()
+    assert lib.flash_attn_fwd_kvcache_workspace_size(2, 4, 2, 1, 100, 128, flash.FA_BF16, 1) == 0
+    rows = 2 * 4 * 3
+    got = lib.flash_attn_fwd_kvcache_workspace_size(2, 4, 2, 3, 100, 128, flash.FA_BF16, 5)
+    assert got == ((5 * rows * 128 * 4 + 255) // 256) * 256 + 5 * rows * 4
+    # long caches with few K/V heads are split, at most 64 ways; short ones are not
+    assert lib.flash_attn_fwd_kvcache_num_splits(1, 8, 1, 1, 32768, 128) == 64
+    assert lib.flash_attn_fwd_kvcache_num_splits(1, 8, 1, 1, 100, 128) == 1
+    assert lib.flash_attn_fwd_kvcache_num_splits(64, 64, 64, 1, 4096, 128) == 1
+    assert lib.flash_attn_fwd_kvcache_num_splits(0, 8, 1, 1, 100, 128) == 1
+
+
+def test_kvcache_empty_problem_is_ok_without_launch():
+    assert _kv(Nq=0, q=0, o=0, lse=0) == flash.FA_OK
+    assert _kv(B=0, q=0, k=0, v=0, o=0, lse=0) == flash.FA_OK
