@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libflashattn.so")
 OBJ = os.path.join(ROOT, "_build")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_decode.hip", "fa_noalloc.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd2.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_decode.hip", "fa_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -1,0 +1,289 @@
+// Fused exact-attention forward for gfx950, 16-bit inputs, two waves per
+// SIMD.
+//
+// The same computation as fwd_kernel (FlashAttention-2 notes, Algorithm 1,
+// eqs. (10)-(15): online softmax over K/V tiles streamed through LDS, O and
+// the row log-sum-exp written once), with a different split of the work:
+//  * 8 waves x 32 query rows = 256 rows per workgroup, two waves per SIMD.
+//    A lone wave per SIMD stalls on its own LDS, DMA and product-result
+//    latencies; with two, one wave's matrix products run while the other
+//    waits or works through its exponentials, so the kernel does not need
+//    an elaborate hand-interleaved schedule.
+//  * 64-key K/V tiles in a ring of three LDS slots, filled by global->LDS
+//    DMA two tiles ahead; one barrier per tile.
+//  * Per tile and wave: S^T = K Q^T (16 products at d = 128) with Q^T in
+//    registers and K fragments read as LDS rows; the running maximum is
+//    refreshed lazily (only when a row's maximum outgrows it by more than
+//    2^8 in exp2 units: every contribution is then taken against the same
+//    stale maximum, and L = m + ln l holds for any m); P = exp2(S c - m);
+//    O^T += V^T P^T (16 products) with V^T read by LDS transpose reads.
+//  * Causal: tiles above a wave's rows are skipped (the wave still joins the
+//    barriers and the DMA); only tiles crossing its diagonal or the sequence
+//    end are masked element-wise; a workgroup runs a long and a short query
+//    block of its head one after the other (balanced work).
+//
+// Used at d = 64 only.  Every product reads one 1 KiB operand fragment from
+// LDS (K in S^T, V^T in O^T); a 32-row wave uses each fragment for one
+// product, so the four SIMDs of a compute unit ask the LDS for 128 bytes per
+// clock at full product rate.  At d = 64 the exponentials take a larger
+// share of each tile and hiding them behind the other wave wins; at d = 128
+// the LDS traffic decides, and fwd_kernel (64 rows per wave, each fragment
+// used twice, one wave per SIMD) is faster.
+#include <type_traits>
+
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+
+// c + a b on v_mfma_f32_32x32x16 (compiler-placed registers and hazards).
+template <typename Tag>
+__device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (std::is_same<Tag, bf16_tag>::value)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8v, a), __builtin_bit_cast(f16x8v, b), c, 0,
+                                                  0, 0);
+}
+
+constexpr int kNW = 8;            // waves per workgroup
+constexpr int kWR = 32;           // query rows per wave
+constexpr int kRows = kNW * kWR;  // query rows per workgroup
+constexpr float kLazy2 = 8.0f;
+
+template <typename Tag, int D, bool CAUSAL>
+__global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
+  constexpr int BC = 64;              // keys per tile
+  constexpr int KS = D / 16;          // k-steps of the S^T products
+  constexpr int MB = D / 32;          // 32-row blocks of O^T
+  constexpr int KB = BC / 32;         // 32-key blocks per tile
+  constexpr int PK = 2;               // 16-key steps per 32-key block
+  constexpr int kRing = 3;
+  using KL = Pad<D, false>;
+  using VL = Pad<D, true>;
+  using KD = Dma<BC, D, false, kNW>;
+  using VD = Dma<BC, D, true, kNW>;
+  constexpr int SLOT = KD::kSlot + VD::kSlot;
+  constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
+  static_assert(2 * C < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, g = lane >> 5;
+  const int per = CAUSAL ? (a.nqb + 1) / 2 : a.nqb;
+  const int lb = xcd_remap(blockIdx.x, a.nblk);
+  const int bh = lb / per;
+  const int pb_ = lb % per;
+  const HeadAt at = query_head(a.sq, bh, a.n);
+  const int n = at.n;
+  const int qsr = a.sq.qsr, ksr = a.sq.ksr;
+  const uint16_t* __restrict__ Qg = reinterpret_cast<const uint16_t*>(a.q) + at.q;
+  const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + at.kv;
+  const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + at.kv;
+  uint16_t* __restrict__ Og = reinterpret_cast<uint16_t*>(a.o) + at.q;
+  float* __restrict__ Lg = a.lse + at.l;
+  const float cs = a.c;
+
+  auto run = [&](const int qb) {
+    const int q0 = qb * kRows;
+    const int qw0 = q0 + w * kWR;  // the wave's first row
+    const int my_q = qw0 + c32;
+
+    u32x4 qreg[KS];  // Q^T fragments (B operands)
+    {
+      const uint16_t* qr = Qg + (size_t)min(my_q, n - 1) * qsr + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qr + 16 * ks);
+    }
+    const int n_tiles = (n + BC - 1) / BC;
+    const int t_end = CAUSAL ? min(n_tiles, (min(q0 + kRows, n) - 1) / BC + 1) : n_tiles;  // the workgroup's tiles
+    const int t_wave = CAUSAL ? min(t_end, (min(qw0 + kWR, n) - 1) / BC + 1) : t_end;      // this wave's
+    // tiles below t_plain have no masked key for this wave (below its
+    // diagonal and inside the sequence)
+    int t_plain = n / BC;
+    if constexpr (CAUSAL) t_plain = min(t_plain, (qw0 + 1) / BC);
+
+    KD kd;
+    VD vd;
+    kd.init(w, lane);
+    vd.init(w, lane);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
+    // tile jt's DMA into slot sl (past the end: a reload of tile 0 into a
+    // slot nobody reads, so every wave issues C instructions per tile)
+    auto issue = [&](int jt, int sl) {
+      const int tt = jt < t_end ? jt : 0;
+      const uint16_t* kt = Kg + (size_t)tt * BC * ksr;
+      const uint16_t* vt = Vg + (size_t)tt * BC * ksr;
+      const int last = n - 1 - tt * BC;
+      const uint32_t dst = lds_base + sl * SLOT + 1024 * w;
+#pragma unroll
+      for (int k = 0; k < KD::kPer; ++k) kd.issue_at(k, kt, last, 2 * ksr, dst);
+#pragma unroll
+      for (int k = 0; k < VD::kPer; ++k) vd.issue_at(k, vt, last, 2 * ksr, dst + KD::kSlot);
+    };
+
+    vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
+    issue(0, 0);
+    issue(1, 1);
+
+    f32x16 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = 0.0f;
+    float m_run = -INFINITY;  // exp2 units
+    float nmu = 0.0f;         // -m_run, 0 while m_run = -inf
+    float l_part[2] = {0.0f, 0.0f};
+    const int krow = KL::row_base(c32, g);
+    const int vtr = KD::kSlot + VL::tr_base(lane);
+
+    // one tile; MASK: element test against the row's last key
+    auto tile = [&](auto mask_c, int jt, int sl) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      const lchar* base = lds_ptr(smem) + sl * SLOT;
+      const lchar* kr = lds_opaque(base + krow);
+      f32x16 s[KB];
+      f32x16 zero = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kf = ld_row(kr + KL::row_off(kb, ks));
+          s[kb] = mma<Tag>(kf, qreg[ks], ks ? s[kb] : zero);
+        }
+      // element v of block kb holds key jt*BC + 32kb + 4g + 8(v/4) + v%4
+      if constexpr (MASK) {
+        int last = n - 1;
+        if constexpr (CAUSAL) last = min(last, my_q);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int lim = last - jt * BC - 32 * kb - 4 * g;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[kb][v] = (8 * (v >> 2) + (v & 3) > lim) ? -INFINITY : s[kb][v];
+        }
+      }
+      // t = S c - m (exp2 units against the stale maximum; masked keys give
+      // -inf).  The fma is the products' first (compiler-visible) reader, so
+      // the compiler spaces it from them; the row maximum of t then runs as
+      // asm v_max3 on VALU results.
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = fmaf(s[kb][v], cs, nmu);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) mx = max3(mx, s[kb][v], s[kb][v + 1]);
+      // a row that has seen no key yet (m = -inf, t the score itself) takes
+      // its first maximum whatever it is
+      const bool first = m_run == -INFINITY;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > kLazy2 || (first && mx > -INFINITY)) != 0, 0)) {
+        // rare: some row outgrew the stale maximum by > 2^8 (the asm keeps the
+        // compiler from flattening this block into every tile)
+        asm volatile("s_nop 0");
+        const float grow = half_max(mx);  // the row's growth (its maximum of t)
+        const bool gr = first ? grow > -INFINITY : grow > kLazy2;
+        const float alpha = gr ? (first ? 0.0f : fast_exp2(-grow)) : 1.0f;
+        const float shift = gr ? grow : 0.0f;
+        if (gr) {
+          m_run = first ? grow : m_run + grow;
+          nmu = -m_run;
+        }
+        l_part[0] *= alpha;
+        l_part[1] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[kb][v] -= shift;
+      }
+      u32x4 pb[KB][PK];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(s[kb][v]);
+          s[kb][v] = p;
+          l_part[v & 1] += p;
+        }
+#pragma unroll
+        for (int kk = 0; kk < PK; ++kk) pb[kb][kk] = pack8<Tag>(s[kb], 8 * kk);
+      }
+      const lchar* vt = lds_opaque(base + vtr);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < PK; ++kk)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const u32x4 vf = ld_tr(vt + VL::tr_off(kb, kk, 0, mb), vt + VL::tr_off(kb, kk, 1, mb));
+            acc[mb] = mma<Tag>(vf, pb[kb][kk], acc[mb]);
+          }
+    };
+
+    for (int jt = 0; jt < t_end; ++jt) {
+      const int sl = jt % kRing;
+      vm_wait<C>();     // tile jt has landed (for this wave's share; jt + 1 may be in flight) ...
+      wg_barrier();     // ... for every wave, and every wave is done with tile jt - 1
+      issue(jt + 2, (jt + 2) % kRing);
+      if (jt < t_plain) tile(std::false_type{}, jt, sl);
+      else if (jt < t_wave) tile(std::true_type{}, jt, sl);
+    }
+    vm_wait<0>();  // the reloads issued past the last tile have landed
+
+    const float l = half_sum(l_part[0] + l_part[1]);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (my_q < n) {
+      uint16_t* op = Og + (size_t)my_q * qsr;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 pk;
+          pk[0] = pack2<Tag>(acc[mb][4 * r] * inv, acc[mb][4 * r + 1] * inv);
+          pk[1] = pack2<Tag>(acc[mb][4 * r + 2] * inv, acc[mb][4 * r + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + 32 * mb + 8 * r + 4 * g) = pk;
+        }
+      if (g == 0) Lg[my_q] = l > 0.0f ? m_run * kLn2 + logf(l) : -INFINITY;
+    }
+  };
+  const int nqb = (n + kRows - 1) / kRows;
+  const int qa = nqb - 1 - pb_;
+  const int nrun = CAUSAL ? (pb_ < qa ? 2 : pb_ == qa ? 1 : 0) : (qa >= 0 ? 1 : 0);
+#pragma clang loop unroll(disable)
+  for (int r = 0; r < nrun; ++r) {
+    if (r) {
+      vm_wait<0>();     // the first block's DMA (reloads included) is done ...
+      __syncthreads();  // ... and every wave is out of its LDS tiles
+    }
+    run(r ? pb_ : qa);
+  }
+}
+
+template <typename Tag, int D>
+hipError_t launch_d(bool causal, const FwdArgs& a, hipStream_t st) {
+  timing_begin(kFwd, st);
+  if (causal) hipLaunchKernelGGL((fwd2_kernel<Tag, D, true>), dim3(a.nblk), dim3(kNW * 64), 0, st, a);
+  else hipLaunchKernelGGL((fwd2_kernel<Tag, D, false>), dim3(a.nblk), dim3(kNW * 64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  timing_end(kFwd, st);
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_fwd2(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
+  a.nqb = (a.n + kRows - 1) / kRows;
+  a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
+  if (d != 64) return hipErrorInvalidValue;
+  return dt == Dt::BF16 ? launch_d<bf16_tag, 64>(causal, a, st) : launch_d<f16_tag, 64>(causal, a, st);
+}
+
+}  // namespace fa
