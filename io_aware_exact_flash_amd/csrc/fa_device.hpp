@@ -441,6 +441,59 @@ struct Dma {
   }
 };
 
+// The K and V tiles of one ring slot as one run of 1 KB DMA blocks: the K
+// image (row-read layout) first, the V image (transpose-read layout) from
+// byte kBytesK on, block b moved by wave b % NW as in Dma.  One run wastes
+// less LDS on block rounding than two Dma images.
+template <int ROWS, int D, int NW>
+struct DmaKV {
+  using LK = Pad<D, false>;
+  using LV = Pad<D, true>;
+  static constexpr int kBytesK = ROWS * LK::S;
+  static constexpr int kBytesV = ROWS * LV::S;
+  static_assert(kBytesK % 1024 == 0, "K image in whole blocks");
+  static constexpr int kBlocksK = kBytesK / 1024;
+  static constexpr int kBlocks = kBlocksK + (kBytesV + 1023) / 1024;
+  static constexpr int kPer = (kBlocks + NW - 1) / NW;  // DMA instructions per wave per tile
+  static constexpr int kSlot = kPer * NW * 1024;        // LDS bytes reserved per slot
+  int row[kPer];   // source row of instruction k's 16 bytes (0 for padding / past the images)
+  int colb[kPer];  // and its column, in bytes
+  bool isv[kPer];  // instruction k moves V (else K)
+
+  __device__ void init(int w, int lane) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = w + NW * k;
+      int src = 0;
+      isv[k] = b >= kBlocksK;
+      if (b < kBlocksK) {
+        const int off = b * 1024 + 16 * lane;
+        const int r = off / LK::S;
+        const int p = off - r * LK::S - LK::rot(r);
+        if (p >= 0 && p < 2 * D) src = r * D + p / 2;
+      } else {
+        const int off = (b - kBlocksK) * 1024 + 16 * lane;
+        if (off < kBytesV) {
+          const int r = off / LV::S;
+          const int p = off - r * LV::S - LV::rot(r);
+          if (p >= 0 && p < 2 * D) src = r * D + p / 2;
+        }
+      }
+      row[k] = src / D;
+      colb[k] = 2 * (src % D);
+    }
+  }
+  // As Dma::issue_at, with the K and V tiles' first rows kt and vt (same
+  // row stride and last valid row).
+  __device__ __forceinline__ void issue_at(int k, const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
+                                           int last, uint32_t rsb, uint32_t lds_w) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t off = __umul24((uint32_t)min(row[k], last), rsb) + colb[k];
+    dma16_s(isv[k] ? vt : kt, off, lds_w + NW * k * 1024);
+#endif
+  }
+};
+
 // Wait until at most N of this wave's global loads (LDS DMA included) are
 // outstanding; a workgroup barrier must follow before other waves read the
 // data.  gfx9 s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and

@@ -1,4 +1,5 @@
-// Fused exact-attention forward for gfx950, 16-bit inputs.
+// Fused exact-attention forward for gfx950, 16-bit inputs: the block-sparse,
+// split-KV and dropout forwards (the dense forward is fwd2_kernel).
 //
 // Computes, per head, O = softmax(scale * Q K^T) V and the row log-sum-exp
 // L = m + ln(l) in one pass over K and V (FlashAttention-2 notes,
@@ -614,16 +615,12 @@ template <int D>
 constexpr int sparse_waves() { return D == 64 ? 2 : 4; }
 
 template <typename Tag, int D>
-hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStream_t st) {
-  dim3 grid(a.nblk), block(kNT);
+hipError_t launch_sparse_d(bool causal, const FwdArgs& a, hipStream_t st) {
   constexpr int SW = sparse_waves<D>();
   timing_begin(kFwd, st);
-  if (causal && sparse)
-    hipLaunchKernelGGL((fwd_kernel<Tag, D, true, true, false, false, SW>), grid, dim3(64 * SW), 0, st, a);
-  else if (causal) hipLaunchKernelGGL((fwd_kernel<Tag, D, true, false>), grid, block, 0, st, a);
-  else if (sparse)
-    hipLaunchKernelGGL((fwd_kernel<Tag, D, false, true, false, false, SW>), grid, dim3(64 * SW), 0, st, a);
-  else hipLaunchKernelGGL((fwd_kernel<Tag, D, false, false>), grid, block, 0, st, a);
+  if (causal)
+    hipLaunchKernelGGL((fwd_kernel<Tag, D, true, true, false, false, SW>), dim3(a.nblk), dim3(64 * SW), 0, st, a);
+  else hipLaunchKernelGGL((fwd_kernel<Tag, D, false, true, false, false, SW>), dim3(a.nblk), dim3(64 * SW), 0, st, a);
   hipError_t e = hipGetLastError();
   timing_end(kFwd, st);
   return e;
@@ -631,14 +628,13 @@ hipError_t launch_d(bool causal, bool sparse, int bh, const FwdArgs& a, hipStrea
 
 }  // namespace
 
-hipError_t launch_fwd(Dt dt, int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st) {
-  const int rows = sparse ? kWQ * (d == 64 ? sparse_waves<64>() : sparse_waves<128>()) : kBR;
+hipError_t launch_fwd_sparse(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
+  const int rows = kWQ * (d == 64 ? sparse_waves<64>() : sparse_waves<128>());
   a.nqb = (a.n + rows - 1) / rows;
   a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
-  if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, sparse, bh, a, st)
-                                     : launch_d<bf16_tag, 128>(causal, sparse, bh, a, st);
-  return d == 64 ? launch_d<f16_tag, 64>(causal, sparse, bh, a, st)
-                 : launch_d<f16_tag, 128>(causal, sparse, bh, a, st);
+  if (dt == Dt::BF16) return d == 64 ? launch_sparse_d<bf16_tag, 64>(causal, a, st)
+                                     : launch_sparse_d<bf16_tag, 128>(causal, a, st);
+  return d == 64 ? launch_sparse_d<f16_tag, 64>(causal, a, st) : launch_sparse_d<f16_tag, 128>(causal, a, st);
 }
 
 hipError_t launch_fwd_dropout(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {

@@ -1,5 +1,5 @@
 // Fused exact-attention forward for gfx950, 16-bit inputs, two waves per
-// SIMD.
+// SIMD (every dense 16-bit forward without dropout).
 //
 // The same computation as fwd_kernel (FlashAttention-2 notes, Algorithm 1,
 // eqs. (10)-(15): online softmax over K/V tiles streamed through LDS, O and
@@ -7,28 +7,31 @@
 //  * 8 waves x 32 query rows = 256 rows per workgroup, two waves per SIMD.
 //    A lone wave per SIMD stalls on its own LDS, DMA and product-result
 //    latencies; with two, one wave's matrix products run while the other
-//    waits or works through its exponentials, so the kernel does not need
-//    an elaborate hand-interleaved schedule.
-//  * 64-key K/V tiles in a ring of three LDS slots, filled by global->LDS
-//    DMA two tiles ahead; one barrier per tile.
-//  * Per tile and wave: S^T = K Q^T (16 products at d = 128) with Q^T in
-//    registers and K fragments read as LDS rows; the running maximum is
-//    refreshed lazily (only when a row's maximum outgrows it by more than
-//    2^8 in exp2 units: every contribution is then taken against the same
-//    stale maximum, and L = m + ln l holds for any m); P = exp2(S c - m);
-//    O^T += V^T P^T (16 products) with V^T read by LDS transpose reads.
+//    waits or works through its exponentials.
+//  * 64-key K/V tiles in a ring of four LDS slots, filled by global->LDS
+//    DMA two tiles ahead (K and V images of a slot in one run of blocks, so
+//    four slots fit at d = 128); one barrier per tile.
+//  * Per tile and wave: S^T = K Q^T with Q^T in registers and K fragments
+//    read as LDS rows; the running maximum is refreshed lazily (only when a
+//    row's maximum outgrows it by more than 2^8 in exp2 units: every
+//    contribution is then taken against the same stale maximum, and
+//    L = m + ln l holds for any m); P = exp2(S c - m); O^T += V^T P^T with
+//    V^T read by LDS transpose reads.  Fragments stream a fixed distance
+//    ahead of their products.
+//  * The waves of SIMD-mates are skewed by one phase: waves 0-3 run a
+//    tile's S, softmax and PV products in order; waves 4-7 start each tile
+//    with the previous tile's PV products, so one wave's exponentials
+//    overlap the other's products instead of every wave reaching its
+//    vector work at the same moment.  The slot a lagging wave still reads
+//    is the fourth ring slot.
 //  * Causal: tiles above a wave's rows are skipped (the wave still joins the
 //    barriers and the DMA); only tiles crossing its diagonal or the sequence
 //    end are masked element-wise; a workgroup runs a long and a short query
 //    block of its head one after the other (balanced work).
-//
-// Used at d = 64 only.  Every product reads one 1 KiB operand fragment from
-// LDS (K in S^T, V^T in O^T); a 32-row wave uses each fragment for one
-// product, so the four SIMDs of a compute unit ask the LDS for 128 bytes per
-// clock at full product rate.  At d = 64 the exponentials take a larger
-// share of each tile and hiding them behind the other wave wins; at d = 128
-// the LDS traffic decides, and fwd_kernel (64 rows per wave, each fragment
-// used twice, one wave per SIMD) is faster.
+//  * Every instance of the tile code holds the O^T accumulators in the same
+//    registers: only the score products differ between masked and unmasked
+//    tiles, and the softmax and PV code is shared (separate copies made the
+//    compiler move the accumulators between register sets every tile).
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -63,13 +66,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
   constexpr int MB = D / 32;          // 32-row blocks of O^T
   constexpr int KB = BC / 32;         // 32-key blocks per tile
   constexpr int PK = 2;               // 16-key steps per 32-key block
-  constexpr int kRing = 3;
+  constexpr int kRing = 4;
   using KL = Pad<D, false>;
   using VL = Pad<D, true>;
-  using KD = Dma<BC, D, false, kNW>;
-  using VD = Dma<BC, D, true, kNW>;
-  constexpr int SLOT = KD::kSlot + VD::kSlot;
-  constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
+  using KVD = DmaKV<BC, D, kNW>;
+  constexpr int SLOT = KVD::kSlot;
+  constexpr int C = KVD::kPer;  // DMA instructions per wave per tile
   static_assert(2 * C < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
@@ -110,10 +112,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
     int t_plain = n / BC;
     if constexpr (CAUSAL) t_plain = min(t_plain, (qw0 + 1) / BC);
 
-    KD kd;
-    VD vd;
-    kd.init(w, lane);
-    vd.init(w, lane);
+    KVD kvd;
+    kvd.init(w, lane);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
     // tile jt's DMA into slot sl (past the end: a reload of tile 0 into a
     // slot nobody reads, so every wave issues C instructions per tile)
@@ -124,9 +124,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
       const int last = n - 1 - tt * BC;
       const uint32_t dst = lds_base + sl * SLOT + 1024 * w;
 #pragma unroll
-      for (int k = 0; k < KD::kPer; ++k) kd.issue_at(k, kt, last, 2 * ksr, dst);
-#pragma unroll
-      for (int k = 0; k < VD::kPer; ++k) vd.issue_at(k, vt, last, 2 * ksr, dst + KD::kSlot);
+      for (int k = 0; k < KVD::kPer; ++k) kvd.issue_at(k, kt, vt, last, 2 * ksr, dst);
     };
 
     vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
@@ -140,23 +138,32 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
     float nmu = 0.0f;         // -m_run, 0 while m_run = -inf
     float l_part[2] = {0.0f, 0.0f};
     const int krow = KL::row_base(c32, g);
-    const int vtr = KD::kSlot + VL::tr_base(lane);
+    const int vtr = KVD::kBytesK + VL::tr_base(lane);
 
-    // one tile; MASK: element test against the row's last key
-    auto tile = [&](auto mask_c, int jt, int sl) {
+    // S^T of one tile into s (element v of block kb: key jt*BC + 32kb + 4g +
+    // 8(v/4) + v%4); MASK: element test against the row's last key.  The
+    // two blocks' product chains alternate, so consecutive products are
+    // independent, and all K fragments are requested before the first.
+    auto scores = [&](auto mask_c, int jt, int sl, f32x16 (&s)[KB]) {
       constexpr bool MASK = decltype(mask_c)::value;
-      const lchar* base = lds_ptr(smem) + sl * SLOT;
-      const lchar* kr = lds_opaque(base + krow);
-      f32x16 s[KB];
-      f32x16 zero = 0.0f;
+      const lchar* kr = lds_opaque(lds_ptr(smem) + sl * SLOT + krow);
+      // a stream of KS*KB fragments (k-step outer), each requested PD
+      // fragments ahead of its product (at most PD + 1 LDS reads
+      // outstanding, inside the wait counter's range)
+      constexpr int NF = KS * KB;
+      constexpr int PD = NF < 8 ? NF : 8;
+      u32x4 kf[NF];
+      const f32x16 zero = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int f = 0; f < PD; ++f) kf[f] = ld_row(kr + KL::row_off(f % KB, f / KB));
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kf = ld_row(kr + KL::row_off(kb, ks));
-          s[kb] = mma<Tag>(kf, qreg[ks], ks ? s[kb] : zero);
-        }
-      // element v of block kb holds key jt*BC + 32kb + 4g + 8(v/4) + v%4
+      for (int f = 0; f < NF; ++f) {
+        if (f + PD < NF) kf[f + PD] = ld_row(kr + KL::row_off((f + PD) % KB, (f + PD) / KB));
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = f % KB, ks = f / KB;
+        s[kb] = mma<Tag>(kf[f], qreg[ks], ks ? s[kb] : zero);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if constexpr (MASK) {
         int last = n - 1;
         if constexpr (CAUSAL) last = min(last, my_q);
@@ -167,6 +174,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
           for (int v = 0; v < 16; ++v) s[kb][v] = (8 * (v >> 2) + (v & 3) > lim) ? -INFINITY : s[kb][v];
         }
       }
+    };
+
+    u32x4 pb[KB][PK];
+    auto softmax = [&](int jt, int sl) {
+      f32x16 s[KB];
+      if (jt < t_plain) scores(std::false_type{}, jt, sl, s);
+      else scores(std::true_type{}, jt, sl, s);
       // t = S c - m (exp2 units against the stale maximum; masked keys give
       // -inf).  The fma is the products' first (compiler-visible) reader, so
       // the compiler spaces it from them; the row maximum of t then runs as
@@ -204,7 +218,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) s[kb][v] -= shift;
       }
-      u32x4 pb[KB][PK];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -216,25 +229,50 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < PK; ++kk) pb[kb][kk] = pack8<Tag>(s[kb], 8 * kk);
       }
-      const lchar* vt = lds_opaque(base + vtr);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < PK; ++kk)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 vf = ld_tr(vt + VL::tr_off(kb, kk, 0, mb), vt + VL::tr_off(kb, kk, 1, mb));
-            acc[mb] = mma<Tag>(vf, pb[kb][kk], acc[mb]);
-          }
     };
-
-    for (int jt = 0; jt < t_end; ++jt) {
-      const int sl = jt % kRing;
-      vm_wait<C>();     // tile jt has landed (for this wave's share; jt + 1 may be in flight) ...
-      wg_barrier();     // ... for every wave, and every wave is done with tile jt - 1
-      issue(jt + 2, (jt + 2) % kRing);
-      if (jt < t_plain) tile(std::false_type{}, jt, sl);
-      else if (jt < t_wave) tile(std::true_type{}, jt, sl);
+    auto pv = [&](int sl) {
+      const lchar* vt = lds_opaque(lds_ptr(smem) + sl * SLOT + vtr);
+      // V^T fragments (16-key step outer, 32-row block inner), each
+      // requested PV fragments ahead of its product (two reads each)
+      constexpr int NV = KB * PK * MB;
+      constexpr int PV = NV < 6 ? NV : 6;
+      u32x4 vf[NV];
+      auto rd_v = [&](int f) {
+        const int q = f / MB, mb = f % MB;
+        return ld_tr(vt + VL::tr_off(q / PK, q % PK, 0, mb), vt + VL::tr_off(q / PK, q % PK, 1, mb));
+      };
+#pragma unroll
+      for (int f = 0; f < PV; ++f) vf[f] = rd_v(f);
+#pragma unroll
+      for (int f = 0; f < NV; ++f) {
+        if (f + PV < NV) vf[f + PV] = rd_v(f + PV);
+        __builtin_amdgcn_sched_barrier(0);
+        const int q = f / MB, mb = f % MB;
+        acc[mb] = mma<Tag>(vf[f], pb[q / PK][q % PK], acc[mb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (w < kNW / 2) {
+      for (int jt = 0; jt < t_end; ++jt) {
+        const int sl = jt % kRing;
+        vm_wait<C>();     // tile jt has landed (for this wave's share; jt + 1 may be in flight) ...
+        wg_barrier();     // ... for every wave, and every wave is done with tile jt - 2
+        issue(jt + 2, (jt + 2) % kRing);
+        if (jt >= t_wave) continue;
+        softmax(jt, sl);
+        pv(sl);
+      }
+    } else {
+      // one phase behind: the previous tile's PV products first
+      for (int jt = 0; jt < t_end; ++jt) {
+        const int sl = jt % kRing;
+        vm_wait<C>();
+        wg_barrier();
+        issue(jt + 2, (jt + 2) % kRing);
+        if (jt > 0 && jt - 1 < t_wave) pv((jt - 1) % kRing);
+        if (jt < t_wave) softmax(jt, sl);
+      }
+      if (t_end > 0 && t_end - 1 < t_wave) pv((t_end - 1) % kRing);
     }
     vm_wait<0>();  // the reloads issued past the last tile have landed
 
@@ -282,8 +320,8 @@ hipError_t launch_d(bool causal, const FwdArgs& a, hipStream_t st) {
 hipError_t launch_fwd2(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
   a.nqb = (a.n + kRows - 1) / kRows;
   a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
-  if (d != 64) return hipErrorInvalidValue;
-  return dt == Dt::BF16 ? launch_d<bf16_tag, 64>(causal, a, st) : launch_d<f16_tag, 64>(causal, a, st);
+  if (dt == Dt::BF16) return d == 64 ? launch_d<bf16_tag, 64>(causal, a, st) : launch_d<bf16_tag, 128>(causal, a, st);
+  return d == 64 ? launch_d<f16_tag, 64>(causal, a, st) : launch_d<f16_tag, 128>(causal, a, st);
 }
 
 }  // namespace fa

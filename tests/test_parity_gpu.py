@@ -540,16 +540,25 @@ def test_dropout_decisions_read_off_the_output(causal):
 
 
 def test_dropout_zero_rate_matches_plain_calls():
-    """p = 0 keeps every element with factor 1: the forward and dK/dV are
-    bit-identical to the plain calls; dQ (a separate, simpler pass) within
-    the gradient bound."""
-    (q, k, v, do), _ = make(2, 2, 400, 128, "bf16", seed=3)
-    o, lse = flash.fwd(q, k, v, causal=True)
-    dq, dk, dv = flash.bwd(q, k, v, o, do, lse, causal=True)
-    o2, lse2 = flash.fwd_dropout(q, k, v, 0.0, 11, 0, causal=True)
-    dq2, dk2, dv2 = flash.bwd_dropout(q, k, v, o2, do, lse2, 0.0, 11, 0, causal=True)
+    """p = 0 keeps every element with factor 1.  The dropout forward (the
+    one-wave kernel) and the plain forward (the two-wave kernel, other tile
+    sizes and so another summation order) both meet the oracle's bounds.
+    Given the same O and LSE, the dK/dV pass with and without the dropout
+    code is bit-identical; dQ (a separate, simpler pass) within the gradient
+    bound."""
+    (q, k, v, do), f64 = make(2, 2, 400, 128, "bf16", seed=3)
+    s = 128 ** -0.5
+    o, lse = flash.fwd(q, k, v, scale=s, causal=True)
+    o2, lse2 = flash.fwd_dropout(q, k, v, 0.0, 11, 0, scale=s, causal=True)
+    dq, dk, dv = flash.bwd(q, k, v, o, do, lse, scale=s, causal=True)
+    dq2, dk2, dv2 = flash.bwd_dropout(q, k, v, o, do, lse, 0.0, 11, 0, scale=s, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    O, L = _oracle_fwd(f64, s, True)
+    for name, got, ref, tol in (("O plain", o, O, "o"), ("O dropout p=0", o2, O, "o")):
+        compare(name, got, ref, TOL["bf16"][tol], REL_RMS["bf16"])
+    compare_lse("LSE plain", lse, L, TOL["bf16"]["lse"])
+    compare_lse("LSE dropout p=0", lse2, L, TOL["bf16"]["lse"])
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
     compare("dQ", dq2, to64(dq), TOL["bf16"]["grad"])
 
 
