@@ -134,17 +134,17 @@ def kernel_bytes(w):
 # size, see profiles/), keyed by kernel and workload, valid only while the
 # kernel's sources hash to the recorded value.
 KERNEL_SOURCES = {
-    "fwd": ["fa_fwd.hip", "fa_device.hpp", "fa_kernels.hpp"],
+    "fwd": ["fa_fwd2.hip", "fa_device.hpp", "fa_kernels.hpp"],
     "bwd_pre": ["fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp"],
     "bwd_dq": ["fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp"],
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, bytes per launch)
-    ("fwd", 4): ("c0f18f7ffd65f24f", 1842014049),
-    ("bwd_pre", 4): ("9f1d786000fbbb8d", 692101209),
-    ("bwd_dkdv", 4): ("9f1d786000fbbb8d", 2120914183),
-    ("bwd_dq", 4): ("9f1d786000fbbb8d", 2476277269),
+    ("fwd", 4): ("845660f819224083", 1966136320),
+    ("bwd_pre", 4): ("e48ed5b283f6c07a", 692115456),
+    ("bwd_dkdv", 4): ("e48ed5b283f6c07a", 2122223616),
+    ("bwd_dq", 4): ("e48ed5b283f6c07a", 2377240576),
 }
 
 
