@@ -377,9 +377,9 @@ fa_status flash_attn_fwd_kvcache(int B, int H, int Hkv, int Nq, int Nk, int d, f
  * 3 backward dK/dV pass, 4 backward dQ pass, 5 split-KV forward ranges,
  * 6 split-KV merge, 7 dK/dV range sum (grouped heads), 8 forward with
  * dropout, 9 dK/dV pass with dropout, 10 dQ pass with dropout, 11 KV-cache
- * decoding, 12 its merge pass; flash_attn_kernel_name(k) names them.  Events are created on first use
- * and reused; no device memory is allocated.  Process-wide, guarded by a
- * mutex.
+ * decoding, 12 its merge pass; flash_attn_kernel_name(k) names them.
+ * Events are created on first use and reused; no device memory is
+ * allocated.  Process-wide, guarded by a mutex.
  */
 fa_status flash_attn_timing_enable(int enable);
 fa_status flash_attn_timing_collect(double* total_ms, int* launches, int n);
