@@ -15,7 +15,13 @@
 //                every row of P and dS is a register row, so P and dS feed
 //                the dV/dK products as B operands without leaving registers;
 //                Q and dO are staged once, row-major, and read both by rows
-//                (for S, dP) and by LDS transpose reads (for dV, dK);
+//                (for S, dP) and by LDS transpose reads (for dV, dK); the
+//                tiles stream through a ring of five LDS slots with the
+//                workgroup barrier between the S, dP products of the next
+//                tile and the dV, dK products of the current one, so each
+//                phase's first operand reads are issued during the phase
+//                before it (with one wave per SIMD nothing else hides their
+//                latency);
 //  3. dQ pass    one workgroup per 256 queries (4 waves x 64 queries), the
 //                forward's orientation: S^T = K Q^T, dP^T = V dO^T,
 //                dS^T = P^T o (dP^T - D), dQ^T += K^T dS^T.
@@ -88,14 +94,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NB = D / 32;          // 32-row blocks of dK^T / dV^T
   constexpr int PK = BQ / 16;         // k-steps of the dK/dV products
   constexpr int NF = PK * NB;         // transpose fragments per operand per tile
-  constexpr int kRing = 4;
+  constexpr int kRing = 5;
   using TL = Pad<D, true>;            // Q and dO tiles: row reads and transpose reads
   using QD = Dma<BQ, D, true, kNT / 64>;
   constexpr int LDO = QD::kSlot;      // dO tile within a slot
   constexpr int LLD = 2 * QD::kSlot;  // base-2 LSE (32 floats) then D (32 floats)
   constexpr int SLOT = 2 * QD::kSlot + 256;
   constexpr int C = 2 * QD::kPer + 1; // DMA instructions per wave per tile
-  static_assert(3 * C < 64, "vmcnt range");
+  static_assert((kRing - 1) * C < 64, "vmcnt range");
   static_assert(SLOT % 256 == 0, "slot alignment");
   __shared__ __attribute__((aligned(256))) char smem[kRing * SLOT];
   __shared__ uint64_t mbits[SPARSE ? kMaskWords : 1];  // kept mask blocks of this key block's column
@@ -276,16 +282,23 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // S = Q K^T and dP = dO V^T for the tile in slot `so` into set Y, the two
     // accumulation chains interleaved (a single chain would wait out each
     // product's latency); vec(u) is vector work after product u (0 .. 2KS-1)
+    // the first kPD row fragments of the next S, dP products, requested
+    // ahead of them (at the end of the previous part B)
+    u32x4 pq[kPD], po[kPD];
+    auto prefetch_a = [&](int so) {
+      const lchar* rq = lds_opaque(lds_ptr(smem) + so + rrow);
+      const lchar* ro = lds_opaque(lds_ptr(smem) + so + LDO + rrow);
+#pragma unroll
+      for (int ks = 0; ks < kPD; ++ks) {
+        pq[ks] = ld_row(rq + TL::row_off(0, ks));
+        po[ks] = ld_row(ro + TL::row_off(0, ks));
+      }
+    };
     auto prod = [&](auto y_c, int so, auto&& vec) {
       constexpr int Y = decltype(y_c)::value;
       const lchar* rq = lds_opaque(lds_ptr(smem) + so + rrow);
       const lchar* ro = lds_opaque(lds_ptr(smem) + so + LDO + rrow);
       u32x4 fq[kPD + 1], fo[kPD + 1];
-#pragma unroll
-      for (int ks = 0; ks < kPD && ks < KS; ++ks) {
-        fq[ks] = ld_row(rq + TL::row_off(0, ks));
-        fo[ks] = ld_row(ro + TL::row_off(0, ks));
-      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + kPD < KS) {
@@ -293,12 +306,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
           fo[(ks + kPD) % (kPD + 1)] = ld_row(ro + TL::row_off(0, ks + kPD));
         }
         const int r = ks % (kPD + 1);
-        if (ks == 0) mfma32_vd<Tag, true, true>(s[Y], fq[r], kreg[0]);
-        else mfma32_vd<Tag, false, true>(s[Y], fq[r], kreg[ks]);
+        const u32x4 aq = ks < kPD ? pq[ks] : fq[r];
+        const u32x4 ao = ks < kPD ? po[ks] : fo[r];
+        if (ks == 0) mfma32_vd<Tag, true, true>(s[Y], aq, kreg[0]);
+        else mfma32_vd<Tag, false, true>(s[Y], aq, kreg[ks]);
         vec(2 * ks);
         __builtin_amdgcn_sched_barrier(0);
-        if (ks == 0) mfma32_vd<Tag, true, true>(dp[Y], fo[r], vreg[0]);
-        else mfma32_vd<Tag, false, true>(dp[Y], fo[r], vreg[ks]);
+        if (ks == 0) mfma32_vd<Tag, true, true>(dp[Y], ao, vreg[0]);
+        else mfma32_vd<Tag, false, true>(dp[Y], ao, vreg[ks]);
         vec(2 * ks + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -308,16 +323,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     int so = 0;       // its slot
 
     // Iteration over tile i (set X) with the next tile in (set Y = 1 - X):
-    //   part A: S, dP of in                   | P, dS of i, DMA
-    //   part B: dV^T, dK^T += ... of i        | DMA
+    //   part A: S, dP of in                   | P, dS of i
+    //   (barrier: the tile after in has landed; every wave is done with the
+    //    previous iteration's part B, so its slot may be refilled)
+    //   part B: dV^T, dK^T += ... of i        | DMA, the next part A's first fragments
+    // A tile is visible from the barrier two iterations before it is X.
     auto step = [&](auto x_c, auto mask_c) {
       constexpr int X = decltype(x_c)::value;
       constexpr int Y = 1 - X;
       constexpr bool MASK = decltype(mask_c)::value;
       const int in = next_tile(i);
       const int son = slot_next(so);
-      vm_wait<C>();      // tile `in` has landed (for this wave's share) ...
-      wg_barrier();      // ... for every wave; the slot refilled below is free
       const int q0 = i * BQ;
       // dropout bytes of tile i: the quad's four lanes (keys 4m .. 4m+3)
       // draw the 4x4 blocks of queries 8a + 4g .. 8a + 4g + 3 (a = lane % 4);
@@ -376,15 +392,26 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if (u >= 1 && u - 1 < 16) st2(u - 1);
         if (u >= 2 && u - 2 < 16) st3(u - 2);
       };
-      constexpr int kDmaA = C / 2;  // DMA instructions in part A; the rest in part B
+      // part B's first transpose fragments are requested during part A's
+      // last products (tile i has been resident since the previous barrier)
+      const lchar* ot = lds_opaque(base + LDO + rtr);
+      const lchar* qt = lds_opaque(base + rtr);
+      auto trf = [&](const lchar* t, int f) {
+        return ld_tr(t + TL::tr_off(0, f / NB, 0, f % NB), t + TL::tr_off(0, f / NB, 1, f % NB));
+      };
+      u32x4 fo[kPD + 1], fq[kPD + 1];
       // ---- part A (16 elements over 2KS products: 1 or 2 per product)
       prod(std::integral_constant<int, Y>{}, son, [&](int u) {
         constexpr int R = 16 / (2 * KS);  // elements entering per product
 #pragma unroll
         for (int e = 0; e < R; ++e) staged(u * R + e);
+        if (u == 2 * KS - 2) {
 #pragma unroll
-        for (int t = 0; t < kDmaA; ++t)
-          if (u == (2 * t + 1) * 2 * KS / (2 * kDmaA)) dma_tile(t);
+          for (int f = 0; f < kPD && f < NF; ++f) {
+            fo[f] = trf(ot, f);
+            fq[f] = trf(qt, f);
+          }
+        }
       });
       staged(16);
       staged(17);
@@ -396,18 +423,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       valu_to_mfma(pb);
       valu_to_mfma(db);
+      vm_wait<C>();   // the tile after `in` has landed (for this wave's share) ...
+      wg_barrier();   // ... for every wave; the slot refilled below is free
       // ---- part B: dV^T += dO^T P, dK^T += Q^T dS (transpose fragments of tile i)
-      const lchar* ot = lds_opaque(base + LDO + rtr);
-      const lchar* qt = lds_opaque(base + rtr);
-      auto trf = [&](const lchar* t, int f) {
-        return ld_tr(t + TL::tr_off(0, f / NB, 0, f % NB), t + TL::tr_off(0, f / NB, 1, f % NB));
-      };
-      u32x4 fo[kPD + 1], fq[kPD + 1];
-#pragma unroll
-      for (int f = 0; f < kPD && f < NF; ++f) {
-        fo[f] = trf(ot, f);
-        fq[f] = trf(qt, f);
-      }
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (f + kPD < NF) {
@@ -417,8 +435,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
         mfma32_acc<Tag>(dvacc[f % NB], fo[f % (kPD + 1)], pb[f / NB]);
         mfma32_acc<Tag>(dkacc[f % NB], fq[f % (kPD + 1)], db[f / NB]);
 #pragma unroll
-        for (int t = kDmaA; t < C; ++t)
-          if (f == (2 * (t - kDmaA) + 1) * NF / (2 * (C - kDmaA))) dma_tile(t);
+        for (int t = 0; t < C; ++t)
+          if (f == (2 * t + 1) * NF / (2 * C)) dma_tile(t);
+        if (f == NF - 2) prefetch_a(slot_next(son));
         __builtin_amdgcn_sched_barrier(0);
       }
       dma_advance();
@@ -457,12 +476,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int u = 0; u < C; ++u) dma_tile(u);
         dma_advance();
       }
-      // the first tile's products, then the pipelined sweep
-      vm_wait<2 * C>();
+      // the first tile's products, then the pipelined sweep (the first two
+      // tiles visible)
+      vm_wait<(kRing - 3) * C>();
       __syncthreads();
       i = i_first;
       so = 0;
+      prefetch_a(so);
       prod(std::integral_constant<int, 0>{}, so, [](int) {});
+      prefetch_a(slot_next(so));
       vgpr_drain(s);
       vgpr_drain(dp);
       for (int t = 0; t < n_pre; t += 2) {
