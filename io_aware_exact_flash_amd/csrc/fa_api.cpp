@@ -186,6 +186,7 @@ fa_status run_fwd(const char* fn, int B, int H, int Hkv, int N, int d, fa_dtype 
     e = fa::launch_fwd_dropout(dt, d, causal != 0, p.bh, a, stream);
   } else {
     if (dtype == FA_F32) e = fa::launch_fwd_f32(d, causal != 0, sparse, p.bh, a, stream);
+    else if (sparse && d == 64) e = fa::launch_fwd2_sparse(dt, d, causal != 0, p.bh, a, stream);
     else if (sparse) e = fa::launch_fwd_sparse(dt, d, causal != 0, p.bh, a, stream);
     else e = fa::launch_fwd2(dt, d, causal != 0, p.bh, a, stream);
   }

@@ -96,11 +96,20 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NF = PK * NB;         // transpose fragments per operand per tile
   constexpr int kRing = 5;
   using TL = Pad<D, true>;            // Q and dO tiles: row reads and transpose reads
-  using QD = Dma<BQ, D, true, kNT / 64>;
-  constexpr int LDO = QD::kSlot;      // dO tile within a slot
-  constexpr int LLD = 2 * QD::kSlot;  // base-2 LSE (32 floats) then D (32 floats)
-  constexpr int SLOT = 2 * QD::kSlot + 256;
-  constexpr int C = 2 * QD::kPer + 1; // DMA instructions per wave per tile
+  // At d = 64 the Q and dO images sit back to back (the DMA's padding
+  // instructions write a 1 KB scratch block), which keeps the five slots
+  // small enough for two workgroups per compute unit where the registers
+  // allow it (the block-sparse variant); at d = 128 (one workgroup per unit
+  // in any case, and no scalar registers to spare) each image is padded to
+  // whole rounds of the four waves' blocks.
+  constexpr bool kPacked = D == 64;
+  using QD = std::conditional_t<kPacked, DmaPacked<BQ, D, true, kNT / 64>, Dma<BQ, D, true, kNT / 64>>;
+  constexpr int kImg = kPacked ? BQ * TL::S : QD::kPer * kNT / 64 * 1024;  // LDS bytes per image
+  constexpr int LDO = kImg;                 // dO tile within a slot
+  constexpr int LPAD = 2 * kImg;            // scratch block of the packed images
+  constexpr int LLD = LPAD + (kPacked ? 1024 : 0);  // base-2 LSE (32 floats) then D (32 floats)
+  constexpr int SLOT = LLD + 256;
+  constexpr int C = 2 * QD::kPer + 1;       // DMA instructions per wave per tile
   static_assert((kRing - 1) * C < 64, "vmcnt range");
   static_assert(SLOT % 256 == 0, "slot alignment");
   __shared__ __attribute__((aligned(256))) char smem[kRing * SLOT];
@@ -257,9 +266,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       d_ld = (lane < 8 ? Ltg : Dg) + min(it * BQ + 4 * (lane & 7), n - 1);
     };
     auto dma_tile = [&](int t) {
-      if (t < QD::kPer) qd.issue_at(t, d_q, d_last, 2 * qsr, d_lds);
-      else if (t < 2 * QD::kPer) qd.issue_at(t - QD::kPer, d_o, d_last, 2 * qsr, d_lds + LDO);
-      else if (lane < 16) dma16(d_ld, d_slot + LLD);
+      if (t < 2 * QD::kPer) {
+        const bool o = t >= QD::kPer;
+        const int k = o ? t - QD::kPer : t;
+        if constexpr (kPacked) qd.issue_at(k, o ? d_o : d_q, d_last, 2 * qsr, d_lds + (o ? LDO : 0), d_slot + LPAD);
+        else qd.issue_at(k, o ? d_o : d_q, d_last, 2 * qsr, d_lds + (o ? LDO : 0));
+      } else if (lane < 16) {
+        dma16(d_ld, d_slot + LLD);
+      }
     };
     auto dma_advance = [&]() {
       if (iq < n_tiles) iq = next_tile(iq);

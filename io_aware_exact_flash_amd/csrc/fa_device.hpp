@@ -494,6 +494,52 @@ struct DmaKV {
   }
 };
 
+// As Dma, for tile images packed back to back in LDS: the image takes
+// exactly kBytes (a whole number of 1 KB blocks), and the instructions of
+// the last round that have no block of the image left (block >= kBlocks)
+// write to a caller-given 1 KB scratch block instead of past the image, so
+// several images can sit next to each other without padding between them.
+template <int ROWS, int D, bool TR, int NW>
+struct DmaPacked {
+  using L = Pad<D, TR>;
+  static constexpr int kBytes = ROWS * L::S;
+  static_assert(kBytes % 1024 == 0, "image in whole blocks");
+  static constexpr int kBlocks = kBytes / 1024;
+  static constexpr int kPer = (kBlocks + NW - 1) / NW;  // DMA instructions per wave per tile
+  int row[kPer];    // source row of instruction k's 16 bytes (0 for padding)
+  int colb[kPer];   // and its column, in bytes
+  bool pad_last;    // this wave's last instruction has no block of the image
+
+  __device__ void init(int w, int lane) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = w + NW * k;
+      int src = 0;
+      if (b < kBlocks) {
+        const int off = b * 1024 + 16 * lane;
+        const int r = off / L::S;
+        const int p = off - r * L::S - L::rot(r);
+        if (p >= 0 && p < 2 * D) src = r * D + p / 2;
+      }
+      row[k] = src / D;
+      colb[k] = 2 * (src % D);
+    }
+    pad_last = w + NW * (kPer - 1) >= kBlocks;
+  }
+  // Instruction k of wave w's share: t0 the tile's first row, last its last
+  // valid row, rsb the row stride in bytes, lds_w the LDS byte address of
+  // the image plus 1024 * w, lds_pad that of the scratch block.  Only the
+  // last round can hold padding.
+  __device__ __forceinline__ void issue_at(int k, const uint16_t* __restrict__ t0, int last, uint32_t rsb,
+                                           uint32_t lds_w, uint32_t lds_pad) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t off = __umul24((uint32_t)min(row[k], last), rsb) + colb[k];
+    const bool pad = kBlocks % NW != 0 && k == kPer - 1 && pad_last;
+    dma16_s(t0, off, pad ? lds_pad : lds_w + NW * k * 1024);
+#endif
+  }
+};
+
 // Wait until at most N of this wave's global loads (LDS DMA included) are
 // outstanding; a workgroup barrier must follow before other waves read the
 // data.  gfx9 s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and

@@ -59,21 +59,30 @@ constexpr int kWR = 32;           // query rows per wave
 constexpr int kRows = kNW * kWR;  // query rows per workgroup
 constexpr float kLazy2 = 8.0f;
 
-template <typename Tag, int D, bool CAUSAL>
-__global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
+// SPARSE (d = 64): block-sparse forward.  Four waves, 128 rows: a
+// workgroup covers exactly one 128-row mask row, so it loads only that
+// row's kept key tiles, and a three-slot ring (72 KB of LDS) lets two
+// workgroups share a compute unit, two waves per SIMD as in the dense
+// kernel; the waves are not skewed.
+template <typename Tag, int D, bool CAUSAL, bool SPARSE = false>
+__global__ __launch_bounds__((SPARSE ? 4 : kNW) * 64, SPARSE ? 2 : 1) void fwd2_kernel(FwdArgs a) {
+  constexpr int NW = SPARSE ? 4 : kNW;  // waves per workgroup
+  constexpr int ROWS = NW * kWR;        // query rows per workgroup
   constexpr int BC = 64;              // keys per tile
   constexpr int KS = D / 16;          // k-steps of the S^T products
   constexpr int MB = D / 32;          // 32-row blocks of O^T
   constexpr int KB = BC / 32;         // 32-key blocks per tile
   constexpr int PK = 2;               // 16-key steps per 32-key block
-  constexpr int kRing = 4;
+  constexpr int kRing = SPARSE ? 3 : 4;
   using KL = Pad<D, false>;
   using VL = Pad<D, true>;
-  using KVD = DmaKV<BC, D, kNW>;
+  using KVD = DmaKV<BC, D, NW>;
   constexpr int SLOT = KVD::kSlot;
   constexpr int C = KVD::kPer;  // DMA instructions per wave per tile
   static_assert(2 * C < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
+  __shared__ uint64_t mbits[SPARSE ? kMaskWords : 1];  // kept mask blocks of the workgroup's mask row
+  __shared__ uint16_t mnext[SPARSE ? kMaskMaxT : 1];   // next kept block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
   const float cs = a.c;
 
   auto run = [&](const int qb) {
-    const int q0 = qb * kRows;
+    const int q0 = qb * ROWS;
     const int qw0 = q0 + w * kWR;  // the wave's first row
     const int my_q = qw0 + c32;
 
@@ -105,12 +114,31 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
       for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qr + 16 * ks);
     }
     const int n_tiles = (n + BC - 1) / BC;
-    const int t_end = CAUSAL ? min(n_tiles, (min(q0 + kRows, n) - 1) / BC + 1) : n_tiles;  // the workgroup's tiles
+    const int t_end = CAUSAL ? min(n_tiles, (min(q0 + ROWS, n) - 1) / BC + 1) : n_tiles;  // the workgroup's tiles
     const int t_wave = CAUSAL ? min(t_end, (min(qw0 + kWR, n) - 1) / BC + 1) : t_end;      // this wave's
     // tiles below t_plain have no masked key for this wave (below its
     // diagonal and inside the sequence)
     int t_plain = n / BC;
     if constexpr (CAUSAL) t_plain = min(t_plain, (qw0 + 1) / BC);
+
+    // block-sparse: the kept entries of the workgroup's mask row, built in
+    // LDS once; the sweep visits kept tiles only (the same ones for every
+    // wave)
+    constexpr int TPB = kMaskBlock / BC;  // key tiles per mask block
+    lds_u16* mn = (lds_u16*)mnext;
+    if constexpr (SPARSE) {
+      lds_u64* mb = (lds_u64*)mbits;
+      mask_bits_build(mb, a.mask + (size_t)(q0 / kMaskBlock) * a.mask_t, 1, a.mask_t, w, NW, lane);
+      __syncthreads();
+      mask_table_build(mn, mb, -1, a.mask_t, tid, NW * 64);
+      __syncthreads();
+    }
+    auto next_tile = [&](int j) {
+      ++j;
+      if constexpr (SPARSE)
+        if (j < t_end) j = min(max(j, TPB * mask_next(mn, j / TPB)), t_end);
+      return j;
+    };
 
     KVD kvd;
     kvd.init(w, lane);
@@ -128,8 +156,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
     };
 
     vm_wait<0>();  // Q loads done: from here vmcnt counts DMA only
-    issue(0, 0);
-    issue(1, 1);
+    const int j0 = SPARSE ? next_tile(-1) : 0;  // the first two tiles
+    const int j1 = next_tile(j0);
+    issue(j0, 0);
+    issue(j1, 1);
 
     f32x16 acc[MB];
 #pragma unroll
@@ -252,7 +282,22 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (w < kNW / 2) {
+    if constexpr (SPARSE) {
+      int jq = next_tile(j1);  // the next tile to load
+      int jt = j0;
+      for (int it = 0; jt < t_end; ++it) {
+        const int sl = it % kRing;
+        vm_wait<C>();     // tile jt has landed (for this wave's share) ...
+        wg_barrier();     // ... for every wave, and every wave is done with the previous tile
+        issue(jq, (it + 2) % kRing);
+        jq = next_tile(jq);
+        if (jt < t_wave) {
+          softmax(jt, sl);
+          pv(sl);
+        }
+        jt = next_tile(jt);
+      }
+    } else if (w < NW / 2) {
       for (int jt = 0; jt < t_end; ++jt) {
         const int sl = jt % kRing;
         vm_wait<C>();     // tile jt has landed (for this wave's share; jt + 1 may be in flight) ...
@@ -292,7 +337,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void fwd2_kernel(FwdArgs a) {
       if (g == 0) Lg[my_q] = l > 0.0f ? m_run * kLn2 + logf(l) : -INFINITY;
     }
   };
-  const int nqb = (n + kRows - 1) / kRows;
+  const int nqb = (n + ROWS - 1) / ROWS;
   const int qa = nqb - 1 - pb_;
   const int nrun = CAUSAL ? (pb_ < qa ? 2 : pb_ == qa ? 1 : 0) : (qa >= 0 ? 1 : 0);
 #pragma clang loop unroll(disable)
@@ -315,7 +360,25 @@ hipError_t launch_d(bool causal, const FwdArgs& a, hipStream_t st) {
   return e;
 }
 
+template <typename Tag>
+hipError_t launch_sparse64(bool causal, const FwdArgs& a, hipStream_t st) {
+  timing_begin(kFwd, st);
+  if (causal) hipLaunchKernelGGL((fwd2_kernel<Tag, 64, true, true>), dim3(a.nblk), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((fwd2_kernel<Tag, 64, false, true>), dim3(a.nblk), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  timing_end(kFwd, st);
+  return e;
+}
+
 }  // namespace
+
+hipError_t launch_fwd2_sparse(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
+  if (d != 64) return hipErrorInvalidValue;
+  constexpr int rows = 4 * kWR;
+  a.nqb = (a.n + rows - 1) / rows;
+  a.nblk = (causal ? (a.nqb + 1) / 2 : a.nqb) * bh;
+  return dt == Dt::BF16 ? launch_sparse64<bf16_tag>(causal, a, st) : launch_sparse64<f16_tag>(causal, a, st);
+}
 
 hipError_t launch_fwd2(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st) {
   a.nqb = (a.n + kRows - 1) / kRows;

@@ -233,6 +233,8 @@ void timing_end(int kernel, hipStream_t st);
 hipError_t launch_fwd_sparse(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
 // Dense forward at two waves per SIMD (no block mask, no dropout).
 hipError_t launch_fwd2(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
+// Block-sparse forward at two waves per SIMD (d = 64; a.mask set).
+hipError_t launch_fwd2_sparse(Dt dt, int d, bool causal, int bh, FwdArgs a, hipStream_t st);
 hipError_t launch_fwd_f32(int d, bool causal, bool sparse, int bh, FwdArgs a, hipStream_t st);
 // Split-KV forward (a.nsplit key ranges per row, partials in a.po / a.plse)
 // followed by the merge into a.o / a.lse.
