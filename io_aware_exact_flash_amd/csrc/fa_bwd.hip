@@ -1078,10 +1078,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 // ------------------------------------------------------------ dQ pass with dropout
 // dS^T = P^T o (dP'^T Z / (1 - p) - D) with dP'^T = V dO^T and Z the
 // dropout decisions (drawn as in the forward: lane = query).  One wave per
-// 32 queries (four per workgroup), K/V tiles of 32 keys in two LDS slots
-// (the next tile's DMA runs while the current one is computed); simpler
-// than the pipelined pass above, whose registers leave no room for the
-// dropout decisions.
+// 32 queries (four per workgroup), K/V tiles of 32 keys in a ring of three
+// LDS slots filled two tiles ahead, one barrier per tile; the small
+// register and LDS footprint lets two workgroups (d = 128) or three
+// (d = 64) share a compute unit, whose waves hide each other's latencies.
+// Simpler than the pipelined pass above, whose registers leave no room for
+// the dropout decisions.
 constexpr int kDqDropRows = 128;
 
 template <typename Tag, int D, bool CAUSAL>
@@ -1094,8 +1096,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
   using VD = Dma<BC, D, false, kNT / 64>;
   constexpr int SLOT = KD::kSlot + VD::kSlot;
   constexpr int C = KD::kPer + VD::kPer;  // DMA instructions per wave per tile
-  static_assert(C < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) char smem[2 * SLOT];
+  constexpr int kRing = 3;
+  static_assert(2 * C < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem[kRing * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1144,27 +1147,27 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
   const int n_tiles = (n + BC - 1) / BC;
   const int j_end = CAUSAL ? min(n_tiles, (min(q0 + kDqDropRows, n) - 1) / BC + 1) : n_tiles;
-  auto dma = [&](int jt) {  // tile jt into slot jt % 2
-    const uint16_t* kt = Kg + (size_t)jt * BC * ksr;
-    const uint16_t* vt = Vg + (size_t)jt * BC * ksr;
-    const int last = n - 1 - jt * BC;
-    const uint32_t slot = lds_base + (jt & 1) * SLOT + 1024 * w;
+  // tile jt into slot jt % kRing (past the end: a reload of tile 0 into a
+  // slot nobody reads, so every iteration issues C instructions)
+  auto dma = [&](int jt) {
+    const int tt = jt < j_end ? jt : 0;
+    const uint16_t* kt = Kg + (size_t)tt * BC * ksr;
+    const uint16_t* vt = Vg + (size_t)tt * BC * ksr;
+    const int last = n - 1 - tt * BC;
+    const uint32_t slot = lds_base + (jt % kRing) * SLOT + 1024 * w;
 #pragma unroll
     for (int k = 0; k < KD::kPer; ++k) kd.issue_at(k, kt, last, 2 * ksr, slot);
 #pragma unroll
     for (int k = 0; k < VD::kPer; ++k) vd.issue_at(k, vt, last, 2 * ksr, slot + KD::kSlot);
   };
   dma(0);
+  dma(1);
 
   for (int j = 0; j < j_end; ++j) {
-    if (j + 1 < j_end) {
-      dma(j + 1);      // into the slot every wave left at the end of the previous iteration
-      vm_wait<C>();    // tile j has landed (for this wave's share) ...
-    } else {
-      vm_wait<0>();
-    }
-    __syncthreads();   // ... for every wave
-    const int so = (j & 1) * SLOT;
+    vm_wait<C>();   // tile j has landed (for this wave's share; j + 1 may be in flight) ...
+    wg_barrier();   // ... for every wave, and every wave is done with tile j - 1
+    dma(j + 2);     // into tile j - 1's slot
+    const int so = (j % kRing) * SLOT;
     const lchar* krows = lds_opaque(lds_ptr(smem) + so + KL::row_base(c32, g));
     const lchar* vrows = lds_opaque(lds_ptr(smem) + so + KD::kSlot + VL::row_base(c32, g));
     const lchar* kcols = lds_opaque(lds_ptr(smem) + so + KL::tr_base(lane));
@@ -1209,8 +1212,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_dq_drop_kernel(BwdArgs a) {
         mfma32_acc<Tag>(acc[f % MB], kt, db[f / MB]);
       }
     }
-    __syncthreads();  // every wave is done with slot j % 2 before tile j + 2 goes there
   }
+  vm_wait<0>();  // the reloads issued past the last tile have landed
 
   agpr_drain(acc);
   if (my_q < n) {
