@@ -10,7 +10,8 @@
 //    waits or works through its exponentials.
 //  * 64-key K/V tiles in a ring of four LDS slots, filled by global->LDS
 //    DMA two tiles ahead (K and V images of a slot in one run of blocks, so
-//    four slots fit at d = 128); one barrier per tile.
+//    four slots fit at d = 128) that only waves 0-3 issue; one barrier per
+//    tile.
 //  * Per tile and wave: S^T = K Q^T with Q^T in registers and K fragments
 //    read as LDS rows; the running maximum is refreshed lazily (only when a
 //    row's maximum outgrows it by more than 2^8 in exp2 units: every
@@ -76,7 +77,15 @@ __global__ __launch_bounds__((SPARSE ? 4 : kNW) * 64, SPARSE ? 2 : 1) void fwd2_
   constexpr int kRing = SPARSE ? 3 : 4;
   using KL = Pad<D, false>;
   using VL = Pad<D, true>;
-  using KVD = DmaKV<BC, D, NW>;
+  // dense: only waves 0-3 issue the DMA.  The lagging waves 4-7 are the
+  // critical path (their chain of PV products, S products and softmax is
+  // the longer one, and the leading waves wait for them at the barrier);
+  // each DMA instruction costs the address unit ~30 cycles, so the
+  // instructions queue after the barrier, and keeping the lagging waves out
+  // of that queue shortens the iteration.  They see the data through the
+  // barrier, which the issuing waves reach after their vm_wait.
+  constexpr int NDMA = SPARSE ? NW : NW / 2;
+  using KVD = DmaKV<BC, D, NDMA>;
   constexpr int SLOT = KVD::kSlot;
   constexpr int C = KVD::kPer;  // DMA instructions per wave per tile
   static_assert(2 * C < 64, "vmcnt range");
@@ -141,11 +150,13 @@ __global__ __launch_bounds__((SPARSE ? 4 : kNW) * 64, SPARSE ? 2 : 1) void fwd2_
     };
 
     KVD kvd;
-    kvd.init(w, lane);
+    kvd.init(w % NDMA, lane);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds_ptr(smem);
     // tile jt's DMA into slot sl (past the end: a reload of tile 0 into a
-    // slot nobody reads, so every wave issues C instructions per tile)
+    // slot nobody reads, so every issuing wave issues C instructions per
+    // tile; the other waves issue none, and their vm_wait is a no-op)
     auto issue = [&](int jt, int sl) {
+      if (w >= NDMA) return;
       const int tt = jt < t_end ? jt : 0;
       const uint16_t* kt = Kg + (size_t)tt * BC * ksr;
       const uint16_t* vt = Vg + (size_t)tt * BC * ksr;
