@@ -141,10 +141,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, bytes per launch)
-    ("fwd", 4): ("845660f819224083", 1966136320),
-    ("bwd_pre", 4): ("e48ed5b283f6c07a", 692115456),
-    ("bwd_dkdv", 4): ("e48ed5b283f6c07a", 2122223616),
-    ("bwd_dq", 4): ("e48ed5b283f6c07a", 2377240576),
+    ("fwd", 4): ("3a587413d31acff7", 1979772928),
+    ("bwd_pre", 4): ("ca9d5a6c178398a1", 692115456),
+    ("bwd_dkdv", 4): ("ca9d5a6c178398a1", 2118136832),
+    ("bwd_dq", 4): ("ca9d5a6c178398a1", 2377652224),
 }
 
 
